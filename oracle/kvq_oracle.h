@@ -1,0 +1,105 @@
+/*
+ * kvq_oracle.h -- plain, slow CPU oracle for the quantized paged KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load this library.  The product path (the
+ * HIP library under paged_attention_quantized_kv_amd/) never calls it, and the
+ * two share no code, headers, tables or constants.
+ *
+ * What it computes, and where the pages define it:
+ *  - INT8 group-64 KV: one int8 code per element and one 2-byte (FP16) scale per
+ *    64 dimensions per token per head.  NInfer-3090 README, "Choosing a KV
+ *    format" (table: int8 at 33,792 B/token = codes + 2-byte group scales) and
+ *    "RotorQuant KV (rk8v4)" / "Lloyd-Max 4-bit keys (rk4v4)" (one FP16 scale
+ *    per 64 dimensions).
+ *  - Row-scaled FP8 E4M3 KV: NInfer-3090 README, intro and "Current limits"
+ *    (row-scaled FP8 E4M3 among the seven KV formats); one fp32 scale per token
+ *    per KV head = absmax / 448.
+ *  - Quantization happens when rows are appended (kv_cache_append owns KV
+ *    quantization): NInfer-3090 README, intro and "RotorQuant KV (rk8v4)".
+ *  - Decode attention re-reads the whole cache each step: NInfer-3090 README,
+ *    "Choosing a KV format".  The result computed is softmax(q k^T * scale) v
+ *    over the dequantized cache, in fp64.
+ *
+ * Parity pins: every function here is checked by tests marked "not gpu"
+ * against library conversions (numpy float16, torch float8_e4m3fn), closed
+ * forms of attention, invariants and the pages' bytes-per-token table.
+ */
+#ifndef KVQ_ORACLE_H
+#define KVQ_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_FMT_INT8_G64 = 0, ORC_FMT_FP8_ROW = 1 };
+enum { ORC_SRC_F32 = 0, ORC_SRC_BF16 = 1 };
+
+/* Scalar conversions, written from the IEEE-754 binary16, bfloat16 and OCP
+ * FP8 E4M3FN definitions. */
+uint16_t orc_f32_to_f16_rne(float f);
+float orc_f16_to_f32(uint16_t h);
+float orc_bf16_to_f32(uint16_t b);
+uint8_t orc_f32_to_e4m3fn(float f); /* RNE, saturate to +-448, NaN -> 0x7F */
+float orc_e4m3fn_to_f32(uint8_t c);
+
+/* One row of D values -> D int8 codes and D/64 fp16 scale bits. */
+void orc_quant_int8_g64(const float *x, int D, int8_t *codes, uint16_t *scales);
+/* One row of D values -> D E4M3FN codes and one fp32 scale. */
+void orc_quant_fp8_row(const float *x, int D, uint8_t *codes, float *scale);
+
+/* Byte offset of (token slot s, dim d) inside one (block, kv head) page. */
+int64_t orc_k_byte(int s, int d, int D);
+int64_t orc_v_byte(int s, int d, int D);
+/* Element index of the scale of (slot s, 64-group g) inside one page
+ * (INT8: D/64 scales per slot), or of slot s (FP8: one per slot, pass g=0). */
+int64_t orc_scale_elem(int fmt, int s, int g, int D);
+
+typedef struct {
+  int32_t format; /* ORC_FMT_* */
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  uint8_t *k_codes;
+  uint8_t *v_codes;
+  void *k_scales; /* uint16 fp16 bits (INT8) or float (FP8) */
+  void *v_scales;
+} orc_pool;
+
+/* Append n_new rows per sequence at positions start_pos[b] .. start_pos[b]+n_new-1.
+ * k_new, v_new: [B][n_new][Hkv][D] in src_dtype.  Returns 0, or -1 on a bad
+ * argument (position outside the block table, block id out of range). */
+int orc_append(const orc_pool *pool, const void *k_new, const void *v_new, int src_dtype,
+               int B, int n_new, const int32_t *block_table, int max_blocks,
+               const int32_t *start_pos);
+
+/* Dequantized value of K (which=0) or V (which=1) at (block, kv head, slot, dim). */
+double orc_dequant(const orc_pool *pool, int which, int block, int kvh, int slot, int d);
+
+/* Dense attention in fp64: for each query row r, keys 0..last[r] are visible.
+ * q: [nq][D], k, v: [L][D]; out: [nq][D].  Returns -1 if some last[r] is
+ * outside [0, L-1]. */
+int orc_dense_attn(const double *q, const double *k, const double *v, int nq, int L, int D,
+                   double scale, const int32_t *last, double *out);
+
+/* Paged decode attention in fp64.  q: [B][T][Hq][D] in q_dtype.  Row t of
+ * sequence b sees keys 0 .. seq_lens[b]-T+t.  Query head h reads KV head
+ * h / (Hq/Hkv).  rows: optional list of flat (b*T+t)*Hq+h indices to compute
+ * (NULL = all B*T*Hq rows in order); out: [nrows][D]. */
+int orc_paged_attn(const orc_pool *pool, const void *q, int q_dtype, int B, int T, int Hq,
+                   const int32_t *block_table, int max_blocks, const int32_t *seq_lens,
+                   float softmax_scale, const int32_t *rows, int nrows, double *out);
+
+/* Array forms (n elements / n rows) used by the pin tests. */
+void orc_f32_to_f16_n(const float *x, uint16_t *y, int64_t n);
+void orc_f16_to_f32_n(const uint16_t *x, float *y, int64_t n);
+void orc_bf16_to_f32_n(const uint16_t *x, float *y, int64_t n);
+void orc_f32_to_e4m3fn_n(const float *x, uint8_t *y, int64_t n);
+void orc_e4m3fn_to_f32_n(const uint8_t *x, float *y, int64_t n);
+void orc_quant_rows(int fmt, const float *x, int64_t n, int D, uint8_t *codes, void *scales);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

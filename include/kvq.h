@@ -1,0 +1,189 @@
+/*
+ * kvq.h -- C ABI of the quantized paged KV cache for gfx950 (MI355X).
+ *
+ * Two operations make up one decode step of a full-attention layer:
+ *
+ *   kv_append_quant    appends new K/V rows to a paged cache and quantizes them
+ *                      on the way in.  The pages name this op kv_cache_append,
+ *                      "the Op that now owns KV quantization", which stores
+ *                      values from the represented BF16 source directly
+ *                      (NInfer-3090 README, intro and "RotorQuant KV (rk8v4)").
+ *   paged_decode_attn  runs decode attention for 1..B sequences with T query
+ *                      rows each (T=1 plain decode, T=4 for an MTP3 verify
+ *                      round: a round covers concurrency x (draft window + 1)
+ *                      token columns, NInfer-3090 README, "v0.9.1 cohort ..."),
+ *                      dequantizing K/V on the fly over a shared page pool
+ *                      (one pool fixed at startup and shared by every lane,
+ *                      gzenz/ninfer README, "Current limits").
+ *
+ * KV formats (NInfer-3090 README, "Choosing a KV format", table):
+ *   KVQ_INT8_G64      int8 code per element, one fp16 scale per 64 dims per
+ *                     token per KV head (33,792 B/token on the 27B = codes +
+ *                     2-byte group scales); scale = fp16_rne(absmax / 127),
+ *                     code = clamp(rint(x / scale), -127, 127).
+ *   KVQ_FP8_E4M3_ROW  OCP FP8 E4M3FN code per element, one fp32 scale per token
+ *                     per KV head = absmax / 448; code = E4M3FN_rne_sat(x / scale).
+ *   A group (or row) whose absmax is 0 stores scale 0 and all-zero codes.
+ *
+ * Conventions for every call:
+ *   - Every pointer is caller-owned DEVICE memory (e.g. torch tensors) unless
+ *     stated; the library allocates nothing, never synchronizes, keeps no
+ *     state between calls and enqueues work only on `stream` (a hipStream_t;
+ *     NULL = the null stream).  Calls are thread-safe.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid call returns a negative KVQ_ERR_* and enqueues nothing.
+ *   - Data pointers (codes, scales, q, k_new, v_new, out, workspace) must be
+ *     16-byte aligned; int32 tables 4-byte aligned.
+ *   - Device-resident table VALUES (block ids, positions, lengths) are not
+ *     readable from the host without a sync, so they are preconditions; the
+ *     kernels bounds-check them and never access memory outside the arrays:
+ *     an append row whose position or block id is out of range is not
+ *     written, and an attention row of a sequence whose length or block ids
+ *     are out of range is written as NaN.
+ *
+ * Supported shapes: block_size 64; head_dim 128 or 256; 1 <= T <= 8;
+ * num_q_heads a multiple of num_kv_heads with T * (num_q_heads/num_kv_heads)
+ * <= 32; 1 <= num_seqs <= 1024.  Anything else returns KVQ_ERR_UNSUPPORTED.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = -1, /* null / misaligned pointer, negative size, bad enum */
+  KVQ_ERR_UNSUPPORTED = -2, /* shape outside the supported set above */
+  KVQ_ERR_WORKSPACE = -3,   /* workspace_bytes below paged_decode_attn_workspace_bytes() */
+  KVQ_ERR_CAPACITY = -4,    /* max_seq_len (or start+n_new bound) beyond max_blocks_per_seq * 64 */
+  KVQ_ERR_LAUNCH = -5       /* the HIP runtime refused a launch (no device, bad stream, ...) */
+};
+
+typedef enum { KVQ_INT8_G64 = 0, KVQ_FP8_E4M3_ROW = 1 } kvq_format_t;
+typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype_t;
+
+/*
+ * The page pool.  A page is 64 token slots of one KV head in one block; page
+ * (blk, h) is page number p = blk * num_kv_heads + h.
+ *
+ *   k_codes, v_codes   num_blocks * num_kv_heads * 64 * head_dim bytes; page p
+ *                      starts at byte p * 64 * head_dim.  int8 (INT8_G64) or
+ *                      E4M3FN bytes (FP8_E4M3_ROW).
+ *   k_scales, v_scales INT8_G64: fp16, 64 * head_dim/64 per page, page p at
+ *                      element p * head_dim;  FP8_E4M3_ROW: fp32, 64 per page,
+ *                      page p at element p * 64.
+ *
+ * Inside a page (s = token slot 0..63, d = dim, D = head_dim, G64 = D/64,
+ * run(s) = (s % 16) / 4, pos(s) = (s / 16) * 4 + s % 4):
+ *   K byte  ((s/16) * (D/16) + d/16) * 256 + (s%16) * 16 + d%16
+ *           (16x16-byte tiles of 16 slots x 16 dims, slot-major inside a tile)
+ *   V byte  ((d/16) * 4 + run(s)) * 256 + (d%16) * 16 + pos(s)
+ *           (dim-major: the 64 slots of one dim in four 16-byte runs)
+ *   INT8 scale of (s, group g)  element (run(s) * G64 + g) * 16 + pos(s)
+ *   FP8 scale of s              element run(s) * 16 + pos(s)
+ * These orders make every 64-lane load of the attention kernel one contiguous
+ * 1 KiB segment that lands directly in matrix-core operand registers.
+ */
+typedef struct {
+  int32_t format;       /* kvq_format_t */
+  int32_t num_blocks;   /* blocks in the pool, >= 1 */
+  int32_t block_size;   /* token slots per page: must be 64 */
+  int32_t num_kv_heads; /* >= 1 */
+  int32_t head_dim;     /* 128 or 256 */
+  int32_t reserved;     /* set to 0 */
+  void *k_codes;
+  void *v_codes;
+  void *k_scales;
+  void *v_scales;
+} kvq_cache_t;
+
+/*
+ * kv_append_quant -- quantize n_new rows per sequence and write them into the
+ * pool (kv_cache_append owns KV quantization: NInfer-3090 README, intro).
+ *
+ *   k_new, v_new        [num_seqs][n_new][num_kv_heads][head_dim] in src_dtype
+ *                       (KVQ_BF16 or KVQ_F32); bf16 widens to fp32 exactly.
+ *   block_table         [num_seqs][max_blocks_per_seq] int32 block ids.
+ *   start_pos           [num_seqs] int32 (device): row t of sequence b goes to
+ *                       position start_pos[b] + t, i.e. slot (pos % 64) of block
+ *                       block_table[b][pos / 64].
+ * Rows of one call must not target the same slot twice.  n_new == 0 is a no-op.
+ * Returns KVQ_OK or KVQ_ERR_*; KVQ_ERR_CAPACITY if n_new > max_blocks_per_seq*64.
+ */
+int kv_append_quant(const kvq_cache_t *cache, const void *k_new, const void *v_new, int32_t src_dtype,
+                    int32_t num_seqs, int32_t n_new, const int32_t *block_table,
+                    int32_t max_blocks_per_seq, const int32_t *start_pos, void *stream);
+
+/*
+ * Bytes of device workspace paged_decode_attn needs for this shape (0 if the
+ * shape is unsupported).  The split of each sequence's context into chunks is
+ * a pure function of these arguments.
+ */
+size_t paged_decode_attn_workspace_bytes(int32_t num_seqs, int32_t T, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len);
+
+/*
+ * paged_decode_attn -- out = softmax(q k^T * softmax_scale) v over the
+ * dequantized cache ("attention re-reads the whole cache each step",
+ * NInfer-3090 README, "Choosing a KV format").
+ *
+ *   q          [num_seqs][T][num_q_heads][head_dim] in q_dtype (KVQ_BF16 | KVQ_F32)
+ *   seq_lens   [num_seqs] int32 (device): keys visible to the LAST query row of
+ *              each sequence, the T new rows included; row t of sequence b sees
+ *              keys 0 .. seq_lens[b] - T + t (the T rows are causal among
+ *              themselves).  Must satisfy T <= seq_lens[b] <= max_seq_len.
+ *   max_seq_len host-side upper bound of seq_lens; sizes the launch grid.
+ *   query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *   out        [num_seqs][T][num_q_heads][head_dim] fp32.
+ *   workspace  >= paged_decode_attn_workspace_bytes(...) bytes, no
+ *              initialization needed; calls that share a workspace must be
+ *              ordered on one stream.
+ * Accuracy: K/V codes and bf16 queries enter the matrix cores exactly; the
+ * softmax weights enter as an fp16 hi+lo pair; all sums are fp32.  Against an
+ * fp64 evaluation of the same formula the error is a few 1e-5 at unit-scale
+ * inputs.
+ */
+int paged_decode_attn(const kvq_cache_t *cache, const void *q, int32_t q_dtype, int32_t num_seqs,
+                      int32_t T, int32_t num_q_heads, const int32_t *block_table,
+                      int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t max_seq_len,
+                      float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/*
+ * The same call in its two phases (same arguments, same validation):
+ *   _split  each workgroup attends over one chunk of one (sequence, KV head)
+ *           and leaves (running max, running sum, unnormalized output) in the
+ *           workspace;
+ *   _merge  combines the chunks of every query row with log-sum-exp weights
+ *           and writes out.
+ * paged_decode_attn == _split then _merge on the same stream.
+ */
+int paged_decode_attn_split(const kvq_cache_t *cache, const void *q, int32_t q_dtype, int32_t num_seqs,
+                            int32_t T, int32_t num_q_heads, const int32_t *block_table,
+                            int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t max_seq_len,
+                            float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                            void *stream);
+int paged_decode_attn_merge(const kvq_cache_t *cache, const void *q, int32_t q_dtype, int32_t num_seqs,
+                            int32_t T, int32_t num_q_heads, const int32_t *block_table,
+                            int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t max_seq_len,
+                            float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *kvq_status_string(int status);
+
+/* Number of context chunks per (sequence, KV head) the attention splits a
+ * max_seq_len context into, and the tokens per chunk (a multiple of 64);
+ * returns 0 for an unsupported shape. */
+int32_t paged_decode_attn_num_splits(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t max_seq_len, int32_t *tokens_per_split);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

@@ -1,0 +1,178 @@
+"""Python binding of libkvq.so, the gfx950 C-ABI library (include/kvq.h).
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the hipStream_t, and a negative status raises KvqError.  Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback, and importing this package fails loudly if the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+INT8_G64 = 0
+FP8_E4M3_ROW = 1
+F32 = 0
+BF16 = 1
+PAGE = 64
+
+_EXPORTS = ("kv_append_quant", "paged_decode_attn", "paged_decode_attn_split", "paged_decode_attn_merge",
+            "paged_decode_attn_workspace_bytes", "paged_decode_attn_num_splits", "kvq_status_string")
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class CacheDesc(C.Structure):
+    _fields_ = [("format", C.c_int32), ("num_blocks", C.c_int32), ("block_size", C.c_int32),
+                ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("reserved", C.c_int32),
+                ("k_codes", C.c_void_p), ("v_codes", C.c_void_p), ("k_scales", C.c_void_p), ("v_scales", C.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with paged_attention_quantized_kv_amd/build.py "
+                          "(or __graft_entry__.build()); there is no fallback path")
+    L = C.CDLL(LIB_PATH)
+    vp, i32 = C.c_void_p, C.c_int32
+    P = C.POINTER(CacheDesc)
+    L.kv_append_quant.argtypes = [P, vp, vp, i32, i32, i32, vp, i32, vp, vp]
+    L.kv_append_quant.restype = C.c_int
+    attn = [P, vp, i32, i32, i32, i32, vp, i32, vp, i32, C.c_float, vp, vp, C.c_size_t, vp]
+    for name in ("paged_decode_attn", "paged_decode_attn_split", "paged_decode_attn_merge"):
+        getattr(L, name).argtypes = attn
+        getattr(L, name).restype = C.c_int
+    L.paged_decode_attn_workspace_bytes.argtypes = [i32] * 6
+    L.paged_decode_attn_workspace_bytes.restype = C.c_size_t
+    L.paged_decode_attn_num_splits.argtypes = [i32] * 6 + [C.POINTER(i32)]
+    L.paged_decode_attn_num_splits.restype = i32
+    L.kvq_status_string.argtypes = [C.c_int]
+    L.kvq_status_string.restype = C.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.kvq_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise KvqError(status, status_string(status))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}: bf16 or fp32")
+
+
+def _stream(stream) -> C.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: torch.Tensor) -> C.c_void_p:
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+class Cache:
+    """A page pool: four device tensors in the layout of kvq.h, plus its shape."""
+
+    def __init__(self, fmt: int, num_blocks: int, num_kv_heads: int, head_dim: int, device="cuda",
+                 k_codes=None, v_codes=None, k_scales=None, v_scales=None):
+        self.format, self.num_blocks, self.num_kv_heads, self.head_dim = fmt, num_blocks, num_kv_heads, head_dim
+        n = num_blocks * num_kv_heads * PAGE
+        if k_codes is None:
+            k_codes = torch.empty(n * head_dim, dtype=torch.uint8, device=device)
+            v_codes = torch.empty(n * head_dim, dtype=torch.uint8, device=device)
+            if fmt == INT8_G64:
+                k_scales = torch.empty(n * (head_dim // 64), dtype=torch.float16, device=device)
+                v_scales = torch.empty(n * (head_dim // 64), dtype=torch.float16, device=device)
+            else:
+                k_scales = torch.empty(n, dtype=torch.float32, device=device)
+                v_scales = torch.empty(n, dtype=torch.float32, device=device)
+        self.k_codes, self.v_codes, self.k_scales, self.v_scales = k_codes, v_codes, k_scales, v_scales
+        self._desc = CacheDesc(fmt, num_blocks, PAGE, num_kv_heads, head_dim, 0, k_codes.data_ptr(),
+                               v_codes.data_ptr(), k_scales.data_ptr(), v_scales.data_ptr())
+
+    @property
+    def desc(self):
+        return C.byref(self._desc)
+
+    def tensors(self):
+        return self.k_codes, self.v_codes, self.k_scales, self.v_scales
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in self.tensors())
+
+
+def kv_append_quant(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, block_table: torch.Tensor,
+                    start_pos: torch.Tensor, stream=None) -> None:
+    """k_new, v_new: [B, n_new, Hkv, D] bf16|fp32; block_table [B, max_blocks] int32; start_pos [B] int32."""
+    if k_new.dtype != v_new.dtype or k_new.shape != v_new.shape or k_new.dim() != 4:
+        raise ValueError("k_new and v_new must both be [B, n_new, Hkv, D] of one dtype")
+    B, n_new = k_new.shape[0], k_new.shape[1]
+    _check(lib.kv_append_quant(cache.desc, _ptr(k_new), _ptr(v_new), _dtype_code(k_new), B, n_new,
+                               _ptr(block_table), block_table.shape[1], _ptr(start_pos), _stream(stream)))
+
+
+def workspace_bytes(num_seqs: int, T: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                    max_seq_len: int) -> int:
+    return int(lib.paged_decode_attn_workspace_bytes(num_seqs, T, num_q_heads, num_kv_heads, head_dim, max_seq_len))
+
+
+def num_splits(num_seqs: int, T: int, num_q_heads: int, num_kv_heads: int, head_dim: int, max_seq_len: int):
+    tps = C.c_int32(0)
+    n = lib.paged_decode_attn_num_splits(num_seqs, T, num_q_heads, num_kv_heads, head_dim, max_seq_len, C.byref(tps))
+    return int(n), int(tps.value)
+
+
+def alloc_workspace(cache: Cache, num_seqs: int, T: int, num_q_heads: int, max_seq_len: int, device="cuda"):
+    n = workspace_bytes(num_seqs, T, num_q_heads, cache.num_kv_heads, cache.head_dim, max_seq_len)
+    if n == 0:
+        raise KvqError(-2, "unsupported shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _attn(fn, cache, q, block_table, seq_lens, max_seq_len, softmax_scale, out, workspace, stream):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, Hq, D]")
+    B, T, Hq = q.shape[0], q.shape[1], q.shape[2]
+    if out.dtype != torch.float32 or out.shape != q.shape:
+        raise ValueError("out must be fp32 with the shape of q")
+    _check(fn(cache.desc, _ptr(q), _dtype_code(q), B, T, Hq, _ptr(block_table), block_table.shape[1],
+              _ptr(seq_lens), int(max_seq_len), float(softmax_scale), _ptr(out), _ptr(workspace),
+              workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def paged_decode_attn(cache, q, block_table, seq_lens, max_seq_len, softmax_scale, out, workspace, stream=None):
+    """out[B, T, Hq, D] (fp32) = softmax(q k^T * softmax_scale) v over the paged cache."""
+    return _attn(lib.paged_decode_attn, cache, q, block_table, seq_lens, max_seq_len, softmax_scale, out, workspace,
+                 stream)
+
+
+def paged_decode_attn_split(cache, q, block_table, seq_lens, max_seq_len, softmax_scale, out, workspace, stream=None):
+    return _attn(lib.paged_decode_attn_split, cache, q, block_table, seq_lens, max_seq_len, softmax_scale, out,
+                 workspace, stream)
+
+
+def paged_decode_attn_merge(cache, q, block_table, seq_lens, max_seq_len, softmax_scale, out, workspace, stream=None):
+    return _attn(lib.paged_decode_attn_merge, cache, q, block_table, seq_lens, max_seq_len, softmax_scale, out,
+                 workspace, stream)

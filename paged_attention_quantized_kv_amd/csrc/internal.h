@@ -1,0 +1,43 @@
+// internal.h -- shared declarations of the HIP library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kPage = 64;       // token slots per page
+constexpr int kWaves = 4;       // waves per attention workgroup
+constexpr int kTargetWgs = 256; // one attention workgroup per compute unit of the chip
+
+// Launch arguments of kv_append_quant, validated on the host.
+struct AppendArgs {
+  const void *k_new, *v_new;
+  uint8_t *k_codes, *v_codes;
+  void *k_scales, *v_scales;
+  const int32_t *block_table;
+  const int32_t *start_pos;
+  int32_t num_seqs, n_new, num_kv_heads, max_blocks, num_blocks;
+};
+
+// Launch arguments of the two attention phases, validated on the host.
+struct AttnArgs {
+  const uint8_t *k_codes, *v_codes;
+  const void *k_scales, *v_scales;
+  const void *q;
+  const int32_t *block_table;
+  const int32_t *seq_lens;
+  float *ws_ml;  // [B][Hkv][n_splits][R][2]: running max (log2 units), running sum
+  float *ws_o;   // [B][Hkv][n_splits][R][D]: unnormalized output
+  float *out;    // [B][T][Hq][D]
+  int32_t num_seqs, num_blocks, num_kv_heads, num_q_heads, group, T, rows;
+  int32_t max_blocks, max_seq_len, tokens_per_split, n_splits;
+  float qk_scale_log2;  // softmax_scale * log2(e)
+};
+
+hipError_t launch_append(int format, int head_dim, int src_dtype, const AppendArgs &a, hipStream_t s);
+hipError_t launch_attn_split(int format, int head_dim, int q_dtype, const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_merge(int head_dim, const AttnArgs &a, hipStream_t s);
+
+}  // namespace kvq

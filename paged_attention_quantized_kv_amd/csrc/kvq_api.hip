@@ -1,0 +1,205 @@
+// kvq_api.hip -- the C ABI (include/kvq.h): host-side validation and dispatch.
+//
+// Validation is pure host code and runs before any HIP call, so every error
+// path can be exercised without a GPU.
+#include "../../include/kvq.h"
+
+#include <math.h>
+
+#include "internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int check_cache(const kvq_cache_t *c) {
+  if (!c) return KVQ_ERR_INVALID_ARG;
+  if (c->format != KVQ_INT8_G64 && c->format != KVQ_FP8_E4M3_ROW) return KVQ_ERR_INVALID_ARG;
+  if (c->num_blocks < 1 || c->num_kv_heads < 1 || c->block_size < 1) return KVQ_ERR_INVALID_ARG;
+  if (c->block_size != kvq::kPage) return KVQ_ERR_UNSUPPORTED;
+  if (c->head_dim != 128 && c->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
+  const void *p[4] = {c->k_codes, c->v_codes, c->k_scales, c->v_scales};
+  for (const void *x : p)
+    if (!x || !aligned16(x)) return KVQ_ERR_INVALID_ARG;
+  return KVQ_OK;
+}
+
+// Chunking of the context: a pure function of the shape.  Pages per chunk are
+// chosen so that num_seqs * num_kv_heads * chunks is about one workgroup per
+// compute unit, rounded to whole rounds of the 4 waves.
+int32_t chunk_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len) {
+  const long pages = (static_cast<long>(max_seq_len) + kvq::kPage - 1) / kvq::kPage;
+  const long total = pages * num_seqs * num_kv_heads;
+  long pps = (total + kvq::kTargetWgs - 1) / kvq::kTargetWgs;
+  pps = ((pps + kvq::kWaves - 1) / kvq::kWaves) * kvq::kWaves;
+  if (pps < kvq::kWaves) pps = kvq::kWaves;
+  return static_cast<int32_t>(pps * kvq::kPage);
+}
+
+struct AttnShape {
+  int32_t group, rows, tokens_per_split, n_splits;
+  size_t ml_bytes, o_bytes;
+};
+
+int attn_shape(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+               int32_t max_seq_len, AttnShape *s) {
+  if (num_seqs < 1 || T < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_seq_len < 1) return KVQ_ERR_INVALID_ARG;
+  if (head_dim != 128 && head_dim != 256) return KVQ_ERR_UNSUPPORTED;
+  if (num_q_heads % num_kv_heads != 0) return KVQ_ERR_UNSUPPORTED;
+  if (T > 8 || num_seqs > 1024 || num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (static_cast<long>(T) * group > 32) return KVQ_ERR_UNSUPPORTED;
+  if (max_seq_len < T) return KVQ_ERR_INVALID_ARG;
+  s->group = group;
+  s->rows = T * group;
+  s->tokens_per_split = chunk_tokens(num_seqs, num_kv_heads, max_seq_len);
+  s->n_splits = (max_seq_len + s->tokens_per_split - 1) / s->tokens_per_split;
+  const size_t parts = static_cast<size_t>(num_seqs) * num_kv_heads * s->n_splits * s->rows;
+  s->ml_bytes = ((parts * 2 * sizeof(float)) + 255) & ~static_cast<size_t>(255);
+  s->o_bytes = parts * head_dim * sizeof(float);
+  return KVQ_OK;
+}
+
+enum class Phase { kBoth, kSplit, kMerge };
+
+int attn_call(Phase phase, const kvq_cache_t *cache, const void *q, int32_t q_dtype, int32_t num_seqs, int32_t T,
+              int32_t num_q_heads, const int32_t *block_table, int32_t max_blocks_per_seq, const int32_t *seq_lens,
+              int32_t max_seq_len, float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+              void *stream) {
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARG;
+  if (!q || !aligned16(q) || !out || !aligned16(out) || !workspace || !aligned16(workspace)) return KVQ_ERR_INVALID_ARG;
+  if (!block_table || !aligned4(block_table) || !seq_lens || !aligned4(seq_lens)) return KVQ_ERR_INVALID_ARG;
+  if (max_blocks_per_seq < 1) return KVQ_ERR_INVALID_ARG;
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVQ_ERR_INVALID_ARG;
+  AttnShape s;
+  rc = attn_shape(num_seqs, T, num_q_heads, cache->num_kv_heads, cache->head_dim, max_seq_len, &s);
+  if (rc) return rc;
+  if (static_cast<long>(max_seq_len) > static_cast<long>(max_blocks_per_seq) * kvq::kPage) return KVQ_ERR_CAPACITY;
+  if (workspace_bytes < s.ml_bytes + s.o_bytes) return KVQ_ERR_WORKSPACE;
+
+  kvq::AttnArgs a;
+  a.k_codes = static_cast<const uint8_t *>(cache->k_codes);
+  a.v_codes = static_cast<const uint8_t *>(cache->v_codes);
+  a.k_scales = cache->k_scales;
+  a.v_scales = cache->v_scales;
+  a.q = q;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.ws_ml = static_cast<float *>(workspace);
+  a.ws_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + s.ml_bytes);
+  a.out = out;
+  a.num_seqs = num_seqs;
+  a.num_blocks = cache->num_blocks;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.group = s.group;
+  a.T = T;
+  a.rows = s.rows;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_seq_len = max_seq_len;
+  a.tokens_per_split = s.tokens_per_split;
+  a.n_splits = s.n_splits;
+  a.qk_scale_log2 = softmax_scale * 1.4426950408889634f;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (phase != Phase::kMerge) {
+    if (kvq::launch_attn_split(cache->format, cache->head_dim, q_dtype, a, st) != hipSuccess) return KVQ_ERR_LAUNCH;
+  }
+  if (phase != Phase::kSplit) {
+    if (kvq::launch_attn_merge(cache->head_dim, a, st) != hipSuccess) return KVQ_ERR_LAUNCH;
+  }
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvq_status_string(int status) {
+  switch (status) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_ERR_INVALID_ARG: return "KVQ_ERR_INVALID_ARG: null or misaligned pointer, bad enum or size";
+    case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED: shape outside the supported set";
+    case KVQ_ERR_WORKSPACE: return "KVQ_ERR_WORKSPACE: workspace smaller than paged_decode_attn_workspace_bytes()";
+    case KVQ_ERR_CAPACITY: return "KVQ_ERR_CAPACITY: context beyond max_blocks_per_seq * 64";
+    case KVQ_ERR_LAUNCH: return "KVQ_ERR_LAUNCH: the HIP runtime refused a kernel launch";
+    default: return "KVQ_ERR_UNKNOWN";
+  }
+}
+
+int kv_append_quant(const kvq_cache_t *cache, const void *k_new, const void *v_new, int32_t src_dtype,
+                    int32_t num_seqs, int32_t n_new, const int32_t *block_table, int32_t max_blocks_per_seq,
+                    const int32_t *start_pos, void *stream) {
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  if (src_dtype != KVQ_F32 && src_dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARG;
+  if (num_seqs < 1 || n_new < 0 || max_blocks_per_seq < 1) return KVQ_ERR_INVALID_ARG;
+  if (num_seqs > 1024) return KVQ_ERR_UNSUPPORTED;
+  if (!block_table || !aligned4(block_table) || !start_pos || !aligned4(start_pos)) return KVQ_ERR_INVALID_ARG;
+  if (n_new == 0) return KVQ_OK;
+  if (!k_new || !aligned16(k_new) || !v_new || !aligned16(v_new)) return KVQ_ERR_INVALID_ARG;
+  if (static_cast<long>(n_new) > static_cast<long>(max_blocks_per_seq) * kvq::kPage) return KVQ_ERR_CAPACITY;
+  const long rows = 2L * num_seqs * n_new * cache->num_kv_heads;
+  if ((rows + 3) / 4 > 0x7FFFFFFFL) return KVQ_ERR_UNSUPPORTED;
+  kvq::AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_codes = static_cast<uint8_t *>(cache->k_codes);
+  a.v_codes = static_cast<uint8_t *>(cache->v_codes);
+  a.k_scales = cache->k_scales;
+  a.v_scales = cache->v_scales;
+  a.block_table = block_table;
+  a.start_pos = start_pos;
+  a.num_seqs = num_seqs;
+  a.n_new = n_new;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = cache->num_blocks;
+  if (kvq::launch_append(cache->format, cache->head_dim, src_dtype, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KVQ_ERR_LAUNCH;
+  return KVQ_OK;
+}
+
+size_t paged_decode_attn_workspace_bytes(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t max_seq_len) {
+  AttnShape s;
+  if (attn_shape(num_seqs, T, num_q_heads, num_kv_heads, head_dim, max_seq_len, &s) != KVQ_OK) return 0;
+  return s.ml_bytes + s.o_bytes;
+}
+
+int32_t paged_decode_attn_num_splits(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t max_seq_len, int32_t *tokens_per_split) {
+  AttnShape s;
+  if (attn_shape(num_seqs, T, num_q_heads, num_kv_heads, head_dim, max_seq_len, &s) != KVQ_OK) return 0;
+  if (tokens_per_split) *tokens_per_split = s.tokens_per_split;
+  return s.n_splits;
+}
+
+int paged_decode_attn(const kvq_cache_t *cache, const void *q, int32_t q_dtype, int32_t num_seqs, int32_t T,
+                      int32_t num_q_heads, const int32_t *block_table, int32_t max_blocks_per_seq,
+                      const int32_t *seq_lens, int32_t max_seq_len, float softmax_scale, float *out, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  return attn_call(Phase::kBoth, cache, q, q_dtype, num_seqs, T, num_q_heads, block_table, max_blocks_per_seq,
+                   seq_lens, max_seq_len, softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+int paged_decode_attn_split(const kvq_cache_t *cache, const void *q, int32_t q_dtype, int32_t num_seqs, int32_t T,
+                            int32_t num_q_heads, const int32_t *block_table, int32_t max_blocks_per_seq,
+                            const int32_t *seq_lens, int32_t max_seq_len, float softmax_scale, float *out,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  return attn_call(Phase::kSplit, cache, q, q_dtype, num_seqs, T, num_q_heads, block_table, max_blocks_per_seq,
+                   seq_lens, max_seq_len, softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+int paged_decode_attn_merge(const kvq_cache_t *cache, const void *q, int32_t q_dtype, int32_t num_seqs, int32_t T,
+                            int32_t num_q_heads, const int32_t *block_table, int32_t max_blocks_per_seq,
+                            const int32_t *seq_lens, int32_t max_seq_len, float softmax_scale, float *out,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  return attn_call(Phase::kMerge, cache, q, q_dtype, num_seqs, T, num_q_heads, block_table, max_blocks_per_seq,
+                   seq_lens, max_seq_len, softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

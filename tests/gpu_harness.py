@@ -1,0 +1,101 @@
+"""Helpers shared by the GPU parity tests, smoke() and bench.py.
+
+They move seeded workloads (kvq_synth) to the device, fill a page pool through
+kv_append_quant, and build the oracle's pool from the same source rows.  No
+value produced here on the GPU ever feeds the oracle.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import kvq_synth as S
+
+POISON_CODE = 0x7F
+POISON_F16 = 0x7E00  # fp16 NaN
+
+
+def src_tensor(a: np.ndarray, src: int, device) -> torch.Tensor:
+    """Source rows / queries (float32 array, or uint16 bf16 bits) -> device tensor."""
+    if src == S.SRC_BF16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+def new_cache(K, w: S.Workload, device, poison: bool = True):
+    s = w.shape
+    cache = K.Cache(s.fmt, w.num_blocks, s.Hkv, s.D, device=device)
+    if poison:
+        cache.k_codes.fill_(POISON_CODE)
+        cache.v_codes.fill_(POISON_CODE)
+        if s.fmt == S.FMT_INT8_G64:
+            cache.k_scales.view(torch.int16).fill_(POISON_F16)
+            cache.v_scales.view(torch.int16).fill_(POISON_F16)
+        else:
+            cache.k_scales.fill_(float("nan"))
+            cache.v_scales.fill_(float("nan"))
+    return cache
+
+
+def fill_gpu(K, w: S.Workload, cache, device, chunk: int = 8192, decode_rows: bool = True):
+    """Append every context row of every sequence: prefill chunks of `chunk` rows
+    (the last prefill chunk is w.shape.chunk rows if set), then the T decode rows
+    of all sequences in one batched call."""
+    s = w.shape
+    bt = torch.from_numpy(w.block_table).to(device)
+    for b in range(s.B):
+        L = int(w.seq_lens[b])
+        stop = L - s.T if decode_rows else L
+        edges = list(range(0, stop, chunk))
+        if s.chunk and stop > s.chunk:
+            edges = list(range(0, stop - s.chunk, chunk)) + [stop - s.chunk]
+        edges.append(stop)
+        for a0, a1 in zip(edges[:-1], edges[1:]):
+            if a1 <= a0:
+                continue
+            k = src_tensor(w.rows("k", b, a0, a1), s.src, device)
+            v = src_tensor(w.rows("v", b, a0, a1), s.src, device)
+            sp = torch.tensor([a0], dtype=torch.int32, device=device)
+            K.kv_append_quant(cache, k, v, bt[b:b + 1].contiguous(), sp)
+    if decode_rows:
+        k = src_tensor(w.new_rows("k"), s.src, device)
+        v = src_tensor(w.new_rows("v"), s.src, device)
+        sp = torch.from_numpy(w.seq_lens - s.T).to(device)
+        K.kv_append_quant(cache, k, v, bt, sp)
+    return bt
+
+
+def oracle_pool(O, w: S.Workload):
+    s = w.shape
+    pool = O.Pool(s.fmt, w.num_blocks, s.Hkv, s.D, fill=POISON_CODE)
+    if s.fmt == S.FMT_INT8_G64:
+        pool.k_scales[:] = POISON_F16
+        pool.v_scales[:] = POISON_F16
+    else:
+        pool.k_scales[:] = np.nan
+        pool.v_scales[:] = np.nan
+    for b in range(s.B):
+        L = int(w.seq_lens[b])
+        pool.append(w.rows("k", b, 0, L), w.rows("v", b, 0, L), s.src, w.block_table[b:b + 1],
+                    np.array([0], np.int32))
+    return pool
+
+
+def pool_equal(cache, pool) -> dict:
+    """Byte-exact comparison of the device pool with the oracle's pool; returns mismatch counts."""
+    res = {}
+    for name in ("k_codes", "v_codes", "k_scales", "v_scales"):
+        g = getattr(cache, name).cpu().numpy().view(np.uint8)
+        o = getattr(pool, name).view(np.uint8)
+        res[name] = int(np.count_nonzero(g != o))
+    return res
+
+
+def run_attn(K, w: S.Workload, cache, bt, device, q=None, stream=None):
+    s = w.shape
+    q = src_tensor(w.q, s.src, device) if q is None else q
+    sl = torch.from_numpy(w.seq_lens).to(device)
+    out = torch.empty(q.shape, dtype=torch.float32, device=device)
+    ws = K.alloc_workspace(cache, s.B, s.T, s.Hq, w.max_seq_len, device=device)
+    K.paged_decode_attn(cache, q, bt, sl, w.max_seq_len, w.softmax_scale, out, ws, stream=stream)
+    return out

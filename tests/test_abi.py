@@ -1,0 +1,107 @@
+"""The C-ABI library without a GPU: it loads, exports every declared call, and
+every invalid argument returns its documented status before anything runs."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def K():
+    import paged_attention_quantized_kv_amd as K
+    return K
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_function_is_exported(K):
+    names = _declared()
+    assert {"kv_append_quant", "paged_decode_attn", "paged_decode_attn_workspace_bytes",
+            "kvq_status_string"} <= set(names)
+    raw = C.CDLL(K.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_status_strings(K):
+    for s in (0, -1, -2, -3, -4, -5):
+        assert K.status_string(s).startswith("KVQ_")
+    assert K.status_string(-99) == "KVQ_ERR_UNKNOWN"
+
+
+def _desc(K, fmt=0, D=256, H=4, nblk=16, block=64, k=0x1000):
+    return K.CacheDesc(fmt, nblk, block, H, D, 0, k, 0x2000, 0x3000, 0x4000)
+
+
+def _append(K, d, B=1, n=4, dtype=1, kn=0x5000, vn=0x6000, bt=0x7000, mb=4, sp=0x8000):
+    return K.lib.kv_append_quant(C.byref(d), C.c_void_p(kn), C.c_void_p(vn), dtype, B, n, C.c_void_p(bt), mb,
+                                 C.c_void_p(sp), None)
+
+
+def _attn(K, d, q=0x5000, qdt=1, B=1, T=4, Hq=24, bt=0x7000, mb=4, sl=0x8000, L=256, scale=0.0625,
+          out=0x9000, ws=0xA000, wsb=1 << 30, fn="paged_decode_attn"):
+    return getattr(K.lib, fn)(C.byref(d), C.c_void_p(q), qdt, B, T, Hq, C.c_void_p(bt), mb, C.c_void_p(sl), L, scale,
+                              C.c_void_p(out), C.c_void_p(ws), wsb, None)
+
+
+def test_append_validation(K):
+    E = dict(inv=-1, uns=-2, cap=-4, launch=-5)
+    assert K.lib.kv_append_quant(None, None, None, 1, 1, 1, None, 1, None, None) == E["inv"]
+    assert _append(K, _desc(K, fmt=2)) == E["inv"]
+    assert _append(K, _desc(K, D=192)) == E["uns"]
+    assert _append(K, _desc(K, block=32)) == E["uns"]
+    assert _append(K, _desc(K, H=0)) == E["inv"]
+    assert _append(K, _desc(K, k=0x1004)) == E["inv"]  # misaligned pool
+    assert _append(K, _desc(K), dtype=7) == E["inv"]
+    assert _append(K, _desc(K), kn=0x5008) == E["inv"]
+    assert _append(K, _desc(K), bt=0) == E["inv"]
+    assert _append(K, _desc(K), sp=0x8002) == E["inv"]
+    assert _append(K, _desc(K), B=0) == E["inv"]
+    assert _append(K, _desc(K), n=-1) == E["inv"]
+    assert _append(K, _desc(K), n=4 * 64 + 1, mb=4) == E["cap"]
+    assert _append(K, _desc(K), n=0) == 0  # no-op, nothing launched
+    assert _append(K, _desc(K), B=2000) == E["uns"]
+    assert _append(K, _desc(K)) == E["launch"]  # valid: reaches the runtime, which has no device here
+
+
+@pytest.mark.parametrize("fn", ["paged_decode_attn", "paged_decode_attn_split", "paged_decode_attn_merge"])
+def test_attention_validation(K, fn):
+    d = _desc(K)
+    assert _attn(K, d, qdt=5, fn=fn) == -1
+    assert _attn(K, d, q=0x5001, fn=fn) == -1
+    assert _attn(K, d, out=0, fn=fn) == -1
+    assert _attn(K, d, ws=0xA008, fn=fn) == -1
+    assert _attn(K, d, sl=0x8001, fn=fn) == -1
+    assert _attn(K, d, scale=float("nan"), fn=fn) == -1
+    assert _attn(K, d, Hq=25, fn=fn) == -2  # not a multiple of Hkv
+    assert _attn(K, d, T=9, fn=fn) == -2
+    assert _attn(K, d, T=8, Hq=32, fn=fn) == -2  # 8 x 8 rows > 32
+    assert _attn(K, d, B=0, fn=fn) == -1
+    assert _attn(K, d, L=3, T=4, fn=fn) == -1  # fewer keys than query rows
+    assert _attn(K, d, L=257, mb=4, fn=fn) == -4
+    assert _attn(K, d, wsb=16, fn=fn) == -3
+    assert _attn(K, _desc(K, D=64), fn=fn) == -2
+    assert _attn(K, d, fn=fn) == -5
+
+
+def test_workspace_and_chunking_are_pure_functions_of_the_shape(K):
+    ws = K.workspace_bytes(1, 4, 24, 4, 256, 131072)
+    assert ws == K.workspace_bytes(1, 4, 24, 4, 256, 131072) > 0
+    n, tps = K.num_splits(1, 4, 24, 4, 256, 131072)
+    assert tps % 64 == 0 and n * tps >= 131072 and (n - 1) * tps < 131072
+    rows = 4 * 6
+    parts = 1 * 4 * n * rows
+    assert ws >= parts * 256 * 4 + parts * 2 * 4
+    assert K.workspace_bytes(1, 9, 24, 4, 256, 1024) == 0
+    assert K.num_splits(1, 9, 24, 4, 256, 1024) == (0, 0)
+    # about one workgroup per compute unit at the headline shapes
+    for L in (32768, 131072, 262144):
+        n, _ = K.num_splits(1, 1, 24, 4, 256, L)
+        assert n * 4 == 256

@@ -1,0 +1,206 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Codes and scales: byte-exact against the oracle's pool.  Attention: max-abs
+error <= 2e-3 against the oracle's fp64 result, element by element, on the
+same seeded inputs.  Small shapes cover several tiles and ragged tails; the
+full-size workloads compare the whole pool and sampled output rows.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kvq_synth as S
+import oracle as O
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 2e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests need an MI355X")
+    import paged_attention_quantized_kv_amd as K
+    return K
+
+
+def check(K, w, rows=None, chunk=8192):
+    s = w.shape
+    say(f"[parity] {s.name} B={s.B} T={s.T} Hq={s.Hq} Hkv={s.Hkv} D={s.D} lens={s.lens[:8]} fmt={s.fmt} src={s.src}")
+    cache = H.new_cache(K, w, DEV)
+    bt = H.fill_gpu(K, w, cache, DEV, chunk=chunk)
+    out = H.run_attn(K, w, cache, bt, DEV)
+    torch.cuda.synchronize()
+    pool = H.oracle_pool(O, w)
+    mism = H.pool_equal(cache, pool)
+    assert mism == {"k_codes": 0, "v_codes": 0, "k_scales": 0, "v_scales": 0}, mism
+    got = out.cpu().numpy().reshape(-1, s.D)
+    ref = pool.paged_attn(w.q, s.src, s.T, s.Hq, w.block_table, w.seq_lens, w.softmax_scale, rows=rows)
+    if rows is not None:
+        got = got[np.asarray(rows)]
+    assert np.all(np.isfinite(got))
+    err = float(np.abs(got - ref).max())
+    say(f"[parity] {s.name}: max-abs err {err:.3e} over {got.size} outputs")
+    assert err <= TOL
+    return cache, bt, out, err
+
+
+SMALL = {
+    "tiny": S.shape("tiny"),
+    "g6_t1_d256_bf16": S.tiny_shape(B=1, T=1, Hq=24, Hkv=4, D=256, lens=(1000,), src=S.SRC_BF16, outliers=True),
+    "g6_t4_d256_bf16": S.tiny_shape(B=1, T=4, Hq=24, Hkv=4, D=256, lens=(777,), src=S.SRC_BF16, outliers=True),
+    "ragged_b3_t4": S.tiny_shape(B=3, T=4, Hq=12, Hkv=2, D=256, lens=(4, 65, 300), src=S.SRC_BF16, outliers=True),
+    "mha_len1": S.tiny_shape(B=2, T=1, Hq=2, Hkv=2, D=256, lens=(1, 130), src=S.SRC_BF16),
+    "fp8_d128_f32": S.tiny_shape(B=2, T=2, Hq=8, Hkv=2, D=128, lens=(129, 64), src=S.SRC_F32, fmt=S.FMT_FP8_ROW),
+    "fp8_g6_t4_bf16": S.tiny_shape(B=1, T=4, Hq=24, Hkv=4, D=256, lens=(1500,), src=S.SRC_BF16,
+                                   fmt=S.FMT_FP8_ROW, outliers=True),
+    "rows32_d128": S.tiny_shape(B=2, T=8, Hq=8, Hkv=2, D=128, lens=(513, 70), src=S.SRC_BF16, outliers=True),
+    "g8_t2_d256_f32": S.tiny_shape(B=1, T=2, Hq=8, Hkv=1, D=256, lens=(2049,), src=S.SRC_F32),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_shapes(K, name):
+    w = S.make(SMALL[name], seed=S.seed_of("tiny") + 100 + list(SMALL).index(name))
+    check(K, w, chunk=100)
+
+
+def _sample_rows(w, n_per_seq):
+    s = w.shape
+    g = np.random.default_rng(7)
+    rows = []
+    for b in range(s.B):
+        for t in sorted({0, s.T - 1}):
+            hs = g.choice(s.Hq, size=min(n_per_seq, s.Hq), replace=False)
+            rows += [(b * s.T + t) * s.Hq + int(h) for h in hs]
+    return np.array(sorted(set(rows)), np.int32)
+
+
+def test_qwen32k_full(K):
+    check(K, S.make("qwen32k"))
+
+
+def test_mtp128k_sampled(K):
+    w = S.make("mtp128k")
+    check(K, w, rows=_sample_rows(w, 3))
+
+
+def test_cohort_c8_sampled(K):
+    w = S.make("c8")
+    check(K, w, rows=_sample_rows(w, 1))
+
+
+@pytest.mark.parametrize("name", ["full256k_int8", "full256k_fp8"])
+def test_full_native_context_sampled(K, name):
+    w = S.make(name)
+    check(K, w, rows=_sample_rows(w, 2), chunk=65536)
+
+
+def test_repeat_and_page_placement_are_bit_identical(K):
+    w = S.make(S.tiny_shape(B=2, T=4, Hq=24, Hkv=4, D=256, lens=(900, 333), src=S.SRC_BF16, outliers=True), seed=5)
+    cache = H.new_cache(K, w, DEV)
+    bt = H.fill_gpu(K, w, cache, DEV)
+    a = H.run_attn(K, w, cache, bt, DEV)
+    b = H.run_attn(K, w, cache, bt, DEV)
+    assert torch.equal(a, b)
+    # move every page to another physical block and rewrite the table
+    n, hkv, D = w.num_blocks, w.shape.Hkv, w.shape.D
+    perm = torch.roll(torch.arange(n), 5)
+    moved = H.new_cache(K, w, DEV)
+    for src_t, dst_t in zip(cache.tensors(), moved.tensors()):
+        per = src_t.numel() // n
+        dst_t.view(n, per)[perm.to(DEV)] = src_t.view(n, per)
+    bt2 = perm.to(DEV)[bt.long()].to(torch.int32).contiguous()
+    c = H.run_attn(K, w, moved, bt2, DEV)
+    assert torch.equal(a, c)
+
+
+def test_two_phase_equals_one_call_and_side_stream(K):
+    w = S.make(S.tiny_shape(B=1, T=4, Hq=24, Hkv=4, D=256, lens=(2000,), src=S.SRC_BF16, outliers=True), seed=6)
+    cache = H.new_cache(K, w, DEV)
+    bt = H.fill_gpu(K, w, cache, DEV)
+    one = H.run_attn(K, w, cache, bt, DEV)
+    s = w.shape
+    q = H.src_tensor(w.q, s.src, DEV)
+    sl = torch.from_numpy(w.seq_lens).to(DEV)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+        ws = K.alloc_workspace(cache, s.B, s.T, s.Hq, w.max_seq_len, device=DEV)
+        K.paged_decode_attn_split(cache, q, bt, sl, w.max_seq_len, w.softmax_scale, out, ws)
+        K.paged_decode_attn_merge(cache, q, bt, sl, w.max_seq_len, w.softmax_scale, out, ws)
+    st.synchronize()
+    assert torch.equal(one, out)
+
+
+def test_verify_rows_match_decode_at_shorter_lengths(K):
+    w = S.make(S.tiny_shape(B=1, T=4, Hq=24, Hkv=4, D=256, lens=(1234,), src=S.SRC_BF16, outliers=True), seed=8)
+    cache = H.new_cache(K, w, DEV)
+    bt = H.fill_gpu(K, w, cache, DEV)
+    out4 = H.run_attn(K, w, cache, bt, DEV).cpu()
+    q = H.src_tensor(w.q, w.shape.src, DEV)
+    for t in range(4):
+        L = 1234 - 4 + t + 1
+        sl = torch.tensor([L], dtype=torch.int32, device=DEV)
+        q1 = q[:, t:t + 1].contiguous()
+        out1 = torch.empty(q1.shape, dtype=torch.float32, device=DEV)
+        ws = K.alloc_workspace(cache, 1, 1, 24, L, device=DEV)
+        K.paged_decode_attn(cache, q1, bt, sl, L, w.softmax_scale, out1, ws)
+        assert float((out1.cpu()[0, 0] - out4[0, t]).abs().max()) <= 1e-5
+
+
+def test_bad_table_values_give_nan_rows_without_touching_others(K):
+    w = S.make(S.tiny_shape(B=3, T=1, Hq=8, Hkv=2, D=128, lens=(200, 300, 100), src=S.SRC_BF16), seed=9)
+    cache = H.new_cache(K, w, DEV)
+    bt = H.fill_gpu(K, w, cache, DEV)
+    good = H.run_attn(K, w, cache, bt, DEV)
+    s = w.shape
+    q = H.src_tensor(w.q, s.src, DEV)
+    bt_bad = bt.clone()
+    bt_bad[1, 2] = w.num_blocks + 7  # block id out of range in sequence 1
+    sl = torch.tensor([200, 300, 10 ** 6], dtype=torch.int32, device=DEV)  # sequence 2 too long
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    ws = K.alloc_workspace(cache, s.B, s.T, s.Hq, 300, device=DEV)
+    K.paged_decode_attn(cache, q, bt_bad, sl, 300, w.softmax_scale, out, ws)
+    assert torch.equal(out[0], good[0])
+    assert torch.isnan(out[1]).all() and torch.isnan(out[2]).all()
+    # appends with an out-of-range position or block id write nothing
+    before = [t.clone() for t in cache.tensors()]
+    k = torch.ones((1, 1, 2, 128), dtype=torch.bfloat16, device=DEV)
+    K.kv_append_quant(cache, k, k, bt[0:1].contiguous(), torch.tensor([10 ** 7], dtype=torch.int32, device=DEV))
+    bt_neg = torch.full((1, 4), -3, dtype=torch.int32, device=DEV)
+    K.kv_append_quant(cache, k, k, bt_neg, torch.tensor([0], dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    for a, b in zip(before, cache.tensors()):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_fp8_code_conversion_is_exact_for_every_code(K):
+    """Each finite E4M3FN code, stored as the single key of its own sequence with a
+    unit row scale, must come back exactly (one key: softmax weight 1)."""
+    D = 128
+    vals = O.e4m3fn_to_f32(np.arange(256, dtype=np.uint16).astype(np.uint8))
+    vals = vals[np.isfinite(vals)]
+    n = vals.size
+    shape = S.tiny_shape(B=n, T=1, Hq=1, Hkv=1, D=D, lens=(1,) * n, src=S.SRC_F32, fmt=S.FMT_FP8_ROW)
+    w = S.make(shape, seed=1)
+    for b in range(n):
+        row = np.zeros((1, 1, D), np.float32)
+        row[0, 0, 0] = 448.0  # absmax 448: the row scale is exactly 1
+        row[0, 0, 1] = vals[b]
+        w.v_src[b] = row
+        w.k_src[b] = np.zeros_like(row)
+    w.q[:] = 0
+    _, _, out, _ = check(K, w)
+    got = out.cpu().numpy()[:, 0, 0, :2]
+    assert np.array_equal(got[:, 0], np.full(n, 448.0, np.float32))
+    assert np.array_equal(got[:, 1], vals)

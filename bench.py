@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the quantized paged KV cache on one MI355X.
+
+One step = the decode hot path of one full-attention layer:
+  kv_append_quant of the T new rows of every sequence, then paged_decode_attn
+  (split kernel + log-sum-exp merge) over the whole context.
+The headline workload is the MTP3 verify step at 131,072 tokens (B=1, T=4,
+Hq=24, Hkv=4, D=256, INT8 group-64 KV); the JSON line also carries the 32K
+(T=1) and 262,144-token (T=1, INT8 and FP8-row) depths of the metric.
+
+Inputs are seeded synthetic data (kvq_synth) already resident in HBM.  Steps
+rotate over several copies of the page pool so the 256 MB Infinity Cache never
+holds the pool a step reads: every timed byte comes from HBM.
+
+Prints ONE JSON line.  --gpus N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+HEADLINE = "mtp128k"
+DEPTHS = ["qwen32k", "mtp128k", "full256k_int8", "full256k_fp8"]
+FLUSH_BYTES = 1.5 * 2 ** 30  # bytes read between two reads of one pool copy (> 256 MB MALL)
+
+
+def host_cpu():
+    model = platform.processor()
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+class Run:
+    """One workload: data on the device, n_copies pools, timed steps."""
+
+    def __init__(self, K, S, H, torch, name, device):
+        self.K, self.S, self.H, self.torch = K, S, H, torch
+        self.name, self.dev = name, device
+        w = S.make(name)
+        self.w = w
+        s = w.shape
+        cache = H.new_cache(K, w, device, poison=True)
+        self.bt = H.fill_gpu(K, w, cache, device, chunk=65536)
+        pool_bytes = cache.nbytes()
+        self.n_copies = int(min(64, max(2, math.ceil(FLUSH_BYTES / max(1, w.kv_bytes())) + 1)))
+        self.caches = [cache]
+        for _ in range(self.n_copies - 1):
+            c = K.Cache(s.fmt, w.num_blocks, s.Hkv, s.D, device=device)
+            for a, b in zip(cache.tensors(), c.tensors()):
+                b.copy_(a)
+            self.caches.append(c)
+        self.pool_bytes = pool_bytes
+        self.q = H.src_tensor(w.q, s.src, device)
+        self.k_new = H.src_tensor(w.new_rows("k"), s.src, device)
+        self.v_new = H.src_tensor(w.new_rows("v"), s.src, device)
+        self.start = torch.from_numpy(w.seq_lens - s.T).to(device)
+        self.sl = torch.from_numpy(w.seq_lens).to(device)
+        self.out = torch.empty(self.q.shape, dtype=torch.float32, device=device)
+        self.ws = K.alloc_workspace(cache, s.B, s.T, s.Hq, w.max_seq_len, device=device)
+        self.n_splits, self.tps = K.num_splits(s.B, s.T, s.Hq, s.Hkv, s.D, w.max_seq_len)
+        torch.cuda.synchronize()
+
+    def attn_args(self, i):
+        w = self.w
+        return (self.caches[i % self.n_copies], self.q, self.bt, self.sl, w.max_seq_len, w.softmax_scale, self.out,
+                self.ws)
+
+    def step(self, i):
+        """One decode step on pool copy i: append the T new rows, then split + merge."""
+        c = self.caches[i % self.n_copies]
+        self.K.kv_append_quant(c, self.k_new, self.v_new, self.bt, self.start)
+        self.K.paged_decode_attn_split(*self.attn_args(i))
+        self.K.paged_decode_attn_merge(*self.attn_args(i))
+
+    def build_graphs(self):
+        """HIP graphs (torch.cuda.CUDAGraph): one step per pool copy, all copies' steps
+        in order, and the split kernel alone over all copies."""
+        torch = self.torch
+        for i in range(self.n_copies):  # eager warm-up of every copy before capture
+            self.step(i)
+        torch.cuda.synchronize()
+        self.g_one = []
+        for i in range(self.n_copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(i)
+            self.g_one.append(g)
+        self.g_all = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g_all):
+            for i in range(self.n_copies):
+                self.step(i)
+        self.g_split = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g_split):
+            for i in range(self.n_copies):
+                self.K.paged_decode_attn_split(*self.attn_args(i))
+        torch.cuda.synchronize()
+
+    def measure_eager(self, steps, warmup):
+        """Plain stream launches, no graphs (for counter runs): every kernel is its own dispatch."""
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(warmup + i)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(self.n_copies):
+            self.K.paged_decode_attn_split(*self.attn_args(i))
+        e1.record()
+        torch.cuda.synchronize()
+        return wall_ms / steps, [e0.elapsed_time(e1) / self.n_copies]
+
+    def measure(self, steps, warmup, eager=False):
+        torch = self.torch
+        if eager:
+            return self.measure_eager(steps, warmup)
+        self.build_graphs()
+        for i in range(warmup):
+            self.g_one[i % self.n_copies].replay()
+        torch.cuda.synchronize()
+        full, rest = divmod(steps, self.n_copies)
+        t0 = time.perf_counter()
+        for _ in range(full):
+            self.g_all.replay()
+        for i in range(rest):
+            self.g_one[i].replay()
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3
+        # the split kernel alone: events on the replay stream around back-to-back launches
+        reps = max(1, steps // self.n_copies)
+        split_ms = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                self.g_split.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            split_ms.append(e0.elapsed_time(e1) / (reps * self.n_copies))
+        return wall_ms / steps, sorted(split_ms)
+
+    def algorithmic_split_bytes(self):
+        """Bytes the split kernel must move by definition: every visible key and value
+        (codes + scales), the block-table entries and the queries."""
+        s = self.w.shape
+        pages = sum(math.ceil(int(L) / 64) for L in self.w.seq_lens)
+        q_bytes = self.q.numel() * self.q.element_size()
+        return self.w.kv_bytes() + pages * 4 + q_bytes
+
+
+def cpu_baseline(S, H, name, rows_target_s=12.0):
+    """The oracle as it stands, single-threaded, on a bounded sample: a few query rows
+    of the same workload (each row re-reads its KV head's whole context, as the
+    oracle does for every row), scaled to the whole call."""
+    import numpy as np
+    import oracle as O
+
+    w = S.make(name)
+    s = w.shape
+    pool = H.oracle_pool(O, w)
+    total_rows = s.B * s.T * s.Hq
+    rows = []
+    t_sum = 0.0
+    for r in range(total_rows):
+        t0 = time.perf_counter()
+        pool.paged_attn(w.q, s.src, s.T, s.Hq, w.block_table, w.seq_lens, w.softmax_scale,
+                        rows=np.array([r], np.int32))
+        t_sum += time.perf_counter() - t0
+        rows.append(r)
+        if t_sum >= rows_target_s:
+            break
+    per_row = t_sum / len(rows)
+    call_s = per_row * total_rows
+    return {"value": round(w.kv_bytes() / call_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(rows)} of {total_rows} query rows of {name} (fp64 oracle, {per_row:.2f} s/row), "
+                      f"scaled to the whole call ({call_s:.1f} s)",
+            "tok_per_s": round(s.B * s.T / call_s, 4)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=HEADLINE, choices=["tiny", "qwen32k", "mtp128k", "c8", "full256k_int8",
+                                                             "full256k_fp8"])
+    ap.add_argument("--headline-only", action="store_true", help="skip the other depths")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch without HIP graphs (for counter collection)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before timing, copy a buffer of this many MiB once (a known-size kernel for counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is a design only)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kvq_synth as S
+    import paged_attention_quantized_kv_amd as K
+    from tests import gpu_harness as H
+
+    dev = "cuda:0"
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * 2 ** 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    names = [args.workload] if args.headline_only else [args.workload] + [d for d in DEPTHS if d != args.workload]
+    results = {}
+    for name in names:
+        print(f"[bench] {name}: generating and appending the context", file=sys.stderr, flush=True)
+        run = Run(K, S, H, torch, name, dev)
+        ms, split_ms = run.measure(args.steps, args.warmup, eager=args.eager)
+        w = run.w
+        s = w.shape
+        split_avg = sum(split_ms) / len(split_ms)
+        alg = run.algorithmic_split_bytes()
+        results[name] = {
+            "ms_per_step": ms,
+            "kv_gbs": w.kv_bytes() / (ms * 1e-3) / 1e9,
+            "tok_per_s": s.B * s.T / (ms * 1e-3),
+            "split_ms_avg": split_avg,
+            "split_ms_min": split_ms[0],
+            "split_ms_max": split_ms[-1],
+            "split_alg_bytes": alg,
+            "split_gbs": alg / (split_avg * 1e-3) / 1e9,
+            "kv_bytes": w.kv_bytes(),
+            "n_copies": run.n_copies,
+            "n_splits": run.n_splits,
+            "tokens_per_split": run.tps,
+        }
+        print(f"[bench] {name}: {ms * 1e3:.1f} us/step, split {split_avg * 1e3:.1f} us "
+              f"({results[name]['split_gbs']:.0f} GB/s), {run.n_copies} pool copies", file=sys.stderr, flush=True)
+        del run
+        torch.cuda.empty_cache()
+
+    head = results[args.workload]
+    shp = S.shape(args.workload)
+    model, ncpu = host_cpu()
+    line = {
+        "metric": "paged decode attention KV GB/s (% of HBM peak) and tok/s at 32K/128K/256K",
+        "value": round(head["kv_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16xf16->f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: B={shp.B} T={shp.T} Hq={shp.Hq} Hkv={shp.Hkv} D={shp.D} "
+                               f"L={shp.lens[0] if shp.B == 1 else 'ragged'} page=64 "
+                               f"{'INT8 g64' if shp.fmt == 0 else 'FP8 E4M3 row'} KV",
+                   "global_batch": shp.B * shp.T, "seq_len": shp.lens[0] if shp.B == 1 else max(shp.lens),
+                   "step": "kv_append_quant(T rows) + paged_decode_attn (split + merge)",
+                   "parallelism": "single GPU"},
+        "pct_hbm_peak": round(100 * head["kv_gbs"] / HBM_PEAK_GBS, 2),
+        "tok_per_s": round(head["tok_per_s"], 1),
+        "roofline": {"bound": "hbm", "achieved": round(head["split_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(head["split_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "attn_split_kernel", "launch_avg_us": round(head["split_ms_avg"] * 1e3, 2),
+                     "alg_bytes_per_launch": head["split_alg_bytes"]},
+        "depths": {n: {"kv_gbs": round(r["kv_gbs"], 1), "pct_hbm_peak": round(100 * r["kv_gbs"] / HBM_PEAK_GBS, 2),
+                       "tok_per_s": round(r["tok_per_s"], 1), "us_per_step": round(r["ms_per_step"] * 1e3, 2),
+                       "split_us": round(r["split_ms_avg"] * 1e3, 2), "split_gbs": round(r["split_gbs"], 1),
+                       "n_splits": r["n_splits"], "pool_copies": r["n_copies"]} for n, r in results.items()},
+        "host": {"cpu": model, "nproc": ncpu},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on a bounded sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(S, H, args.workload)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -84,8 +84,9 @@ typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype_t;
  *           (16x16-byte tiles of 16 slots x 16 dims, slot-major inside a tile)
  *   V byte  ((d/16) * 4 + run(s)) * 256 + (d%16) * 16 + pos(s)
  *           (dim-major: the 64 slots of one dim in four 16-byte runs)
- *   INT8 scale of (s, group g)  element (run(s) * G64 + g) * 16 + pos(s)
- *   FP8 scale of s              element run(s) * 16 + pos(s)
+ *   INT8 K scale of (s, group g)  element ((run(s) * 4 + s/16) * G64 + g) * 4 + s%4
+ *   INT8 V scale of (s, group g)  element (run(s) * G64 + g) * 16 + pos(s)
+ *   FP8 K or V scale of s         element run(s) * 16 + pos(s)
  * These orders make every 64-lane load of the attention kernel one contiguous
  * 1 KiB segment that lands directly in matrix-core operand registers.
  */

@@ -59,7 +59,7 @@ def lib():
         L.orc_k_byte.restype = i64
         L.orc_v_byte.argtypes = [i32, i32, i32]
         L.orc_v_byte.restype = i64
-        L.orc_scale_elem.argtypes = [i32, i32, i32, i32]
+        L.orc_scale_elem.argtypes = [i32, i32, i32, i32, i32]
         L.orc_scale_elem.restype = i64
         L.orc_append.argtypes = [C.POINTER(_Pool), vp, vp, i32, i32, i32, vp, i32, vp]
         L.orc_append.restype = i32
@@ -140,8 +140,8 @@ def v_byte(s: int, d: int, D: int) -> int:
     return lib().orc_v_byte(s, d, D)
 
 
-def scale_elem(fmt: int, s: int, g: int, D: int) -> int:
-    return lib().orc_scale_elem(fmt, s, g, D)
+def scale_elem(fmt: int, which: int, s: int, g: int, D: int) -> int:
+    return lib().orc_scale_elem(fmt, which, s, g, D)
 
 
 # ---------------------------------------------------------------- pool

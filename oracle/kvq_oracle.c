@@ -202,12 +202,16 @@ int64_t orc_v_byte(int s, int d, int D) {
   return ((int64_t)(d / 16) * 4 + r) * 256 + (d % 16) * 16 + (s / 16) * 4 + (s % 4);
 }
 
-/* Scales follow the same slot runs: run r = (s % 16) / 4 is the slowest index. */
-int64_t orc_scale_elem(int fmt, int s, int g, int D) {
-  int r = (s % 16) / 4;
-  int pos = (s / 16) * 4 + (s % 4);
-  if (fmt == ORC_FMT_INT8_G64) return ((int64_t)r * (D / 64) + g) * 16 + pos;
-  return (int64_t)r * 16 + pos;
+/* Scales follow the same slot runs: run r = (s % 16) / 4 is the slowest index.
+ * INT8 K scales: (run, s/16, group, s%4); INT8 V scales: (run, group, s/16, s%4);
+ * FP8 scales (K and V): (run, s/16, s%4). */
+int64_t orc_scale_elem(int fmt, int which, int s, int g, int D) {
+  int r = (s % 16) / 4, j = s / 16, i = s % 4;
+  if (fmt == ORC_FMT_INT8_G64) {
+    if (which == 0) return (((int64_t)r * 4 + j) * (D / 64) + g) * 4 + i;
+    return ((int64_t)r * (D / 64) + g) * 16 + j * 4 + i;
+  }
+  return (int64_t)r * 16 + j * 4 + i;
 }
 
 static int64_t page_index(const orc_pool *p, int block, int kvh) {
@@ -251,12 +255,12 @@ int orc_append(const orc_pool *p, const void *k_new, const void *v_new, int src_
           if (p->format == ORC_FMT_INT8_G64) {
             orc_quant_int8_g64(x, D, (int8_t *)codes, s16);
             uint16_t *sc = (uint16_t *)pool_scales + pg * 64 * G;
-            for (int g = 0; g < G; ++g) sc[orc_scale_elem(p->format, slot, g, D)] = s16[g];
+            for (int g = 0; g < G; ++g) sc[orc_scale_elem(p->format, which, slot, g, D)] = s16[g];
           } else {
             float s;
             orc_quant_fp8_row(x, D, codes, &s);
             float *sc = (float *)pool_scales + pg * 64;
-            sc[orc_scale_elem(p->format, slot, 0, D)] = s;
+            sc[orc_scale_elem(p->format, which, slot, 0, D)] = s;
           }
           for (int d = 0; d < D; ++d)
             page[which ? orc_v_byte(slot, d, D) : orc_k_byte(slot, d, D)] = codes[d];
@@ -278,10 +282,10 @@ double orc_dequant(const orc_pool *p, int which, int block, int kvh, int slot, i
   uint8_t byte = page[which ? orc_v_byte(slot, d, D) : orc_k_byte(slot, d, D)];
   const void *scales = which ? p->v_scales : p->k_scales;
   if (p->format == ORC_FMT_INT8_G64) {
-    uint16_t h = ((const uint16_t *)scales)[pg * 64 * (D / 64) + orc_scale_elem(p->format, slot, d / 64, D)];
+    uint16_t h = ((const uint16_t *)scales)[pg * 64 * (D / 64) + orc_scale_elem(p->format, which, slot, d / 64, D)];
     return (double)(int8_t)byte * (double)orc_f16_to_f32(h);
   }
-  float s = ((const float *)scales)[pg * 64 + orc_scale_elem(p->format, slot, 0, D)];
+  float s = ((const float *)scales)[pg * 64 + orc_scale_elem(p->format, which, slot, 0, D)];
   return (double)orc_e4m3fn_to_f32(byte) * (double)s;
 }
 

@@ -52,9 +52,10 @@ void orc_quant_fp8_row(const float *x, int D, uint8_t *codes, float *scale);
 /* Byte offset of (token slot s, dim d) inside one (block, kv head) page. */
 int64_t orc_k_byte(int s, int d, int D);
 int64_t orc_v_byte(int s, int d, int D);
-/* Element index of the scale of (slot s, 64-group g) inside one page
- * (INT8: D/64 scales per slot), or of slot s (FP8: one per slot, pass g=0). */
-int64_t orc_scale_elem(int fmt, int s, int g, int D);
+/* Element index of the scale of K (which=0) or V (which=1) for (slot s,
+ * 64-group g) inside one page (INT8: D/64 scales per slot), or of slot s (FP8:
+ * one per slot, pass g=0). */
+int64_t orc_scale_elem(int fmt, int which, int s, int g, int D);
 
 typedef struct {
   int32_t format; /* ORC_FMT_* */

@@ -90,7 +90,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     if ((lane % LPG) == 0) {
       const int g = lane / LPG;
       _Float16 *sc = static_cast<_Float16 *>(which ? a.v_scales : a.k_scales) + page * D;
-      sc[(run * E + g) * 16 + spos] = s16;
+      // K: (run, slot/16, group, slot%4); V: (run, group, slot/16, slot%4)
+      const int e = which ? (run * E + g) * 16 + spos : ((run * 4 + slot / 16) * E + g) * 4 + slot % 4;
+      sc[e] = s16;
     }
   } else {  // FP8 E4M3FN, one fp32 scale per row
     float amax = 0.0f;

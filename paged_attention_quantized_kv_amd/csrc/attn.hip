@@ -6,18 +6,25 @@
 // chunks (split-K over the context) whose partial results are merged with
 // log-sum-exp weights.
 //
-// Split kernel: one workgroup = 4 independent waves on one chunk of one
-// (sequence, KV head); the waves take the chunk's pages round-robin.  All
-// T*G query rows of the KV head (T new tokens x G query heads of the group)
-// ride along as the N dimension of 16x16x32 f16 matrix-core products, so every
-// KV byte is read once:
+// Split kernel: a workgroup owns one chunk of one (sequence, KV head) and runs
+// NTEAM teams of 4 waves; team t takes the chunk's pages t, t+NTEAM, ...  The
+// 4 waves of a team share each page: wave w computes the scores of key tile w
+// (16 keys) and accumulates the output for dim quarter w, so a wave holds a
+// quarter of the page and a quarter of the output.  All T*G query rows of the
+// KV head (T new tokens x G query heads of the group) ride along as the N
+// dimension of 16x16x32 f16 matrix-core products, so every KV byte is read once:
 //   S^T[key][row] = K[key][dim] * Q^T[dim][row]   (A = K codes, B = Q)
 //   O^T[dim][row] = V^T[dim][key] * P^T[key][row] (A = V codes, B = softmax weights)
-// K/V codes are converted to f16 exactly (int8 via byte permutes and one
-// packed subtract, FP8 via the hardware converter); queries and softmax
-// weights enter as f16 hi+lo pairs, so the only rounding is fp32 summation.
-// The page layout (kvq.h) makes each 64-lane 16-byte load one contiguous KiB
-// that lands in the operand registers with no LDS staging.
+// Per page the team exchanges row maxima and softmax weights through LDS (two
+// barriers); the next page's codes and scales are already in flight in a
+// second register buffer.  K/V codes are converted to f16 exactly (int8 via
+// byte permutes and one packed subtract, FP8 via the hardware converter);
+// softmax weights enter as f16 hi+lo pairs, fp32 queries as hi+lo, bf16
+// queries as one f16 (exact in f16's normal range), so the rounding is fp32
+// summation.  The page layout (kvq.h) makes each 64-lane 16-byte load one
+// contiguous KiB that lands in the operand registers.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace kvq {
@@ -68,30 +75,88 @@ __device__ inline void split_f16(float x0, float x1, f16x2 &hi, f16x2 &lo) {
                                                             x1 - static_cast<float>(hi[1])));
 }
 
-template <int QDT>
+// Element i of the query tensor, widened to fp32 (bf16 widening is exact).
+template <bool BF16>
 __device__ inline float load_q(const void *q, size_t i) {
-  if constexpr (QDT == 1) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(q)[i]) << 16);
+  if constexpr (BF16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(q)[i]) << 16);
   return static_cast<const float *>(q)[i];
 }
 
 __device__ inline f16x8 lds_f16x8(const uint4 *p) { return __builtin_bit_cast(f16x8, *p); }
 
-// Split kernel.  D: head_dim; NT: 16-row tiles of query rows (rows = T*G);
-// FMT: 0 = INT8 g64, 1 = FP8 row; QDT: 0 = fp32 q, 1 = bf16 q.
-template <int D, int NT, int FMT, int QDT>
-__global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
-  constexpr int G64 = D / 64;  // 64-dim groups
-  constexpr int NCH = D / 16;  // 16-dim chunks (= output dim tiles)
-  constexpr int ROWS = 16 * NT;
-  constexpr int QS_U4 = NT * G64 * 2 * 2 * 64;          // Q operand entries (uint4)
-  constexpr int O_STRIDE = D + 4;                        // padded LDS row of the merge buffer
-  constexpr int O_FLOATS = ROWS * O_STRIDE;
-  constexpr int SM_U4 = (QS_U4 * 4 > O_FLOATS ? QS_U4 * 4 : O_FLOATS) / 4;
-  __shared__ uint4 smem[SM_U4];
-  __shared__ float lds_m[kWaves][ROWS];
-  __shared__ float lds_l[kWaves][ROWS];
+// 2^x with the hardware exponential: exact at 0 and -inf; results below the
+// normal range (weights under 2^-126 of the running maximum) may flush to zero.
+__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// One wave's share of one page: its K tile (16 keys x all dims) and its V dim
+// tiles (all 64 keys), with their scales.
+template <int D, int FMT>
+struct PageRegs {
+  static constexpr int G64 = D / 64, DPW = D / 64;  // dim tiles per wave = D/16/4
+  static constexpr int KSN = (FMT == 0) ? (D / 128) : 1, VSN = (FMT == 0) ? 2 : 4;
+  uint4 k[G64];
+  uint4 v[DPW];
+  uint4 ks[KSN];
+  uint4 vs[VSN];
+};
+
+template <int D, int FMT>
+__device__ inline void load_page(PageRegs<D, FMT> &r, const AttnArgs &a, int pg_any, int wave, int lane, int q4) {
+  constexpr int G64 = D / 64, NCH = D / 16, DPW = D / 64;
+  const size_t pg = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pg_any));  // wave-uniform page
+  const uint4 *kp = reinterpret_cast<const uint4 *>(a.k_codes + pg * kPage * D);
+  const uint4 *vp = reinterpret_cast<const uint4 *>(a.v_codes + pg * kPage * D);
+#pragma unroll
+  for (int cg = 0; cg < G64; ++cg) r.k[cg] = kp[(wave * NCH + 4 * cg) * 16 + lane];
+#pragma unroll
+  for (int j = 0; j < DPW; ++j) r.v[j] = vp[(wave * DPW + j) * 64 + lane];
+  if constexpr (FMT == 0) {
+    const uint4 *ksp = reinterpret_cast<const uint4 *>(static_cast<const _Float16 *>(a.k_scales) + pg * D);
+    const uint4 *vsp = reinterpret_cast<const uint4 *>(static_cast<const _Float16 *>(a.v_scales) + pg * D);
+    const int g = (wave * DPW) / 4;  // the 64-dim group of this wave's dims
+#pragma unroll
+    for (int j = 0; j < PageRegs<D, FMT>::KSN; ++j) r.ks[j] = ksp[(q4 * 4 + wave) * PageRegs<D, FMT>::KSN + j];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) r.vs[j] = vsp[(q4 * G64 + g) * 2 + j];
+  } else {
+    const uint4 *ksp = reinterpret_cast<const uint4 *>(static_cast<const float *>(a.k_scales) + pg * kPage);
+    const uint4 *vsp = reinterpret_cast<const uint4 *>(static_cast<const float *>(a.v_scales) + pg * kPage);
+    r.ks[0] = ksp[q4 * 4 + wave];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.vs[j] = vsp[q4 * 4 + j];
+  }
+}
+
+__device__ inline void f16x2_to_f32(uint32_t w, float &x, float &y) {
+  const f16x2 h = __builtin_bit_cast(f16x2, w);
+  x = static_cast<float>(h[0]);
+  y = static_cast<float>(h[1]);
+}
+
+template <int D, int NT, int NTEAM, int QP>
+struct Smem {
+  static constexpr int ROWS = 16 * NT, PST = 64 + 4, G64 = D / 64;
+  static constexpr int QS = NT * G64 * 2 * QP * 64;            // Q operand entries (uint4)
+  static constexpr int PB = NTEAM * 2 * ROWS * PST;             // softmax-weight exchange (floats)
+  static constexpr int FIN = (NTEAM > 1 ? NTEAM - 1 : 1) * ROWS * (D + 4);  // team merge (floats), aliases pb
+  static constexpr int PBF = PB > FIN ? PB : FIN;
+};
+
+template <int D, int NT, int FMT, int QLO, int NTEAM>
+__global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) {
+  constexpr int G64 = D / 64, NCH = D / 16, DPW = D / 64;
+  constexpr int QP = QLO ? 2 : 1;
+  using SM = Smem<D, NT, NTEAM, QP>;
+  constexpr int ROWS = SM::ROWS, PST = SM::PST;
+  __shared__ uint4 qs[SM::QS];
+  __shared__ float4 pbuf4[SM::PBF / 4];
+  __shared__ float lds_mx[NTEAM][2][4][ROWS];
+  __shared__ float lds_l[NTEAM][4][ROWS];
+  __shared__ float lds_m[NTEAM][ROWS];
+  __shared__ int32_t lds_pg[kMaxChunkPages];  // pool page (block * Hkv + kvh) of each page of the chunk
+  float *pbuf = reinterpret_cast<float *>(pbuf4);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = (tid >> 6) & 3, team = tid >> 8;
   const int q4 = lane >> 4, c16 = lane & 15;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int L = a.seq_lens[b];
@@ -102,376 +167,439 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   const int page0 = tok0 / kPage, page1 = (tok1 + kPage - 1) / kPage;
   const int R = a.rows;
 
-  // ---- queries -> LDS in B-operand order: entry (nt, cg, half, hl, lane) holds
-  // dims 64cg + 16(lane/16) + 8half + 0..7 of row 16nt + lane%16, as f16 hi (hl=0) or lo (hl=1).
-  for (int e = threadIdx.x; e < NT * G64 * 2 * 64; e += 256) {
-    const int ln = e & 63, half = (e >> 6) & 1, cg = (e >> 7) % G64, nt = (e >> 7) / G64;
+  // ---- queries -> LDS in B-operand order: entry (nt, cg, hk, hl, lane) holds dims
+  // 64cg + 16(lane/16) + 8hk + 0..7 of row 16nt + lane%16, as f16 hi (hl=0) or lo (hl=1).
+  for (int e = tid; e < NT * G64 * 2 * 64; e += 256 * NTEAM) {
+    const int ln = e & 63, hk = (e >> 6) & 1, cg = (e >> 7) % G64, nt = (e >> 7) / G64;
     const int r = 16 * nt + (ln & 15);
-    const int d0 = 64 * cg + 16 * (ln >> 4) + 8 * half;
+    const int d0 = 64 * cg + 16 * (ln >> 4) + 8 * hk;
     f16x2 hi[4], lo[4];
     if (r < R) {
-      const int t = r / a.group, h = kvh * a.group + r % a.group;
-      const size_t qb = ((static_cast<size_t>(b) * a.T + t) * a.num_q_heads + h) * D + d0;
+      const int t = r / a.group, hq = kvh * a.group + r % a.group;
+      const size_t qb = ((static_cast<size_t>(b) * a.T + t) * a.num_q_heads + hq) * D + d0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) split_f16(load_q<QDT>(a.q, qb + 2 * j), load_q<QDT>(a.q, qb + 2 * j + 1), hi[j], lo[j]);
+      for (int j = 0; j < 4; ++j) {
+        // QLO is set exactly for fp32 queries; bf16 queries need no lo part
+        const float x0 = load_q<!QLO>(a.q, qb + 2 * j), x1 = load_q<!QLO>(a.q, qb + 2 * j + 1);
+        if constexpr (QLO) {
+          split_f16(x0, x1, hi[j], lo[j]);
+        } else {
+          hi[j] = f16x2{static_cast<_Float16>(x0), static_cast<_Float16>(x1)};  // RNE; exact for bf16 in range
+          lo[j] = f16x2{0, 0};
+        }
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) hi[j] = lo[j] = f16x2{0, 0};
     }
-    const int idx = (((nt * G64 + cg) * 2 + half) * 2) * 64 + ln;
-    smem[idx] = __builtin_bit_cast(uint4, f16x8{hi[0][0], hi[0][1], hi[1][0], hi[1][1], hi[2][0], hi[2][1], hi[3][0], hi[3][1]});
-    smem[idx + 64] = __builtin_bit_cast(uint4, f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]});
+    const int idx = ((nt * G64 + cg) * 2 + hk) * QP * 64 + ln;
+    qs[idx] = __builtin_bit_cast(uint4, f16x8{hi[0][0], hi[0][1], hi[1][0], hi[1][1], hi[2][0], hi[2][1], hi[3][0], hi[3][1]});
+    if constexpr (QLO)
+      qs[idx + 64] = __builtin_bit_cast(uint4, f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]});
   }
-  __syncthreads();
+  // ---- the chunk's block ids -> pool pages in LDS (an invalid id reads block 0 and flags the chunk)
+  bool bad = false;
+  {
+    const int32_t *bt = a.block_table + static_cast<size_t>(b) * a.max_blocks;
+    for (int i = tid; i < page1 - page0; i += 256 * NTEAM) {
+      const int blk = bt[page0 + i];
+      const bool ok = (blk >= 0) && (blk < a.num_blocks);
+      bad |= !ok;
+      lds_pg[i] = (ok ? blk : 0) * a.num_kv_heads + kvh;
+    }
+  }
+  bad = __syncthreads_or(bad ? 1 : 0) != 0;
 
-  // Per-lane state: this lane's query row is 16nt + c16 in every tile.
+  // ---- per-lane state; this lane's query row is 16nt + c16
   float m[NT], lsum[NT];
-  f32x4 o[NT][NCH];
+  int last[NT];
+  f32x4 o[NT][DPW];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     m[nt] = -INFINITY;
     lsum[nt] = 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < NCH; ++dt) o[nt][dt] = f32x4{0, 0, 0, 0};
-  }
-  // last visible key of this lane's row in each tile (-1: padding row, sees nothing)
-  int last[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
     const int r = 16 * nt + c16;
-    last[nt] = (r < R) ? (L - a.T + r / a.group) : -1;
+    last[nt] = (r < R) ? (L - a.T + r / a.group) : -1;  // -1: padding row, sees nothing
+#pragma unroll
+    for (int j = 0; j < DPW; ++j) o[nt][j] = f32x4{0, 0, 0, 0};
   }
-  bool bad = false;
+  const int n_it = (page1 - page0 + NTEAM - 1) / NTEAM;
+  // pool page of iteration it for this team (clamped: iterations past the team's last
+  // page reload that page and skip the math)
+  auto page_of = [&](int it) -> int { return lds_pg[min(it * NTEAM + team, page1 - page0 - 1)]; };
 
-  for (int p = page0 + wave; p < page1; p += kWaves) {
-    const int blk = a.block_table[static_cast<size_t>(b) * a.max_blocks + p];
-    if (blk < 0 || blk >= a.num_blocks) {
-      bad = true;
-      continue;
+  // ---- phase 1: scores of this wave's 16 keys (S^T = K Q^T), in log2 units, and their row maxima
+  auto scores = [&](auto masked_tag, PageRegs<D, FMT> &pr, int p, float (&z)[NT][4], float (&mloc)[NT]) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int key0 = p * kPage + 16 * wave + 4 * q4;  // key of i is key0 + i
+    f32x4 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      acc[nt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[nt][i] = 0.0f;
     }
-    const size_t pg = static_cast<size_t>(blk) * a.num_kv_heads + kvh;
-    const uint4 *kp = reinterpret_cast<const uint4 *>(a.k_codes + pg * kPage * D);
-    const uint4 *vp = reinterpret_cast<const uint4 *>(a.v_codes + pg * kPage * D);
-
-    // ---- loads: K tile (kt, cg) and V dim tile dt are each one contiguous KiB
-    uint4 kr[4][G64], vr[NCH];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int cg = 0; cg < G64; ++cg) kr[kt][cg] = kp[(kt * NCH + 4 * cg) * 16 + lane];
-#pragma unroll
-    for (int dt = 0; dt < NCH; ++dt) vr[dt] = vp[dt * 64 + lane];
-    // scales of this lane group's 16 keys (key 16kt + 4q4 + i at position 4kt + i)
-    uint4 ks[FMT == 0 ? G64 * 2 : 4], vs[FMT == 0 ? G64 * 2 : 4];
-    if constexpr (FMT == 0) {
-      const uint4 *ksp = reinterpret_cast<const uint4 *>(static_cast<const _Float16 *>(a.k_scales) + pg * D);
-      const uint4 *vsp = reinterpret_cast<const uint4 *>(static_cast<const _Float16 *>(a.v_scales) + pg * D);
-#pragma unroll
-      for (int j = 0; j < G64 * 2; ++j) {
-        ks[j] = ksp[q4 * G64 * 2 + j];
-        vs[j] = vsp[q4 * G64 * 2 + j];
-      }
-    } else {
-      const uint4 *ksp = reinterpret_cast<const uint4 *>(static_cast<const float *>(a.k_scales) + pg * kPage);
-      const uint4 *vsp = reinterpret_cast<const uint4 *>(static_cast<const float *>(a.v_scales) + pg * kPage);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ks[j] = ksp[q4 * 4 + j];
-        vs[j] = vsp[q4 * 4 + j];
-      }
-    }
-    const int key0 = p * kPage + 4 * q4;  // key of (kt, i) is key0 + 16kt + i
-    const bool full = (p * kPage + kPage - 1) <= (L - a.T);  // every real row sees every key
-
-    if (!full) {
-      // slots at or past L may hold anything (never written): zero their V codes
-      uint32_t mw[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w |= (key0 + 16 * kt + i < L) ? (0xFFu << (8 * i)) : 0u;
-        mw[kt] = w;
-      }
-#pragma unroll
-      for (int dt = 0; dt < NCH; ++dt) {
-        vr[dt].x &= mw[0];
-        vr[dt].y &= mw[1];
-        vr[dt].z &= mw[2];
-        vr[dt].w &= mw[3];
-      }
-    }
-
-    // ---- S^T = K Q^T
-    float z[NT][4][4];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) z[nt][kt][i] = 0.0f;
-    f32x4 acc[NT][4];
 #pragma unroll
     for (int cg = 0; cg < G64; ++cg) {
-      if (FMT == 0 || cg == 0) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt) acc[nt][kt] = f32x4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        f16x8 qh[NT], ql[NT];
+      for (int hk = 0; hk < 2; ++hk) {
+        const f16x8 ka = hk ? codes_to_f16<FMT>(pr.k[cg].z, pr.k[cg].w) : codes_to_f16<FMT>(pr.k[cg].x, pr.k[cg].y);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const int idx = (((nt * G64 + cg) * 2 + half) * 2) * 64 + lane;
-          qh[nt] = lds_f16x8(&smem[idx]);
-          ql[nt] = lds_f16x8(&smem[idx + 64]);
-        }
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const f16x8 ka = half ? codes_to_f16<FMT>(kr[kt][cg].z, kr[kt][cg].w) : codes_to_f16<FMT>(kr[kt][cg].x, kr[kt][cg].y);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            acc[nt][kt] = mfma16(ka, qh[nt], acc[nt][kt]);
-            acc[nt][kt] = mfma16(ka, ql[nt], acc[nt][kt]);
-          }
+          const int idx = ((nt * G64 + cg) * 2 + hk) * QP * 64 + lane;
+          acc[nt] = mfma16(ka, lds_f16x8(&qs[idx]), acc[nt]);
+          if constexpr (QLO) acc[nt] = mfma16(ka, lds_f16x8(&qs[idx + 64]), acc[nt]);
         }
       }
-      if constexpr (FMT == 0) {
-        // fold the fp16 group scale of each key
+      if constexpr (FMT == 0) {  // fold each key's fp16 group scale, restart the group sum
+        const uint4 w = pr.ks[cg >> 1];
+        float sk[4];
+        f16x2_to_f32((cg & 1) ? w.z : w.x, sk[0], sk[1]);
+        f16x2_to_f32((cg & 1) ? w.w : w.y, sk[2], sk[3]);
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const uint4 sw = ks[cg * 2 + (kt >> 1)];
-          const uint32_t s01 = (kt & 1) ? sw.z : sw.x, s23 = (kt & 1) ? sw.w : sw.y;
-          const f16x2 sa = __builtin_bit_cast(f16x2, s01), sb = __builtin_bit_cast(f16x2, s23);
-          const float sk[4] = {static_cast<float>(sa[0]), static_cast<float>(sa[1]), static_cast<float>(sb[0]),
-                               static_cast<float>(sb[1])};
+        for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) z[nt][kt][i] += sk[i] * acc[nt][kt][i];
+          for (int i = 0; i < 4; ++i) z[nt][i] += sk[i] * acc[nt][i];
+          acc[nt] = f32x4{0, 0, 0, 0};
         }
       }
     }
     if constexpr (FMT == 1) {
+      const float sk[4] = {__uint_as_float(pr.ks[0].x), __uint_as_float(pr.ks[0].y), __uint_as_float(pr.ks[0].z),
+                           __uint_as_float(pr.ks[0].w)};
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const uint4 sw = ks[kt];
-        const float sk[4] = {__uint_as_float(sw.x), __uint_as_float(sw.y), __uint_as_float(sw.z), __uint_as_float(sw.w)};
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) z[nt][kt][i] = sk[i] * acc[nt][kt][i];
-      }
+        for (int i = 0; i < 4; ++i) z[nt][i] = sk[i] * acc[nt][i];
     }
-
-    // ---- online softmax (log2 domain), per row = per lane column
-    float pw[NT][4][4];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = z[nt][kt][i] * a.qk_scale_log2;
-          if (!full) v = (key0 + 16 * kt + i <= last[nt]) ? v : -INFINITY;
-          z[nt][kt][i] = v;
-          mx = fmaxf(mx, v);
-        }
+      for (int i = 0; i < 4; ++i) {
+        float v = z[nt][i] * a.qk_scale_log2;
+        if constexpr (MASKED) v = (key0 + i <= last[nt]) ? v : -INFINITY;
+        z[nt][i] = v;
+        mx = fmaxf(mx, v);
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[nt], mx);
-      const float msafe = (mnew == -INFINITY) ? 0.0f : mnew;
-      const float alpha = exp2f(m[nt] - msafe);
-      m[nt] = mnew;
-      float ps = 0.0f;
+      mloc[nt] = mx;
+    }
+  };
+
+  // ---- phase 3: O^T += V^T P^T for this wave's dim tiles; each key's V scale folded into its weight
+  auto accumulate = [&](auto masked_tag, PageRegs<D, FMT> &pr, int p, const float *pb) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    if constexpr (MASKED) {
+      // slots at or past L may hold anything (never written): zero their V codes
+      const int kbase = p * kPage + 4 * q4;  // key of (kt, i) is kbase + 16kt + i
+      uint32_t mw[4];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < 4; ++kt) {
+        uint32_t wv = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pw[nt][kt][i] = exp2f(z[nt][kt][i] - msafe);
-          ps += pw[nt][kt][i];
-        }
-      lsum[nt] = lsum[nt] * alpha + ps;
-      if (__any(alpha != 1.0f)) {
+        for (int i = 0; i < 4; ++i) wv |= (kbase + 16 * kt + i < L) ? (0xFFu << (8 * i)) : 0u;
+        mw[kt] = wv;
+      }
 #pragma unroll
-        for (int dt = 0; dt < NCH; ++dt) o[nt][dt] *= alpha;
+      for (int j = 0; j < DPW; ++j) {
+        pr.v[j].x &= mw[0];
+        pr.v[j].y &= mw[1];
+        pr.v[j].z &= mw[2];
+        pr.v[j].w &= mw[3];
       }
     }
-
-    // ---- O^T += V^T P^T, with each key's V scale folded into its weight
 #pragma unroll
-    for (int cg = 0; cg < G64; ++cg) {
-      f16x8 bh[NT][2], bl[NT][2];
-      if (FMT == 0 || cg == 0) {
+    for (int ks = 0; ks < 2; ++ks) {
+      f16x8 bh[NT], bl[NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt) {
+        f16x2 hi[4], lo[4];
 #pragma unroll
-          for (int ks2 = 0; ks2 < 2; ++ks2) {
-            f16x2 h[4], l[4];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-              const int kt = 2 * ks2 + kk;
-              float sv[4];
-              if constexpr (FMT == 0) {
-                const uint4 sw = vs[cg * 2 + (kt >> 1)];
-                const uint32_t s01 = (kt & 1) ? sw.z : sw.x, s23 = (kt & 1) ? sw.w : sw.y;
-                const f16x2 sa = __builtin_bit_cast(f16x2, s01), sb = __builtin_bit_cast(f16x2, s23);
-                sv[0] = static_cast<float>(sa[0]);
-                sv[1] = static_cast<float>(sa[1]);
-                sv[2] = static_cast<float>(sb[0]);
-                sv[3] = static_cast<float>(sb[1]);
-              } else {
-                const uint4 sw = vs[kt];
-                sv[0] = __uint_as_float(sw.x);
-                sv[1] = __uint_as_float(sw.y);
-                sv[2] = __uint_as_float(sw.z);
-                sv[3] = __uint_as_float(sw.w);
-              }
-              float pv[4];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                pv[i] = pw[nt][kt][i] * sv[i];
-                if (!full) pv[i] = (pw[nt][kt][i] != 0.0f) ? pv[i] : 0.0f;  // unwritten slots: NaN scales
-              }
-              split_f16(pv[0], pv[1], h[2 * kk], l[2 * kk]);
-              split_f16(pv[2], pv[3], h[2 * kk + 1], l[2 * kk + 1]);
-            }
-            bh[nt][ks2] = f16x8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
-            bl[nt][ks2] = f16x8{l[0][0], l[0][1], l[1][0], l[1][1], l[2][0], l[2][1], l[3][0], l[3][1]};
+        for (int kk = 0; kk < 2; ++kk) {
+          const int kt = 2 * ks + kk;
+          const float4 pw = *reinterpret_cast<const float4 *>(pb + (16 * nt + c16) * PST + 16 * kt + 4 * q4);
+          float sv[4];
+          if constexpr (FMT == 0) {
+            const uint4 w = pr.vs[ks];
+            f16x2_to_f32(kk ? w.z : w.x, sv[0], sv[1]);
+            f16x2_to_f32(kk ? w.w : w.y, sv[2], sv[3]);
+          } else {
+            sv[0] = __uint_as_float(pr.vs[kt].x);
+            sv[1] = __uint_as_float(pr.vs[kt].y);
+            sv[2] = __uint_as_float(pr.vs[kt].z);
+            sv[3] = __uint_as_float(pr.vs[kt].w);
           }
+          const float pp[4] = {pw.x, pw.y, pw.z, pw.w};
+          float pv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pv[i] = pp[i] * sv[i];
+            if constexpr (MASKED) pv[i] = (pp[i] != 0.0f) ? pv[i] : 0.0f;  // unwritten slots: NaN scales
+          }
+          split_f16(pv[0], pv[1], hi[2 * kk], lo[2 * kk]);
+          split_f16(pv[2], pv[3], hi[2 * kk + 1], lo[2 * kk + 1]);
+        }
+        bh[nt] = f16x8{hi[0][0], hi[0][1], hi[1][0], hi[1][1], hi[2][0], hi[2][1], hi[3][0], hi[3][1]};
+        bl[nt] = f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]};
       }
 #pragma unroll
-      for (int dd = 0; dd < 4; ++dd) {
-        const int dt = 4 * cg + dd;
+      for (int j = 0; j < DPW; ++j) {
+        const f16x8 va = ks ? codes_to_f16<FMT>(pr.v[j].z, pr.v[j].w) : codes_to_f16<FMT>(pr.v[j].x, pr.v[j].y);
 #pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2) {
-          const f16x8 va = ks2 ? codes_to_f16<FMT>(vr[dt].z, vr[dt].w) : codes_to_f16<FMT>(vr[dt].x, vr[dt].y);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            o[nt][dt] = mfma16(va, bh[nt][ks2], o[nt][dt]);
-            o[nt][dt] = mfma16(va, bl[nt][ks2], o[nt][dt]);
-          }
+        for (int nt = 0; nt < NT; ++nt) {
+          o[nt][j] = mfma16(va, bh[nt], o[nt][j]);
+          o[nt][j] = mfma16(va, bl[nt], o[nt][j]);
         }
       }
+    }
+  };
+
+  auto step = [&](PageRegs<D, FMT> &pr, int it) {
+    const int p = page0 + it * NTEAM + team;
+    const bool valid = p < page1;                              // uniform per team
+    const bool full = (p * kPage + kPage - 1) <= (L - a.T);   // every real row sees every key of the page
+    const int buf = it & 1;
+    float z[NT][4];
+    float mloc[NT];
+    if (valid && full) {
+      scores(std::false_type{}, pr, p, z, mloc);
+    } else if (valid) {
+      scores(std::true_type{}, pr, p, z, mloc);
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        mloc[nt] = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[nt][i] = -INFINITY;
+      }
+    }
+    if (q4 == 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) lds_mx[team][buf][wave][16 * nt + c16] = mloc[nt];
+    }
+    __syncthreads();
+
+    // ---- phase 2: online softmax over the page (identical in the 4 waves of the team)
+    float *pb = pbuf + (team * 2 + buf) * ROWS * PST;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int r = 16 * nt + c16;
+      float pmax = lds_mx[team][buf][0][r];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) pmax = fmaxf(pmax, lds_mx[team][buf][w][r]);
+      const float mnew = fmaxf(m[nt], pmax);
+      const float msafe = (mnew == -INFINITY) ? 0.0f : mnew;
+      const float alpha = exp2_hw(m[nt] - msafe);
+      m[nt] = mnew;
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[i] = exp2_hw(z[nt][i] - msafe);
+      lsum[nt] = lsum[nt] * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int j = 0; j < DPW; ++j) o[nt][j] *= alpha;
+      }
+      *reinterpret_cast<float4 *>(pb + r * PST + 16 * wave + 4 * q4) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+    }
+    __syncthreads();
+
+    if (valid && full) {
+      accumulate(std::false_type{}, pr, p, pb);
+    } else if (valid) {
+      accumulate(std::true_type{}, pr, p, pb);
+    }
+  };
+
+  if (n_it > 0) {
+    PageRegs<D, FMT> rA, rB;
+    load_page<D, FMT>(rA, a, page_of(0), wave, lane, q4);
+    for (int it = 0;; it += 2) {
+      load_page<D, FMT>(rB, a, page_of(min(it + 1, n_it - 1)), wave, lane, q4);
+      step(rA, it);
+      if (it + 1 >= n_it) break;
+      load_page<D, FMT>(rA, a, page_of(min(it + 2, n_it - 1)), wave, lane, q4);
+      step(rB, it + 1);
+      if (it + 2 >= n_it) break;
     }
   }
 
-  // ---- finish this wave: full running sum of each row
+  // ---- per-wave row sums, then the team's and the workgroup's totals
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     lsum[nt] += __shfl_xor(lsum[nt], 16);
     lsum[nt] += __shfl_xor(lsum[nt], 32);
   }
-
-  // ---- merge the 4 waves of the workgroup (fixed order: deterministic)
-  __syncthreads();  // Q operands no longer needed: smem becomes the merge buffer
-  float *lds_o = reinterpret_cast<float *>(smem);
   if (q4 == 0) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      lds_m[wave][16 * nt + c16] = m[nt];
-      lds_l[wave][16 * nt + c16] = lsum[nt];
+      lds_l[team][wave][16 * nt + c16] = lsum[nt];
+      if (wave == 0) lds_m[team][16 * nt + c16] = m[nt];
     }
   }
   const int any_bad = __syncthreads_or(bad ? 1 : 0);
-  float Mrow[NT], Lrow[NT];
+  float Mrow[NT], Lrow[NT], fown[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = 16 * nt + c16;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds_m[w][r]);
+    for (int t = 0; t < NTEAM; ++t) M = fmaxf(M, lds_m[t][r]);
     const float Ms = (M == -INFINITY) ? 0.0f : M;
     float Lt = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) Lt += lds_l[w][r] * exp2f(lds_m[w][r] - Ms);
+    for (int t = 0; t < NTEAM; ++t) {
+      const float lt = (lds_l[t][0][r] + lds_l[t][1][r]) + (lds_l[t][2][r] + lds_l[t][3][r]);
+      Lt += lt * exp2f(lds_m[t][r] - Ms);
+    }
     Mrow[nt] = M;
     Lrow[nt] = any_bad ? NAN : Lt;
-    const float f = exp2f(m[nt] - Ms);
-#pragma unroll
-    for (int dt = 0; dt < NCH; ++dt) o[nt][dt] *= f;
+    fown[nt] = exp2f(m[nt] - Ms);
   }
-  for (int w = 0; w < kWaves; ++w) {
-    if (wave == w) {
+  // teams 1.. hand their scaled outputs to team 0 through LDS (fixed order: deterministic)
+  float *fin = pbuf;
+  if constexpr (NTEAM > 1) {
+    if (team > 0) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int dt = 0; dt < NCH; ++dt) {
-          float4 *dst = reinterpret_cast<float4 *>(lds_o + (16 * nt + c16) * O_STRIDE + 16 * dt + 4 * q4);
-          float4 v = make_float4(o[nt][dt][0], o[nt][dt][1], o[nt][dt][2], o[nt][dt][3]);
-          if (w != 0) {
-            const float4 prev = *dst;
-            v.x += prev.x;
-            v.y += prev.y;
-            v.z += prev.z;
-            v.w += prev.w;
-          }
-          *dst = v;
+        for (int j = 0; j < DPW; ++j) {
+          const f32x4 v = o[nt][j] * fown[nt];
+          *reinterpret_cast<float4 *>(fin + ((team - 1) * ROWS + 16 * nt + c16) * (D + 4) + 16 * (wave * DPW + j) +
+                                      4 * q4) = make_float4(v[0], v[1], v[2], v[3]);
         }
     }
     __syncthreads();
   }
-
-  // ---- write this chunk's partial
-  const size_t part = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits + split;
-  float *po = a.ws_o + part * R * D;
-  for (int e = threadIdx.x; e < R * (D / 4); e += 256) {
-    const int r = e / (D / 4), c4 = e % (D / 4);
-    reinterpret_cast<float4 *>(po)[e] = *reinterpret_cast<const float4 *>(lds_o + r * O_STRIDE + 4 * c4);
-  }
-  if (wave == 0 && q4 == 0) {
+  if (team == 0) {
+    const size_t part = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits + split;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int r = 16 * nt + c16;
       if (r < R) {
-        a.ws_ml[(part * R + r) * 2 + 0] = Mrow[nt];
-        a.ws_ml[(part * R + r) * 2 + 1] = Lrow[nt];
+#pragma unroll
+        for (int j = 0; j < DPW; ++j) {
+          f32x4 v = o[nt][j] * fown[nt];
+          const int d = 16 * (wave * DPW + j) + 4 * q4;
+#pragma unroll
+          for (int t = 1; t < NTEAM; ++t) {
+            const float4 x = *reinterpret_cast<const float4 *>(fin + ((t - 1) * ROWS + r) * (D + 4) + d);
+            v += f32x4{x.x, x.y, x.z, x.w};
+          }
+          *reinterpret_cast<float4 *>(a.ws_o + (part * R + r) * D + d) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+        if (wave == 0 && q4 == 0) {
+          a.ws_ml[(part * R + r) * 2 + 0] = Mrow[nt];
+          a.ws_ml[(part * R + r) * 2 + 1] = Lrow[nt];
+        }
       }
     }
   }
 }
 
-// Merge kernel: one workgroup per output row (b, t, h); thread d owns dim d.
+// Merge kernel: one workgroup of 256 threads per output row (b, t, h).  The
+// chunk maxima and sums are read in parallel and reduced to log-sum-exp
+// weights in LDS; then every thread owns 4 dims of one slice of the chunks and
+// issues all of its partial-output loads at once; the slices are summed in a
+// fixed order (deterministic).
 template <int D>
-__global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a) {
-  const int row = blockIdx.x;
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  constexpr int C4 = D / 4;             // float4 columns of one row
+  constexpr int NSL = 256 / C4;         // chunk slices (4 for D=256, 8 for D=128)
+  constexpr int MAXS = kMergeMaxSplits;  // chunks per sequence handled with one load each
+  __shared__ float w_s[MAXS];
+  __shared__ float red[256];
+  __shared__ float4 acc_s[NSL][C4];
+  const int row = blockIdx.x, tid = threadIdx.x;
   const int h = row % a.num_q_heads, t = (row / a.num_q_heads) % a.T, b = row / (a.num_q_heads * a.T);
-  const int d = threadIdx.x;
-  float *dst = a.out + static_cast<size_t>(row) * D + d;
+  float *dst = a.out + static_cast<size_t>(row) * D;
   const int L = a.seq_lens[b];
   if (L < a.T || L > a.max_seq_len || L > a.max_blocks * kPage) {
-    *dst = NAN;
+    if (tid < D) dst[tid] = NAN;
     return;
   }
   const int kvh = h / a.group, r = t * a.group + h % a.group;
   const int ns = (L + a.tokens_per_split - 1) / a.tokens_per_split;
   const size_t part0 = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.ws_ml[((part0 + s) * a.rows + r) * 2]);
+
+  // ---- maxima: each thread takes chunks tid, tid+256, ...
+  float mx = -INFINITY;
+  for (int s = tid; s < ns; s += 256) mx = fmaxf(mx, a.ws_ml[((part0 + s) * a.rows + r) * 2]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+    __syncthreads();
+  }
+  const float M = red[0];
   const float Ms = (M == -INFINITY) ? 0.0f : M;
-  float acc = 0.0f, lt = 0.0f;
-  for (int s = 0; s < ns; ++s) {
+  __syncthreads();
+  // ---- weights and the weighted sum of chunk sums
+  float lt = 0.0f;
+  for (int s = tid; s < ns; s += 256) {
     const size_t pr = (part0 + s) * a.rows + r;
     const float w = exp2f(a.ws_ml[pr * 2] - Ms);
+    if (s < MAXS) w_s[s] = w;
     lt += w * a.ws_ml[pr * 2 + 1];
-    acc += w * a.ws_o[pr * D + d];
   }
-  *dst = acc / lt;
+  red[tid] = lt;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) red[tid] += red[tid + off];
+    __syncthreads();
+  }
+  const float Lt = red[0];
+  // ---- outputs: thread (slice, c4) sums chunks slice, slice + NSL, ... in ascending
+  // order, 8 loads in flight at a time
+  const int c4 = tid % C4, slice = tid / C4;
+  float4 acc = make_float4(0, 0, 0, 0);
+  constexpr int BATCH = 8;
+  for (int s0 = slice; s0 < ns; s0 += BATCH * NSL) {
+    float4 x[BATCH];
+    float w[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int s = s0 + k * NSL;
+      const size_t pr = (part0 + min(s, ns - 1)) * a.rows + r;
+      x[k] = reinterpret_cast<const float4 *>(a.ws_o + pr * D)[c4];
+      w[k] = (s >= ns) ? 0.0f : (s < MAXS) ? w_s[s] : exp2f(a.ws_ml[pr * 2] - Ms);
+    }
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      acc.x += w[k] * x[k].x;
+      acc.y += w[k] * x[k].y;
+      acc.z += w[k] * x[k].z;
+      acc.w += w[k] * x[k].w;
+    }
+  }
+  acc_s[slice][c4] = acc;
+  __syncthreads();
+  if (tid < C4) {
+    float4 v = acc_s[0][tid];
+#pragma unroll
+    for (int sl = 1; sl < NSL; ++sl) {
+      const float4 x = acc_s[sl][tid];
+      v.x += x.x;
+      v.y += x.y;
+      v.z += x.z;
+      v.w += x.w;
+    }
+    reinterpret_cast<float4 *>(dst)[tid] = make_float4(v.x / Lt, v.y / Lt, v.z / Lt, v.w / Lt);
+  }
 }
 
 template <int D, int NT, int FMT, int QDT>
 hipError_t split_one(const AttnArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_split_kernel<D, NT, FMT, QDT>), dim3(a.n_splits, a.num_kv_heads, a.num_seqs), dim3(256), 0,
-                     s, a);
+  // fp32 queries need the hi+lo pair; bf16 queries are one exact f16
+  hipLaunchKernelGGL((attn_split_kernel<D, NT, FMT, QDT == 0 ? 1 : 0, kTeams>), dim3(a.n_splits, a.num_kv_heads, a.num_seqs),
+                     dim3(256 * kTeams), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t merge_one(const AttnArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(a.num_seqs * a.T * a.num_q_heads), dim3(D), 0, s, a);
+  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(a.num_seqs * a.T * a.num_q_heads), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -8,8 +8,10 @@
 namespace kvq {
 
 constexpr int kPage = 64;       // token slots per page
-constexpr int kWaves = 4;       // waves per attention workgroup
+constexpr int kTeams = 2;       // 4-wave teams per attention workgroup
 constexpr int kTargetWgs = 256; // one attention workgroup per compute unit of the chip
+constexpr int kMaxChunkPages = 256;   // pages of one attention chunk (block ids staged in LDS)
+constexpr int kMergeMaxSplits = 1024; // chunk weights the merge keeps in LDS
 
 // Launch arguments of kv_append_quant, validated on the host.
 struct AppendArgs {

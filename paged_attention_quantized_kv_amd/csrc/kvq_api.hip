@@ -27,13 +27,14 @@ int check_cache(const kvq_cache_t *c) {
 
 // Chunking of the context: a pure function of the shape.  Pages per chunk are
 // chosen so that num_seqs * num_kv_heads * chunks is about one workgroup per
-// compute unit, rounded to whole rounds of the 4 waves.
+// compute unit, rounded to whole rounds of the workgroup's teams.
 int32_t chunk_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len) {
   const long pages = (static_cast<long>(max_seq_len) + kvq::kPage - 1) / kvq::kPage;
   const long total = pages * num_seqs * num_kv_heads;
   long pps = (total + kvq::kTargetWgs - 1) / kvq::kTargetWgs;
-  pps = ((pps + kvq::kWaves - 1) / kvq::kWaves) * kvq::kWaves;
-  if (pps < kvq::kWaves) pps = kvq::kWaves;
+  pps = ((pps + kvq::kTeams - 1) / kvq::kTeams) * kvq::kTeams;
+  if (pps < kvq::kTeams) pps = kvq::kTeams;
+  if (pps > kvq::kMaxChunkPages) pps = kvq::kMaxChunkPages;
   return static_cast<int32_t>(pps * kvq::kPage);
 }
 

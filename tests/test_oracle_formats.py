@@ -174,10 +174,11 @@ def test_page_layout_is_a_bijection(D):
     k = {O.k_byte(s, d, D) for s in range(64) for d in range(D)}
     v = {O.v_byte(s, d, D) for s in range(64) for d in range(D)}
     assert k == set(range(64 * D)) and v == set(range(64 * D))
-    si = {O.scale_elem(O.FMT_INT8_G64, s, g, D) for s in range(64) for g in range(D // 64)}
-    assert si == set(range(64 * D // 64))
-    sf = {O.scale_elem(O.FMT_FP8_ROW, s, 0, D) for s in range(64)}
-    assert sf == set(range(64))
+    for which in (0, 1):
+        si = {O.scale_elem(O.FMT_INT8_G64, which, s, g, D) for s in range(64) for g in range(D // 64)}
+        assert si == set(range(64 * D // 64))
+        sf = {O.scale_elem(O.FMT_FP8_ROW, which, s, 0, D) for s in range(64)}
+        assert sf == set(range(64))
 
 
 def _golden_table():

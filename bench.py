@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the quantized paged KV cache on one MI355X.
 
-One step = the decode hot path of one full-attention layer:
-  kv_append_quant of the T new rows of every sequence, then paged_decode_attn
-  (split kernel + log-sum-exp merge) over the whole context.
+One step = the decode hot path of one full-attention layer: the T new rows of
+every sequence are quantized into the pool, then paged decode attention runs
+over the whole context (paged_decode_step: the split kernel quantizes the new
+rows it holds, then the log-sum-exp merge).  The same step as the two calls
+kv_append_quant + paged_decode_attn is timed beside it.
 The headline workload is the MTP3 verify step at 131,072 tokens (B=1, T=4,
 Hq=24, Hkv=4, D=256, INT8 group-64 KV); the JSON line also carries the 32K
 (T=1) and 262,144-token (T=1, INT8 and FP8-row) depths of the metric.
@@ -82,33 +84,37 @@ class Run:
                 self.ws)
 
     def step(self, i):
-        """One decode step on pool copy i: append the T new rows, then split + merge."""
+        """One decode step on pool copy i, one call: append the T new rows and attend
+        (split kernel with the rows quantized in, then the merge)."""
+        c, q, bt, sl, L, scale, out, ws = self.attn_args(i)
+        self.K.paged_decode_step(c, self.k_new, self.v_new, q, bt, sl, L, scale, out, ws)
+
+    def step_two_calls(self, i):
+        """The same step as kv_append_quant followed by paged_decode_attn (3 kernels)."""
         c = self.caches[i % self.n_copies]
         self.K.kv_append_quant(c, self.k_new, self.v_new, self.bt, self.start)
-        self.K.paged_decode_attn_split(*self.attn_args(i))
-        self.K.paged_decode_attn_merge(*self.attn_args(i))
+        self.K.paged_decode_attn(*self.attn_args(i))
+
+    def _graph(self, fn, idx):
+        g = self.torch.cuda.CUDAGraph()
+        with self.torch.cuda.graph(g):
+            for i in idx:
+                fn(i)
+        return g
 
     def build_graphs(self):
         """HIP graphs (torch.cuda.CUDAGraph): one step per pool copy, all copies' steps
-        in order, and the split kernel alone over all copies."""
+        in order, the same for the two-call step, and the split kernel alone."""
         torch = self.torch
         for i in range(self.n_copies):  # eager warm-up of every copy before capture
             self.step(i)
+            self.step_two_calls(i)
         torch.cuda.synchronize()
-        self.g_one = []
-        for i in range(self.n_copies):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                self.step(i)
-            self.g_one.append(g)
-        self.g_all = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.g_all):
-            for i in range(self.n_copies):
-                self.step(i)
-        self.g_split = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.g_split):
-            for i in range(self.n_copies):
-                self.K.paged_decode_attn_split(*self.attn_args(i))
+        allc = range(self.n_copies)
+        self.g_one = [self._graph(self.step, [i]) for i in allc]
+        self.g_all = self._graph(self.step, allc)
+        self.g_all_two = self._graph(self.step_two_calls, allc)
+        self.g_split = self._graph(lambda i: self.K.paged_decode_attn_split(*self.attn_args(i)), allc)
         torch.cuda.synchronize()
 
     def measure_eager(self, steps, warmup):
@@ -128,7 +134,20 @@ class Run:
             self.K.paged_decode_attn_split(*self.attn_args(i))
         e1.record()
         torch.cuda.synchronize()
-        return wall_ms / steps, [e0.elapsed_time(e1) / self.n_copies]
+        return wall_ms / steps, [e0.elapsed_time(e1) / self.n_copies], None
+
+    def _events(self, g, reps, per):
+        torch = self.torch
+        out = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) / (reps * per))
+        return sorted(out)
 
     def measure(self, steps, warmup, eager=False):
         torch = self.torch
@@ -139,25 +158,26 @@ class Run:
             self.g_one[i % self.n_copies].replay()
         torch.cuda.synchronize()
         full, rest = divmod(steps, self.n_copies)
+        # exactly `steps` steps, synchronized on both sides; GPU time from events on the
+        # replay stream, host wall time beside it (the host launch cadence of Python graph
+        # replays can trail the GPU)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
+        e0.record()
         for _ in range(full):
             self.g_all.replay()
         for i in range(rest):
             self.g_one[i].replay()
+        e1.record()
         torch.cuda.synchronize()
-        wall_ms = (time.perf_counter() - t0) * 1e3
-        # the split kernel alone: events on the replay stream around back-to-back launches
+        self.wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+        gpu_ms = e0.elapsed_time(e1)
         reps = max(1, steps // self.n_copies)
-        split_ms = []
-        for _ in range(3):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(reps):
-                self.g_split.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            split_ms.append(e0.elapsed_time(e1) / (reps * self.n_copies))
-        return wall_ms / steps, sorted(split_ms)
+        # the split kernel alone: events on the replay stream around back-to-back launches
+        split_ms = self._events(self.g_split, reps, self.n_copies)
+        two_ms = self._events(self.g_all_two, reps, self.n_copies)
+        return gpu_ms / steps, split_ms, two_ms
 
     def algorithmic_split_bytes(self):
         """Bytes the split kernel must move by definition: every visible key and value
@@ -237,7 +257,7 @@ def main():
     for name in names:
         print(f"[bench] {name}: generating and appending the context", file=sys.stderr, flush=True)
         run = Run(K, S, H, torch, name, dev)
-        ms, split_ms = run.measure(args.steps, args.warmup, eager=args.eager)
+        ms, split_ms, two_ms = run.measure(args.steps, args.warmup, eager=args.eager)
         w = run.w
         s = w.shape
         split_avg = sum(split_ms) / len(split_ms)
@@ -255,6 +275,8 @@ def main():
             "n_copies": run.n_copies,
             "n_splits": run.n_splits,
             "tokens_per_split": run.tps,
+            "two_call_ms": (sum(two_ms) / len(two_ms)) if two_ms else None,
+            "wall_ms": getattr(run, "wall_ms", None),
         }
         print(f"[bench] {name}: {ms * 1e3:.1f} us/step, split {split_avg * 1e3:.1f} us "
               f"({results[name]['split_gbs']:.0f} GB/s), {run.n_copies} pool copies", file=sys.stderr, flush=True)
@@ -281,7 +303,7 @@ def main():
                                f"L={shp.lens[0] if shp.B == 1 else 'ragged'} page=64 "
                                f"{'INT8 g64' if shp.fmt == 0 else 'FP8 E4M3 row'} KV",
                    "global_batch": shp.B * shp.T, "seq_len": shp.lens[0] if shp.B == 1 else max(shp.lens),
-                   "step": "kv_append_quant(T rows) + paged_decode_attn (split + merge)",
+                   "step": "paged_decode_step: append of the T new rows + paged decode attention (2 kernels)",
                    "parallelism": "single GPU"},
         "pct_hbm_peak": round(100 * head["kv_gbs"] / HBM_PEAK_GBS, 2),
         "tok_per_s": round(head["tok_per_s"], 1),
@@ -292,6 +314,8 @@ def main():
         "depths": {n: {"kv_gbs": round(r["kv_gbs"], 1), "pct_hbm_peak": round(100 * r["kv_gbs"] / HBM_PEAK_GBS, 2),
                        "tok_per_s": round(r["tok_per_s"], 1), "us_per_step": round(r["ms_per_step"] * 1e3, 2),
                        "split_us": round(r["split_ms_avg"] * 1e3, 2), "split_gbs": round(r["split_gbs"], 1),
+                       "us_per_step_two_calls": round(r["two_call_ms"] * 1e3, 2) if r["two_call_ms"] else None,
+                       "us_per_step_host_wall": round(r["wall_ms"] * 1e3, 2) if r["wall_ms"] else None,
                        "n_splits": r["n_splits"], "pool_copies": r["n_copies"]} for n, r in results.items()},
         "host": {"cpu": model, "nproc": ncpu},
     }

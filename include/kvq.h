@@ -175,6 +175,22 @@ int paged_decode_attn_merge(const kvq_cache_t *cache, const void *q, int32_t q_d
                             float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
                             void *stream);
 
+/*
+ * paged_decode_step -- one decode step of a full-attention layer in one call:
+ * kv_append_quant of the T new rows of every sequence at positions
+ * seq_lens[b]-T .. seq_lens[b]-1 (start_pos = seq_lens - T), then
+ * paged_decode_attn over the cache including them.  Same results as the two
+ * calls in sequence; the rows are quantized inside the attention launch by the
+ * workgroup whose context chunk holds them, which saves one launch per step.
+ *
+ *   k_new, v_new  [num_seqs][T][num_kv_heads][head_dim], same dtype as q (dtype)
+ *   other arguments as for paged_decode_attn (workspace size included).
+ */
+int paged_decode_step(const kvq_cache_t *cache, const void *k_new, const void *v_new, const void *q, int32_t dtype,
+                      int32_t num_seqs, int32_t T, int32_t num_q_heads, const int32_t *block_table,
+                      int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t max_seq_len, float softmax_scale,
+                      float *out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *kvq_status_string(int status);
 

@@ -22,7 +22,8 @@ BF16 = 1
 PAGE = 64
 
 _EXPORTS = ("kv_append_quant", "paged_decode_attn", "paged_decode_attn_split", "paged_decode_attn_merge",
-            "paged_decode_attn_workspace_bytes", "paged_decode_attn_num_splits", "kvq_status_string")
+            "paged_decode_step", "paged_decode_attn_workspace_bytes", "paged_decode_attn_num_splits",
+            "kvq_status_string")
 
 
 class KvqError(RuntimeError):
@@ -50,6 +51,9 @@ def _load():
     for name in ("paged_decode_attn", "paged_decode_attn_split", "paged_decode_attn_merge"):
         getattr(L, name).argtypes = attn
         getattr(L, name).restype = C.c_int
+    L.paged_decode_step.argtypes = [P, vp, vp, vp, i32, i32, i32, i32, vp, i32, vp, i32, C.c_float, vp, vp,
+                                    C.c_size_t, vp]
+    L.paged_decode_step.restype = C.c_int
     L.paged_decode_attn_workspace_bytes.argtypes = [i32] * 6
     L.paged_decode_attn_workspace_bytes.restype = C.c_size_t
     L.paged_decode_attn_num_splits.argtypes = [i32] * 6 + [C.POINTER(i32)]
@@ -122,12 +126,25 @@ class Cache:
         return sum(t.numel() * t.element_size() for t in self.tensors())
 
 
+def _check_table(t: torch.Tensor, B: int, name: str, ndim: int) -> None:
+    if t.dtype != torch.int32 or t.dim() != ndim or t.shape[0] != B or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor with {B} rows")
+
+
+def _check_rows(x: torch.Tensor, cache: Cache, name: str) -> None:
+    if x.dim() != 4 or x.shape[2] != cache.num_kv_heads or x.shape[3] != cache.head_dim:
+        raise ValueError(f"{name} must be [B, n, {cache.num_kv_heads}, {cache.head_dim}]")
+
+
 def kv_append_quant(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, block_table: torch.Tensor,
                     start_pos: torch.Tensor, stream=None) -> None:
     """k_new, v_new: [B, n_new, Hkv, D] bf16|fp32; block_table [B, max_blocks] int32; start_pos [B] int32."""
     if k_new.dtype != v_new.dtype or k_new.shape != v_new.shape or k_new.dim() != 4:
         raise ValueError("k_new and v_new must both be [B, n_new, Hkv, D] of one dtype")
+    _check_rows(k_new, cache, "k_new")
     B, n_new = k_new.shape[0], k_new.shape[1]
+    _check_table(block_table, B, "block_table", 2)
+    _check_table(start_pos, B, "start_pos", 1)
     _check(lib.kv_append_quant(cache.desc, _ptr(k_new), _ptr(v_new), _dtype_code(k_new), B, n_new,
                                _ptr(block_table), block_table.shape[1], _ptr(start_pos), _stream(stream)))
 
@@ -150,12 +167,21 @@ def alloc_workspace(cache: Cache, num_seqs: int, T: int, num_q_heads: int, max_s
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def _check_attn(cache, q, block_table, seq_lens, out, workspace):
+    if q.dim() != 4 or q.shape[3] != cache.head_dim:
+        raise ValueError(f"q must be [B, T, Hq, {cache.head_dim}]")
+    B = q.shape[0]
+    _check_table(block_table, B, "block_table", 2)
+    _check_table(seq_lens, B, "seq_lens", 1)
+    if out.dtype != torch.float32 or out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor with the shape of q")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+
+
 def _attn(fn, cache, q, block_table, seq_lens, max_seq_len, softmax_scale, out, workspace, stream):
-    if q.dim() != 4:
-        raise ValueError("q must be [B, T, Hq, D]")
+    _check_attn(cache, q, block_table, seq_lens, out, workspace)
     B, T, Hq = q.shape[0], q.shape[1], q.shape[2]
-    if out.dtype != torch.float32 or out.shape != q.shape:
-        raise ValueError("out must be fp32 with the shape of q")
     _check(fn(cache.desc, _ptr(q), _dtype_code(q), B, T, Hq, _ptr(block_table), block_table.shape[1],
               _ptr(seq_lens), int(max_seq_len), float(softmax_scale), _ptr(out), _ptr(workspace),
               workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -176,3 +202,23 @@ def paged_decode_attn_split(cache, q, block_table, seq_lens, max_seq_len, softma
 def paged_decode_attn_merge(cache, q, block_table, seq_lens, max_seq_len, softmax_scale, out, workspace, stream=None):
     return _attn(lib.paged_decode_attn_merge, cache, q, block_table, seq_lens, max_seq_len, softmax_scale, out,
                  workspace, stream)
+
+
+def paged_decode_step(cache, k_new, v_new, q, block_table, seq_lens, max_seq_len, softmax_scale, out, workspace,
+                      stream=None):
+    """Append the T new rows of each sequence (at seq_lens - T) and attend, in one launch.
+    k_new, v_new: [B, T, Hkv, D] with the dtype of q."""
+    _check_attn(cache, q, block_table, seq_lens, out, workspace)
+    if k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must have one shape")
+    _check_rows(k_new, cache, "k_new")
+    if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+        raise TypeError("the new rows and the queries must share one dtype")
+    B, T, Hq = q.shape[0], q.shape[1], q.shape[2]
+    if k_new.shape[0] != B or k_new.shape[1] != T:
+        raise ValueError("k_new must hold T rows per sequence")
+    _check(lib.paged_decode_step(cache.desc, _ptr(k_new), _ptr(v_new), _ptr(q), _dtype_code(q), B, T, Hq,
+                                 _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(max_seq_len),
+                                 float(softmax_scale), _ptr(out), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out

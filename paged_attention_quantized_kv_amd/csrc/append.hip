@@ -6,45 +6,13 @@
 // consecutive dims, so a 64-dim group is 64/(D/64) adjacent lanes and its
 // absmax is a butterfly over those lanes.  Codes go straight to their byte
 // positions in the page (see kvq.h for the in-page order).
-#include "internal.h"
+#include "quant_row.h"
 
 namespace kvq {
 namespace {
 
-template <int SRC>
-__device__ inline float load_src(const void *p, size_t i);
-template <>
-__device__ inline float load_src<0>(const void *p, size_t i) {  // fp32
-  return static_cast<const float *>(p)[i];
-}
-template <>
-__device__ inline float load_src<1>(const void *p, size_t i) {  // bf16: exact widening
-  return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(p)[i]) << 16);
-}
-
-// OCP FP8 E4M3FN of v, round to nearest even, magnitudes >= 448 saturate to
-// 448, NaN -> 0x7F, sign kept (a negative value that rounds to zero -> 0x80).
-__device__ inline uint32_t e4m3fn_rne_sat(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float ax = fabsf(v);
-  if (!(ax == ax)) return 0x7Fu;
-  uint32_t code;
-  if (ax >= 448.0f) {
-    code = 0x7Eu;
-  } else if (ax < 0.015625f) {  // below 2^-6: subnormals, multiples of 2^-9
-    code = static_cast<uint32_t>(rintf(ax * 512.0f));  // 8 lands on 2^-6 = code 0x08
-  } else {
-    const int e = static_cast<int>((__float_as_uint(ax) >> 23) & 0xFFu) - 127;  // -6..8
-    const float r = rintf(ldexpf(ax, 3 - e));  // significand * 8 in [8, 16]
-    code = static_cast<uint32_t>((e + 7) * 8) + static_cast<uint32_t>(r) - 8u;  // r == 16 carries
-  }
-  return sign | code;
-}
-
 template <int FMT, int D, int SRC>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  constexpr int E = D / 64;            // elements per lane
-  constexpr int LPG = 64 / E;          // lanes per 64-dim group
   const int lane = threadIdx.x & 63;
   const long row = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const long nrows = 2L * a.num_seqs * a.n_new * a.num_kv_heads;
@@ -55,77 +23,11 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   rest /= a.num_kv_heads;
   const int t = static_cast<int>(rest % a.n_new);
   const int b = static_cast<int>(rest / a.n_new);
-
   const long pos = static_cast<long>(a.start_pos[b]) + t;
   if (pos < 0 || pos >= static_cast<long>(a.max_blocks) * kPage) return;
   const int blk = a.block_table[static_cast<long>(b) * a.max_blocks + pos / kPage];
   if (blk < 0 || blk >= a.num_blocks) return;
-  const int slot = static_cast<int>(pos % kPage);
-  const int run = (slot % 16) / 4, spos = (slot / 16) * 4 + slot % 4;
-
-  const void *src = which ? a.v_new : a.k_new;
-  const size_t base = ((static_cast<size_t>(b) * a.n_new + t) * a.num_kv_heads + h) * D + lane * E;
-  float x[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) x[e] = load_src<SRC>(src, base + e);
-
-  const size_t page = static_cast<size_t>(blk) * a.num_kv_heads + h;
-  uint8_t *codes = (which ? a.v_codes : a.k_codes) + page * kPage * D;
-  uint32_t c[E];
-
-  if constexpr (FMT == 0) {  // INT8, one fp16 scale per 64 dims
-    float amax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(x[e]));
-#pragma unroll
-    for (int off = 1; off < LPG; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    const _Float16 s16 = static_cast<_Float16>(amax / 127.0f);  // IEEE division, RNE to fp16
-    const float s = static_cast<float>(s16);
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float r = 0.0f;
-      if (s != 0.0f) r = fminf(fmaxf(rintf(x[e] / s), -127.0f), 127.0f);
-      c[e] = static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu;
-    }
-    if ((lane % LPG) == 0) {
-      const int g = lane / LPG;
-      _Float16 *sc = static_cast<_Float16 *>(which ? a.v_scales : a.k_scales) + page * D;
-      // K: (run, slot/16, group, slot%4); V: (run, group, slot/16, slot%4)
-      const int e = which ? (run * E + g) * 16 + spos : ((run * 4 + slot / 16) * E + g) * 4 + slot % 4;
-      sc[e] = s16;
-    }
-  } else {  // FP8 E4M3FN, one fp32 scale per row
-    float amax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(x[e]));
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    const float s = amax / 448.0f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) c[e] = (s != 0.0f) ? e4m3fn_rne_sat(x[e] / s) : 0u;
-    if (lane == 0) {
-      float *sc = static_cast<float *>(which ? a.v_scales : a.k_scales) + page * kPage;
-      sc[run * 16 + spos] = s;
-    }
-  }
-
-  const int d0 = lane * E;
-  if (which == 0) {
-    // K: the E dims of this lane are adjacent bytes of one 16-byte tile row
-    const size_t off = (static_cast<size_t>(slot / 16) * (D / 16) + d0 / 16) * 256 + (slot % 16) * 16 + d0 % 16;
-    if constexpr (E == 4) {
-      *reinterpret_cast<uint32_t *>(codes + off) = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    } else {
-      *reinterpret_cast<uint16_t *>(codes + off) = static_cast<uint16_t>(c[0] | (c[1] << 8));
-    }
-  } else {
-    // V: dim-major, one byte per dim
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int d = d0 + e;
-      codes[(static_cast<size_t>(d / 16) * 4 + run) * 256 + (d % 16) * 16 + spos] = static_cast<uint8_t>(c[e]);
-    }
-  }
+  quant_row<FMT, D, SRC>(a, b, t, h, which, pos, blk, lane);
 }
 
 template <int FMT, int D, int SRC>

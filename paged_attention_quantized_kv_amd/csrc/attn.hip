@@ -25,7 +25,7 @@
 // contiguous KiB that lands in the operand registers.
 #include <type_traits>
 
-#include "internal.h"
+#include "quant_row.h"
 
 namespace kvq {
 namespace {
@@ -84,6 +84,25 @@ __device__ inline float load_q(const void *q, size_t i) {
 
 __device__ inline f16x8 lds_f16x8(const uint4 *p) { return __builtin_bit_cast(f16x8, *p); }
 
+// Butterfly steps across the 16-lane rows of a wave without LDS: lane l gets
+// op(x[l], x[l ^ 16]) and op(x[l], x[l ^ 32]) via the gfx950 row/half swaps.
+__device__ inline float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // 2^x with the hardware exponential: exact at 0 and -inf; results below the
 // normal range (weights under 2^-126 of the running maximum) may flush to zero.
 __device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -100,6 +119,17 @@ struct PageRegs {
   uint4 vs[VSN];
 };
 
+// The pages are streamed once per call: load them with the non-temporal hint.
+__device__ inline uint4 ld_stream(const uint4 *p) {
+#if KVQ_NT_LOADS
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+#else
+  return *p;
+#endif
+}
+
 template <int D, int FMT>
 __device__ inline void load_page(PageRegs<D, FMT> &r, const AttnArgs &a, int pg_any, int wave, int lane, int q4) {
   constexpr int G64 = D / 64, NCH = D / 16, DPW = D / 64;
@@ -107,9 +137,9 @@ __device__ inline void load_page(PageRegs<D, FMT> &r, const AttnArgs &a, int pg_
   const uint4 *kp = reinterpret_cast<const uint4 *>(a.k_codes + pg * kPage * D);
   const uint4 *vp = reinterpret_cast<const uint4 *>(a.v_codes + pg * kPage * D);
 #pragma unroll
-  for (int cg = 0; cg < G64; ++cg) r.k[cg] = kp[(wave * NCH + 4 * cg) * 16 + lane];
+  for (int cg = 0; cg < G64; ++cg) r.k[cg] = ld_stream(kp + (wave * NCH + 4 * cg) * 16 + lane);
 #pragma unroll
-  for (int j = 0; j < DPW; ++j) r.v[j] = vp[(wave * DPW + j) * 64 + lane];
+  for (int j = 0; j < DPW; ++j) r.v[j] = ld_stream(vp + (wave * DPW + j) * 64 + lane);
   if constexpr (FMT == 0) {
     const uint4 *ksp = reinterpret_cast<const uint4 *>(static_cast<const _Float16 *>(a.k_scales) + pg * D);
     const uint4 *vsp = reinterpret_cast<const uint4 *>(static_cast<const _Float16 *>(a.v_scales) + pg * D);
@@ -142,7 +172,9 @@ struct Smem {
   static constexpr int PBF = PB > FIN ? PB : FIN;
 };
 
-template <int D, int NT, int FMT, int QLO, int NTEAM>
+// APP: 1 = also quantize and append the T new rows of each sequence (the fused
+// decode step; the source dtype is the query dtype), 0 = the cache is complete.
+template <int D, int NT, int FMT, int QLO, int NTEAM, int APP>
 __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) {
   constexpr int G64 = D / 64, NCH = D / 16, DPW = D / 64;
   constexpr int QP = QLO ? 2 : 1;
@@ -150,7 +182,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   constexpr int ROWS = SM::ROWS, PST = SM::PST;
   __shared__ uint4 qs[SM::QS];
   __shared__ float4 pbuf4[SM::PBF / 4];
-  __shared__ float lds_mx[NTEAM][2][4][ROWS];
+  __shared__ float4 lds_mx[NTEAM][2][ROWS];  // per row: the 4 waves' page maxima
   __shared__ float lds_l[NTEAM][4][ROWS];
   __shared__ float lds_m[NTEAM][ROWS];
   __shared__ int32_t lds_pg[kMaxChunkPages];  // pool page (block * Hkv + kvh) of each page of the chunk
@@ -166,6 +198,27 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   const int tok1 = min(tok0 + a.tokens_per_split, L);
   const int page0 = tok0 / kPage, page1 = (tok1 + kPage - 1) / kPage;
   const int R = a.rows;
+
+  // ---- the chunk's block ids -> pool pages in LDS (an invalid id reads block 0 and flags the chunk)
+  bool bad = false;
+  const int32_t *bt = a.block_table + static_cast<size_t>(b) * a.max_blocks;
+  for (int i = tid; i < page1 - page0; i += 256 * NTEAM) {
+    const int blk = bt[page0 + i];
+    const bool ok = (blk >= 0) && (blk < a.num_blocks);
+    bad |= !ok;
+    lds_pg[i] = (ok ? blk : 0) * a.num_kv_heads + kvh;
+  }
+  bad = __syncthreads_or(bad ? 1 : 0) != 0;
+
+  const int n_it = (page1 - page0 + NTEAM - 1) / NTEAM;
+  // pool page of iteration it for this team (clamped: iterations past the team's last
+  // page reload that page and skip the math)
+  auto page_of = [&](int it) -> int { return lds_pg[min(it * NTEAM + team, page1 - page0 - 1)]; };
+  PageRegs<D, FMT> rA, rB;
+  // the first pages load while the queries are staged (and, for the fused step, the new
+  // rows quantized) -- unless one of them holds new rows, which must be written first
+  const bool early = (APP == 0) || (page0 + NTEAM - 1 < (L - a.T) / kPage);
+  if (early && n_it > 0) load_page<D, FMT>(rA, a, page_of(0), wave, lane, q4);
 
   // ---- queries -> LDS in B-operand order: entry (nt, cg, hk, hl, lane) holds dims
   // 64cg + 16(lane/16) + 8hk + 0..7 of row 16nt + lane%16, as f16 hi (hl=0) or lo (hl=1).
@@ -197,18 +250,37 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     if constexpr (QLO)
       qs[idx + 64] = __builtin_bit_cast(uint4, f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]});
   }
-  // ---- the chunk's block ids -> pool pages in LDS (an invalid id reads block 0 and flags the chunk)
-  bool bad = false;
-  {
-    const int32_t *bt = a.block_table + static_cast<size_t>(b) * a.max_blocks;
-    for (int i = tid; i < page1 - page0; i += 256 * NTEAM) {
-      const int blk = bt[page0 + i];
-      const bool ok = (blk >= 0) && (blk < a.num_blocks);
-      bad |= !ok;
-      lds_pg[i] = (ok ? blk : 0) * a.num_kv_heads + kvh;
+  if constexpr (APP != 0) {
+    // fused decode step: the T new rows at positions L-T .. L-1 that fall in this chunk
+    // are quantized into the pool here, before any wave loads their page (the barrier
+    // below orders the stores before the loads)
+    const int t_lo = max(0, tok0 - (L - a.T)), t_hi = min(a.T, tok1 - (L - a.T));
+    AppendArgs aa;
+    aa.k_new = a.k_new;
+    aa.v_new = a.v_new;
+    aa.k_codes = const_cast<uint8_t *>(a.k_codes);
+    aa.v_codes = const_cast<uint8_t *>(a.v_codes);
+    aa.k_scales = const_cast<void *>(a.k_scales);
+    aa.v_scales = const_cast<void *>(a.v_scales);
+    aa.block_table = a.block_table;
+    aa.start_pos = nullptr;
+    aa.num_seqs = a.num_seqs;
+    aa.n_new = a.T;
+    aa.num_kv_heads = a.num_kv_heads;
+    aa.max_blocks = a.max_blocks;
+    aa.num_blocks = a.num_blocks;
+    for (int r = (tid >> 6); r < 2 * (t_hi - t_lo); r += 4 * NTEAM) {
+      const int t = t_lo + (r >> 1), which = r & 1;
+      const long pos = static_cast<long>(L) - a.T + t;
+      const int blk = bt[pos / kPage];
+      if (blk >= 0 && blk < a.num_blocks) quant_row<FMT, D, QLO ? 0 : 1>(aa, b, t, kvh, which, pos, blk, lane);
     }
+    // a wave that wrote rows waits until its stores have reached L2, so every wave of this
+    // workgroup loads the new rows after the barrier below (no other workgroup reads them)
+    if ((tid >> 6) < 2 * (t_hi - t_lo)) __builtin_amdgcn_s_waitcnt(0);
   }
-  bad = __syncthreads_or(bad ? 1 : 0) != 0;
+  __syncthreads();
+  if (!early && n_it > 0) load_page<D, FMT>(rA, a, page_of(0), wave, lane, q4);
 
   // ---- per-lane state; this lane's query row is 16nt + c16
   float m[NT], lsum[NT];
@@ -223,11 +295,6 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 #pragma unroll
     for (int j = 0; j < DPW; ++j) o[nt][j] = f32x4{0, 0, 0, 0};
   }
-  const int n_it = (page1 - page0 + NTEAM - 1) / NTEAM;
-  // pool page of iteration it for this team (clamped: iterations past the team's last
-  // page reload that page and skip the math)
-  auto page_of = [&](int it) -> int { return lds_pg[min(it * NTEAM + team, page1 - page0 - 1)]; };
-
   // ---- phase 1: scores of this wave's 16 keys (S^T = K Q^T), in log2 units, and their row maxima
   auto scores = [&](auto masked_tag, PageRegs<D, FMT> &pr, int p, float (&z)[NT][4], float (&mloc)[NT]) {
     constexpr bool MASKED = decltype(masked_tag)::value;
@@ -282,9 +349,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
         z[nt][i] = v;
         mx = fmaxf(mx, v);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      mloc[nt] = mx;
+      mloc[nt] = max_xor32(max_xor16(mx));
     }
   };
 
@@ -377,7 +442,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     }
     if (q4 == 0) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) lds_mx[team][buf][wave][16 * nt + c16] = mloc[nt];
+      for (int nt = 0; nt < NT; ++nt) reinterpret_cast<float *>(&lds_mx[team][buf][16 * nt + c16])[wave] = mloc[nt];
     }
     __syncthreads();
 
@@ -386,9 +451,8 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int r = 16 * nt + c16;
-      float pmax = lds_mx[team][buf][0][r];
-#pragma unroll
-      for (int w = 1; w < 4; ++w) pmax = fmaxf(pmax, lds_mx[team][buf][w][r]);
+      const float4 mw4 = lds_mx[team][buf][r];
+      const float pmax = fmaxf(fmaxf(mw4.x, mw4.y), fmaxf(mw4.z, mw4.w));
       const float mnew = fmaxf(m[nt], pmax);
       const float msafe = (mnew == -INFINITY) ? 0.0f : mnew;
       const float alpha = exp2_hw(m[nt] - msafe);
@@ -413,8 +477,6 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   };
 
   if (n_it > 0) {
-    PageRegs<D, FMT> rA, rB;
-    load_page<D, FMT>(rA, a, page_of(0), wave, lane, q4);
     for (int it = 0;; it += 2) {
       load_page<D, FMT>(rB, a, page_of(min(it + 1, n_it - 1)), wave, lane, q4);
       step(rA, it);
@@ -428,8 +490,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   // ---- per-wave row sums, then the team's and the workgroup's totals
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    lsum[nt] += __shfl_xor(lsum[nt], 16);
-    lsum[nt] += __shfl_xor(lsum[nt], 32);
+    lsum[nt] = sum_xor32(sum_xor16(lsum[nt]));
   }
   if (q4 == 0) {
 #pragma unroll
@@ -498,18 +559,34 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   }
 }
 
-// Merge kernel: one workgroup of 256 threads per output row (b, t, h).  The
-// chunk maxima and sums are read in parallel and reduced to log-sum-exp
-// weights in LDS; then every thread owns 4 dims of one slice of the chunks and
-// issues all of its partial-output loads at once; the slices are summed in a
+// Merge kernel: one workgroup of 256 threads per output row (b, t, h).  Every
+// load is issued up front: thread (slice, c4) holds 4 dims of up to MPER
+// chunks of its slice, and the chunk maxima and sums are read beside them;
+// block reductions give the log-sum-exp weights; the slices are summed in a
 // fixed order (deterministic).
+__device__ inline float block_max(float v, float *red) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+__device__ inline float block_sum(float v, float *red) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  constexpr int C4 = D / 4;             // float4 columns of one row
-  constexpr int NSL = 256 / C4;         // chunk slices (4 for D=256, 8 for D=128)
-  constexpr int MAXS = kMergeMaxSplits;  // chunks per sequence handled with one load each
+  constexpr int C4 = D / 4;        // float4 columns of one row
+  constexpr int NSL = 256 / C4;    // chunk slices (4 for D=256, 8 for D=128)
+  constexpr int MPER = 16;         // chunks per slice kept in registers
+  constexpr int MAXS = kMergeMaxSplits;
   __shared__ float w_s[MAXS];
-  __shared__ float red[256];
+  __shared__ float red[4];
   __shared__ float4 acc_s[NSL][C4];
   const int row = blockIdx.x, tid = threadIdx.x;
   const int h = row % a.num_q_heads, t = (row / a.num_q_heads) % a.T, b = row / (a.num_q_heads * a.T);
@@ -522,20 +599,19 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int kvh = h / a.group, r = t * a.group + h % a.group;
   const int ns = (L + a.tokens_per_split - 1) / a.tokens_per_split;
   const size_t part0 = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits;
+  const int c4 = tid % C4, slice = tid / C4;
 
-  // ---- maxima: each thread takes chunks tid, tid+256, ...
+  // ---- issue the first MPER partial-output loads of this slice and the chunk statistics
+  float4 x[MPER];
+#pragma unroll
+  for (int k = 0; k < MPER; ++k) {
+    const int s = min(slice + k * NSL, ns - 1);
+    x[k] = reinterpret_cast<const float4 *>(a.ws_o + ((part0 + s) * a.rows + r) * D)[c4];
+  }
   float mx = -INFINITY;
   for (int s = tid; s < ns; s += 256) mx = fmaxf(mx, a.ws_ml[((part0 + s) * a.rows + r) * 2]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
-    __syncthreads();
-  }
-  const float M = red[0];
+  const float M = block_max(mx, red);
   const float Ms = (M == -INFINITY) ? 0.0f : M;
-  __syncthreads();
-  // ---- weights and the weighted sum of chunk sums
   float lt = 0.0f;
   for (int s = tid; s < ns; s += 256) {
     const size_t pr = (part0 + s) * a.rows + r;
@@ -543,35 +619,27 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     if (s < MAXS) w_s[s] = w;
     lt += w * a.ws_ml[pr * 2 + 1];
   }
-  red[tid] = lt;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) red[tid] += red[tid + off];
-    __syncthreads();
-  }
-  const float Lt = red[0];
-  // ---- outputs: thread (slice, c4) sums chunks slice, slice + NSL, ... in ascending
-  // order, 8 loads in flight at a time
-  const int c4 = tid % C4, slice = tid / C4;
+  const float Lt = block_sum(lt, red);  // its barriers also publish w_s
+  auto weight = [&](int s) -> float {
+    return (s < MAXS) ? w_s[s] : exp2f(a.ws_ml[((part0 + s) * a.rows + r) * 2] - Ms);
+  };
   float4 acc = make_float4(0, 0, 0, 0);
-  constexpr int BATCH = 8;
-  for (int s0 = slice; s0 < ns; s0 += BATCH * NSL) {
-    float4 x[BATCH];
-    float w[BATCH];
 #pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      const int s = s0 + k * NSL;
-      const size_t pr = (part0 + min(s, ns - 1)) * a.rows + r;
-      x[k] = reinterpret_cast<const float4 *>(a.ws_o + pr * D)[c4];
-      w[k] = (s >= ns) ? 0.0f : (s < MAXS) ? w_s[s] : exp2f(a.ws_ml[pr * 2] - Ms);
-    }
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      acc.x += w[k] * x[k].x;
-      acc.y += w[k] * x[k].y;
-      acc.z += w[k] * x[k].z;
-      acc.w += w[k] * x[k].w;
-    }
+  for (int k = 0; k < MPER; ++k) {
+    const int s = slice + k * NSL;
+    const float w = (s < ns) ? weight(s) : 0.0f;
+    acc.x += w * x[k].x;
+    acc.y += w * x[k].y;
+    acc.z += w * x[k].z;
+    acc.w += w * x[k].w;
+  }
+  for (int s = slice + MPER * NSL; s < ns; s += NSL) {  // long contexts with many chunks
+    const float w = weight(s);
+    const float4 y = reinterpret_cast<const float4 *>(a.ws_o + ((part0 + s) * a.rows + r) * D)[c4];
+    acc.x += w * y.x;
+    acc.y += w * y.y;
+    acc.z += w * y.z;
+    acc.w += w * y.w;
   }
   acc_s[slice][c4] = acc;
   __syncthreads();
@@ -579,11 +647,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     float4 v = acc_s[0][tid];
 #pragma unroll
     for (int sl = 1; sl < NSL; ++sl) {
-      const float4 x = acc_s[sl][tid];
-      v.x += x.x;
-      v.y += x.y;
-      v.z += x.z;
-      v.w += x.w;
+      const float4 y = acc_s[sl][tid];
+      v.x += y.x;
+      v.y += y.y;
+      v.z += y.z;
+      v.w += y.w;
     }
     reinterpret_cast<float4 *>(dst)[tid] = make_float4(v.x / Lt, v.y / Lt, v.z / Lt, v.w / Lt);
   }
@@ -592,8 +660,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 template <int D, int NT, int FMT, int QDT>
 hipError_t split_one(const AttnArgs &a, hipStream_t s) {
   // fp32 queries need the hi+lo pair; bf16 queries are one exact f16
-  hipLaunchKernelGGL((attn_split_kernel<D, NT, FMT, QDT == 0 ? 1 : 0, kTeams>), dim3(a.n_splits, a.num_kv_heads, a.num_seqs),
-                     dim3(256 * kTeams), 0, s, a);
+  constexpr int QLO = QDT == 0 ? 1 : 0;
+  const dim3 grid(a.n_splits, a.num_kv_heads, a.num_seqs);
+  if (a.k_new != nullptr)
+    hipLaunchKernelGGL((attn_split_kernel<D, NT, FMT, QLO, kTeams, 1>), grid, dim3(256 * kTeams), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_split_kernel<D, NT, FMT, QLO, kTeams, 0>), grid, dim3(256 * kTeams), 0, s, a);
   return hipGetLastError();
 }
 

@@ -7,9 +7,16 @@
 
 namespace kvq {
 
-constexpr int kPage = 64;       // token slots per page
-constexpr int kTeams = 2;       // 4-wave teams per attention workgroup
-constexpr int kTargetWgs = 256; // one attention workgroup per compute unit of the chip
+#ifndef KVQ_NT_LOADS
+#define KVQ_NT_LOADS 1
+#endif
+#ifndef KVQ_TEAMS
+#define KVQ_TEAMS 2
+#endif
+
+constexpr int kPage = 64;                   // token slots per page
+constexpr int kTeams = KVQ_TEAMS;           // 4-wave teams per attention workgroup
+constexpr int kTargetWgs = 512 / KVQ_TEAMS; // 8 waves per compute unit of the 256-CU chip
 constexpr int kMaxChunkPages = 256;   // pages of one attention chunk (block ids staged in LDS)
 constexpr int kMergeMaxSplits = 1024; // chunk weights the merge keeps in LDS
 
@@ -33,6 +40,7 @@ struct AttnArgs {
   float *ws_ml;  // [B][Hkv][n_splits][R][2]: running max (log2 units), running sum
   float *ws_o;   // [B][Hkv][n_splits][R][D]: unnormalized output
   float *out;    // [B][T][Hq][D]
+  const void *k_new, *v_new;  // fused decode step: [B][T][Hkv][D] rows to append first (else null)
   int32_t num_seqs, num_blocks, num_kv_heads, num_q_heads, group, T, rows;
   int32_t max_blocks, max_seq_len, tokens_per_split, n_splits;
   float qk_scale_log2;  // softmax_scale * log2(e)

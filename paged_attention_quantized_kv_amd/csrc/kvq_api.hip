@@ -67,9 +67,11 @@ enum class Phase { kBoth, kSplit, kMerge };
 int attn_call(Phase phase, const kvq_cache_t *cache, const void *q, int32_t q_dtype, int32_t num_seqs, int32_t T,
               int32_t num_q_heads, const int32_t *block_table, int32_t max_blocks_per_seq, const int32_t *seq_lens,
               int32_t max_seq_len, float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
-              void *stream) {
+              void *stream, const void *k_new = nullptr, const void *v_new = nullptr) {
   int rc = check_cache(cache);
   if (rc) return rc;
+  if ((k_new == nullptr) != (v_new == nullptr)) return KVQ_ERR_INVALID_ARG;
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return KVQ_ERR_INVALID_ARG;
   if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARG;
   if (!q || !aligned16(q) || !out || !aligned16(out) || !workspace || !aligned16(workspace)) return KVQ_ERR_INVALID_ARG;
   if (!block_table || !aligned4(block_table) || !seq_lens || !aligned4(seq_lens)) return KVQ_ERR_INVALID_ARG;
@@ -92,6 +94,8 @@ int attn_call(Phase phase, const kvq_cache_t *cache, const void *q, int32_t q_dt
   a.ws_ml = static_cast<float *>(workspace);
   a.ws_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + s.ml_bytes);
   a.out = out;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.num_seqs = num_seqs;
   a.num_blocks = cache->num_blocks;
   a.num_kv_heads = cache->num_kv_heads;
@@ -201,6 +205,15 @@ int paged_decode_attn_merge(const kvq_cache_t *cache, const void *q, int32_t q_d
                             void *workspace, size_t workspace_bytes, void *stream) {
   return attn_call(Phase::kMerge, cache, q, q_dtype, num_seqs, T, num_q_heads, block_table, max_blocks_per_seq,
                    seq_lens, max_seq_len, softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+int paged_decode_step(const kvq_cache_t *cache, const void *k_new, const void *v_new, const void *q, int32_t dtype,
+                      int32_t num_seqs, int32_t T, int32_t num_q_heads, const int32_t *block_table,
+                      int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t max_seq_len, float softmax_scale,
+                      float *out, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!k_new || !v_new) return KVQ_ERR_INVALID_ARG;
+  return attn_call(Phase::kBoth, cache, q, dtype, num_seqs, T, num_q_heads, block_table, max_blocks_per_seq, seq_lens,
+                   max_seq_len, softmax_scale, out, workspace, workspace_bytes, stream, k_new, v_new);
 }
 
 }  // extern "C"

@@ -204,3 +204,52 @@ def test_fp8_code_conversion_is_exact_for_every_code(K):
     got = out.cpu().numpy()[:, 0, 0, :2]
     assert np.array_equal(got[:, 0], np.full(n, 448.0, np.float32))
     assert np.array_equal(got[:, 1], vals)
+
+
+def _fused_check(K, w, rows=None):
+    """Fill all but the T decode rows, then one paged_decode_step call; the pool must
+    equal the oracle's and the outputs must match it."""
+    s = w.shape
+    say(f"[fused] {s.name} B={s.B} T={s.T} lens={s.lens[:8]} fmt={s.fmt}")
+    cache = H.new_cache(K, w, DEV)
+    bt = torch.from_numpy(w.block_table).to(DEV)
+    for b in range(s.B):
+        L = int(w.seq_lens[b])
+        if L - s.T > 0:
+            k = H.src_tensor(w.rows("k", b, 0, L - s.T), s.src, DEV)
+            v = H.src_tensor(w.rows("v", b, 0, L - s.T), s.src, DEV)
+            K.kv_append_quant(cache, k, v, bt[b:b + 1].contiguous(), torch.tensor([0], dtype=torch.int32, device=DEV))
+    q = H.src_tensor(w.q, s.src, DEV)
+    kn = H.src_tensor(w.new_rows("k"), s.src, DEV)
+    vn = H.src_tensor(w.new_rows("v"), s.src, DEV)
+    sl = torch.from_numpy(w.seq_lens).to(DEV)
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    ws = K.alloc_workspace(cache, s.B, s.T, s.Hq, w.max_seq_len, device=DEV)
+    K.paged_decode_step(cache, kn, vn, q, bt, sl, w.max_seq_len, w.softmax_scale, out, ws)
+    torch.cuda.synchronize()
+    pool = H.oracle_pool(O, w)
+    mism = H.pool_equal(cache, pool)
+    assert mism == {"k_codes": 0, "v_codes": 0, "k_scales": 0, "v_scales": 0}, mism
+    got = out.cpu().numpy().reshape(-1, s.D)
+    ref = pool.paged_attn(w.q, s.src, s.T, s.Hq, w.block_table, w.seq_lens, w.softmax_scale, rows=rows)
+    if rows is not None:
+        got = got[np.asarray(rows)]
+    err = float(np.abs(got - ref).max())
+    say(f"[fused] {s.name}: max-abs err {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= TOL
+    # the same step through the two separate calls gives bit-identical outputs
+    two = H.run_attn(K, w, cache, bt, DEV)
+    assert torch.equal(two, out)
+
+
+@pytest.mark.parametrize("name", ["tiny", "g6_t4_d256_bf16", "ragged_b3_t4", "mha_len1", "fp8_d128_f32",
+                                  "rows32_d128"])
+def test_fused_step_small(K, name):
+    _fused_check(K, S.make(SMALL[name], seed=S.seed_of("tiny") + 200 + list(SMALL).index(name)))
+
+
+def test_fused_step_mtp128k_and_cohort(K):
+    w = S.make("mtp128k")
+    _fused_check(K, w, rows=_sample_rows(w, 2))
+    w = S.make("c8")
+    _fused_check(K, w, rows=_sample_rows(w, 1))

@@ -19,6 +19,7 @@ Prints ONE JSON line.  --gpus N > 1 exits: this build runs on one GPU.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -34,6 +35,37 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 HEADLINE = "mtp128k"
 DEPTHS = ["qwen32k", "mtp128k", "full256k_int8", "full256k_fp8"]
 FLUSH_BYTES = 1.5 * 2 ** 30  # bytes read between two reads of one pool copy (> 256 MB MALL)
+KERNEL_SOURCES = ("internal.h", "quant_row.h", "attn.hip")  # what the split kernel is built from
+
+
+def kernel_sources_sha256():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_attention_quantized_kv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per split-kernel launch from the committed counter summary of this
+    workload (FETCH_SIZE and WRITE_SIZE passes, each scaled by what the same counter
+    reads for a copy kernel of known size).  None when there is no summary or the
+    kernel sources have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"attn_split_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for line in fh:
+            if "=" in line and not line.startswith((" ", "#")):
+                k, v = line.split("=", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return int(rec["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def host_cpu():
@@ -308,7 +340,8 @@ def main():
         "pct_hbm_peak": round(100 * head["kv_gbs"] / HBM_PEAK_GBS, 2),
         "tok_per_s": round(head["tok_per_s"], 1),
         "roofline": {"bound": "hbm", "achieved": round(head["split_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(head["split_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(head["split_gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(args.workload),
                      "kernel": "attn_split_kernel", "launch_avg_us": round(head["split_ms_avg"] * 1e3, 2),
                      "alg_bytes_per_launch": head["split_alg_bytes"]},
         "depths": {n: {"kv_gbs": round(r["kv_gbs"], 1), "pct_hbm_peak": round(100 * r["kv_gbs"] / HBM_PEAK_GBS, 2),

@@ -4,17 +4,17 @@
  * Two operations make up one decode step of a full-attention layer:
  *
  *   kv_append_quant    appends new K/V rows to a paged cache and quantizes them
- *                      on the way in.  The pages name this op kv_cache_append,
- *                      "the Op that now owns KV quantization", which stores
- *                      values from the represented BF16 source directly
+ *                      on the way in: in the engine of the pages, the append op
+ *                      (kv_cache_append) is where KV quantization happens, and
+ *                      values are quantized straight from their bf16 source
  *                      (NInfer-3090 README, intro and "RotorQuant KV (rk8v4)").
  *   paged_decode_attn  runs decode attention for 1..B sequences with T query
  *                      rows each (T=1 plain decode, T=4 for an MTP3 verify
- *                      round: a round covers concurrency x (draft window + 1)
- *                      token columns, NInfer-3090 README, "v0.9.1 cohort ..."),
- *                      dequantizing K/V on the fly over a shared page pool
- *                      (one pool fixed at startup and shared by every lane,
- *                      gzenz/ninfer README, "Current limits").
+ *                      round, whose width is the lane count times the draft
+ *                      window plus one: NInfer-3090 README, "Decode after the small-T kernels"),
+ *                      dequantizing K/V on the fly over one page pool that all
+ *                      sequences share, sized once at startup (gzenz/ninfer
+ *                      README, "Current limits").
  *
  * KV formats (NInfer-3090 README, "Choosing a KV format", table):
  *   KVQ_INT8_G64      int8 code per element, one fp16 scale per 64 dims per
@@ -105,7 +105,7 @@ typedef struct {
 
 /*
  * kv_append_quant -- quantize n_new rows per sequence and write them into the
- * pool (kv_cache_append owns KV quantization: NInfer-3090 README, intro).
+ * pool; quantization happens here (NInfer-3090 README, intro).
  *
  *   k_new, v_new        [num_seqs][n_new][num_kv_heads][head_dim] in src_dtype
  *                       (KVQ_BF16 or KVQ_F32); bf16 widens to fp32 exactly.
@@ -130,8 +130,9 @@ size_t paged_decode_attn_workspace_bytes(int32_t num_seqs, int32_t T, int32_t nu
 
 /*
  * paged_decode_attn -- out = softmax(q k^T * softmax_scale) v over the
- * dequantized cache ("attention re-reads the whole cache each step",
- * NInfer-3090 README, "Choosing a KV format").
+ * dequantized cache; every decode step reads the whole cache again, which
+ * is why the KV format sets the cost at depth (NInfer-3090 README, "Choosing
+ * a KV format").
  *
  *   q          [num_seqs][T][num_q_heads][head_dim] in q_dtype (KVQ_BF16 | KVQ_F32)
  *   seq_lens   [num_seqs] int32 (device): keys visible to the LAST query row of

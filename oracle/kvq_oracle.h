@@ -15,11 +15,11 @@
  *  - Row-scaled FP8 E4M3 KV: NInfer-3090 README, intro and "Current limits"
  *    (row-scaled FP8 E4M3 among the seven KV formats); one fp32 scale per token
  *    per KV head = absmax / 448.
- *  - Quantization happens when rows are appended (kv_cache_append owns KV
- *    quantization): NInfer-3090 README, intro and "RotorQuant KV (rk8v4)".
- *  - Decode attention re-reads the whole cache each step: NInfer-3090 README,
- *    "Choosing a KV format".  The result computed is softmax(q k^T * scale) v
- *    over the dequantized cache, in fp64.
+ *  - Quantization happens when rows are appended, in the append op:
+ *    NInfer-3090 README, intro and "RotorQuant KV (rk8v4)".
+ *  - Each decode step reads the whole cache: NInfer-3090 README, "Choosing a
+ *    KV format".  The result computed is softmax(q k^T * scale) v over the
+ *    dequantized cache, in fp64.
  *
  * Parity pins: every function here is checked by tests marked "not gpu"
  * against library conversions (numpy float16, torch float8_e4m3fn), closed

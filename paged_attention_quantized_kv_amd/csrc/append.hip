@@ -1,6 +1,6 @@
 // append.hip -- kv_append_quant: quantize new K/V rows on the way into the page
-// pool (kv_cache_append owns KV quantization: NInfer-3090 README, intro and
-// "RotorQuant KV (rk8v4)").
+// pool; the append op is where KV quantization happens (NInfer-3090 README,
+// intro and "RotorQuant KV (rk8v4)").
 //
 // One wave per (sequence, new row, KV head, K|V).  Each lane holds D/64
 // consecutive dims, so a 64-dim group is 64/(D/64) adjacent lanes and its

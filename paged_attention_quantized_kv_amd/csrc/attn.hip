@@ -1,8 +1,8 @@
 // attn.hip -- paged decode attention over the quantized page pool.
 //
-// The result is out = softmax(q k^T * scale) v over the dequantized cache
-// ("attention re-reads the whole cache each step": NInfer-3090 README,
-// "Choosing a KV format"); the context of each (sequence, KV head) is cut into
+// The result is out = softmax(q k^T * scale) v over the dequantized cache,
+// which every decode step reads in full (NInfer-3090 README, "Choosing a KV
+// format"); the context of each (sequence, KV head) is cut into
 // chunks (split-K over the context) whose partial results are merged with
 // log-sum-exp weights.
 //

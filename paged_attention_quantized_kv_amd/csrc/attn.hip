@@ -215,8 +215,50 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   // page reload that page and skip the math)
   auto page_of = [&](int it) -> int { return lds_pg[min(it * NTEAM + team, page1 - page0 - 1)]; };
   PageRegs<D, FMT> rA, rB;
+
+  // ---- fused decode step: the new rows at positions L-T .. L-1 that fall in this chunk
+  // (K and V of each, one wave per row).  When their first page is not loaded before
+  // iteration 3, the source rows are read now, quantized and stored during page 0, and
+  // the writing waves wait for their stores at the end of page 0, before the barrier
+  // that precedes every load of iteration 3 on; otherwise they are written here.
+  constexpr int NW = 4 * NTEAM, RPW = (16 + NW - 1) / NW;  // T <= 8: at most 16 rows
+  [[maybe_unused]] AppendArgs aa;
+  [[maybe_unused]] float xr[RPW][G64];
+  [[maybe_unused]] int blk_r[RPW];
+  int t_lo = 0, n_rows = 0;
+  bool defer = false;
+  if constexpr (APP != 0) {
+    aa.k_new = a.k_new;
+    aa.v_new = a.v_new;
+    aa.k_codes = const_cast<uint8_t *>(a.k_codes);
+    aa.v_codes = const_cast<uint8_t *>(a.v_codes);
+    aa.k_scales = const_cast<void *>(a.k_scales);
+    aa.v_scales = const_cast<void *>(a.v_scales);
+    aa.block_table = a.block_table;
+    aa.start_pos = nullptr;
+    aa.num_seqs = a.num_seqs;
+    aa.n_new = a.T;
+    aa.num_kv_heads = a.num_kv_heads;
+    aa.max_blocks = a.max_blocks;
+    aa.num_blocks = a.num_blocks;
+    t_lo = max(0, tok0 - (L - a.T));
+    n_rows = 2 * max(0, min(a.T, tok1 - (L - a.T)) - t_lo);
+    defer = (max((L - a.T) / kPage, page0) - page0) / NTEAM >= 3;
+    if (defer) {
+#pragma unroll
+      for (int k = 0; k < RPW; ++k) {
+        const int r = (tid >> 6) + k * NW;
+        blk_r[k] = -1;
+        if (r < n_rows) {
+          const int t = t_lo + (r >> 1);
+          blk_r[k] = bt[(L - a.T + t) / kPage];
+          load_row<D, QLO ? 0 : 1>(aa, b, t, kvh, r & 1, lane, xr[k]);
+        }
+      }
+    }
+  }
   // the first pages load while the queries are staged (and, for the fused step, the new
-  // rows quantized) -- unless one of them holds new rows, which must be written first
+  // rows read) -- unless one of them holds new rows, which must be written first
   const bool early = (APP == 0) || (page0 + NTEAM - 1 < (L - a.T) / kPage);
   if (early && n_it > 0) load_page<D, FMT>(rA, a, page_of(0), wave, lane, q4);
 
@@ -251,33 +293,17 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
       qs[idx + 64] = __builtin_bit_cast(uint4, f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]});
   }
   if constexpr (APP != 0) {
-    // fused decode step: the T new rows at positions L-T .. L-1 that fall in this chunk
-    // are quantized into the pool here, before any wave loads their page (the barrier
-    // below orders the stores before the loads)
-    const int t_lo = max(0, tok0 - (L - a.T)), t_hi = min(a.T, tok1 - (L - a.T));
-    AppendArgs aa;
-    aa.k_new = a.k_new;
-    aa.v_new = a.v_new;
-    aa.k_codes = const_cast<uint8_t *>(a.k_codes);
-    aa.v_codes = const_cast<uint8_t *>(a.v_codes);
-    aa.k_scales = const_cast<void *>(a.k_scales);
-    aa.v_scales = const_cast<void *>(a.v_scales);
-    aa.block_table = a.block_table;
-    aa.start_pos = nullptr;
-    aa.num_seqs = a.num_seqs;
-    aa.n_new = a.T;
-    aa.num_kv_heads = a.num_kv_heads;
-    aa.max_blocks = a.max_blocks;
-    aa.num_blocks = a.num_blocks;
-    for (int r = (tid >> 6); r < 2 * (t_hi - t_lo); r += 4 * NTEAM) {
-      const int t = t_lo + (r >> 1), which = r & 1;
-      const long pos = static_cast<long>(L) - a.T + t;
-      const int blk = bt[pos / kPage];
-      if (blk >= 0 && blk < a.num_blocks) quant_row<FMT, D, QLO ? 0 : 1>(aa, b, t, kvh, which, pos, blk, lane);
+    if (!defer) {
+      for (int r = (tid >> 6); r < n_rows; r += NW) {
+        const int t = t_lo + (r >> 1);
+        const long pos = static_cast<long>(L) - a.T + t;
+        const int blk = bt[pos / kPage];
+        if (blk >= 0 && blk < a.num_blocks) quant_row<FMT, D, QLO ? 0 : 1>(aa, b, t, kvh, r & 1, pos, blk, lane);
+      }
+      // a wave that wrote rows waits until its stores have reached L2, so every wave of this
+      // workgroup loads the new rows after the barrier below (no other workgroup reads them)
+      if ((tid >> 6) < n_rows) __builtin_amdgcn_s_waitcnt(0);
     }
-    // a wave that wrote rows waits until its stores have reached L2, so every wave of this
-    // workgroup loads the new rows after the barrier below (no other workgroup reads them)
-    if ((tid >> 6) < 2 * (t_hi - t_lo)) __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
   if (!early && n_it > 0) load_page<D, FMT>(rA, a, page_of(0), wave, lane, q4);
@@ -469,10 +495,23 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     }
     __syncthreads();
 
+    if constexpr (APP != 0) {
+      if (defer && it == 0) {  // the deferred rows of the fused step (see above)
+#pragma unroll
+        for (int k = 0; k < RPW; ++k) {
+          const int r = (tid >> 6) + k * NW;
+          if (r < n_rows && blk_r[k] >= 0 && blk_r[k] < a.num_blocks)
+            store_row<FMT, D>(aa, xr[k], kvh, r & 1, static_cast<long>(L) - a.T + t_lo + (r >> 1), blk_r[k], lane);
+        }
+      }
+    }
     if (valid && full) {
       accumulate(std::false_type{}, pr, p, pb);
     } else if (valid) {
       accumulate(std::true_type{}, pr, p, pb);
+    }
+    if constexpr (APP != 0) {
+      if (defer && it == 0 && (tid >> 6) < n_rows) __builtin_amdgcn_s_waitcnt(0);
     }
   };
 

@@ -37,21 +37,27 @@ __device__ inline uint32_t e4m3fn_rne_sat(float v) {
   return sign | code;
 }
 
-// Row t of sequence b, KV head h, K (which=0) or V (which=1): read from the
-// [B][n_new][Hkv][D] source, quantize, and store at position pos of the
-// sequence (slot pos % 64 of block blk).  Called by all 64 lanes of a wave.
-template <int FMT, int D, int SRC>
-__device__ inline void quant_row(const AppendArgs &a, int b, int t, int h, int which, long pos, int blk, int lane) {
+// Row t of sequence b, KV head h, K (which=0) or V (which=1) of the
+// [B][n_new][Hkv][D] source: this lane's D/64 consecutive elements, widened.
+template <int D, int SRC>
+__device__ inline void load_row(const AppendArgs &a, int b, int t, int h, int which, int lane, float (&x)[D / 64]) {
+  constexpr int E = D / 64;
+  const void *src = which ? a.v_new : a.k_new;
+  const size_t base = ((static_cast<size_t>(b) * a.n_new + t) * a.num_kv_heads + h) * D + lane * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = load_src<SRC>(src, base + e);
+}
+
+// Quantize a row held as x (D/64 elements per lane, see load_row) and store it
+// at position pos of the sequence: slot pos % 64 of block blk, KV head h.
+// Called by all 64 lanes of a wave.
+template <int FMT, int D>
+__device__ inline void store_row(const AppendArgs &a, const float (&x)[D / 64], int h, int which, long pos, int blk,
+                                 int lane) {
   constexpr int E = D / 64;            // elements per lane
   constexpr int LPG = 64 / E;          // lanes per 64-dim group
   const int slot = static_cast<int>(pos % kPage);
   const int run = (slot % 16) / 4, spos = (slot / 16) * 4 + slot % 4;
-
-  const void *src = which ? a.v_new : a.k_new;
-  const size_t base = ((static_cast<size_t>(b) * a.n_new + t) * a.num_kv_heads + h) * D + lane * E;
-  float x[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) x[e] = load_src<SRC>(src, base + e);
 
   const size_t page = static_cast<size_t>(blk) * a.num_kv_heads + h;
   uint8_t *codes = (which ? a.v_codes : a.k_codes) + page * kPage * D;
@@ -110,6 +116,14 @@ __device__ inline void quant_row(const AppendArgs &a, int b, int t, int h, int w
       codes[(static_cast<size_t>(d / 16) * 4 + run) * 256 + (d % 16) * 16 + spos] = static_cast<uint8_t>(c[e]);
     }
   }
+}
+
+// load_row then store_row: row t of sequence b goes to position pos (block blk).
+template <int FMT, int D, int SRC>
+__device__ inline void quant_row(const AppendArgs &a, int b, int t, int h, int which, long pos, int blk, int lane) {
+  float x[D / 64];
+  load_row<D, SRC>(a, b, t, h, which, lane, x);
+  store_row<FMT, D>(a, x, h, which, pos, blk, lane);
 }
 
 }  // namespace kvq

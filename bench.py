@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 HEADLINE = "mtp128k"
 DEPTHS = ["qwen32k", "mtp128k", "full256k_int8", "full256k_fp8"]
+SETTLE_S = 0.2  # seconds of untimed back-to-back steps before the warmup steps
 FLUSH_BYTES = 1.5 * 2 ** 30  # bytes read between two reads of one pool copy (> 256 MB MALL)
 KERNEL_SOURCES = ("internal.h", "quant_row.h", "attn.hip")  # what the split kernel is built from
 
@@ -190,8 +191,17 @@ class Run:
         if eager:
             return self.measure_eager(steps, warmup)
         self.build_graphs()
-        for i in range(warmup):
-            self.g_one[i % self.n_copies].replay()
+        # the GPU reaches its steady clocks only after tens of ms of sustained load: run
+        # back-to-back steps for SETTLE_S seconds, then the W warmup steps, untimed
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < SETTLE_S:
+            self.g_all.replay()
+            torch.cuda.synchronize()
+        wfull, wrest = divmod(warmup, self.n_copies)
+        for _ in range(wfull):
+            self.g_all.replay()
+        for i in range(wrest):
+            self.g_one[i].replay()
         torch.cuda.synchronize()
         full, rest = divmod(steps, self.n_copies)
         # exactly `steps` steps, synchronized on both sides; GPU time from events on the

@@ -75,6 +75,16 @@ __device__ inline void split_f16(float x0, float x1, f16x2 &hi, f16x2 &lo) {
                                                             x1 - static_cast<float>(hi[1])));
 }
 
+// The same split of the products p * s (s in fp16): hi = f16(p*s) toward zero, lo =
+// f16(p*s - hi) with the residual taken from the unrounded product; each product and
+// residual is one mixed-precision fma.
+__device__ inline void split_scaled(float p0, float p1, f16x2 s, f16x2 &hi, f16x2 &lo) {
+  const float s0 = static_cast<float>(s[0]), s1 = static_cast<float>(s[1]);
+  hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf(p0, s0, 0.0f), __builtin_fmaf(p1, s1, 0.0f)));
+  lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf(p0, s0, -static_cast<float>(hi[0])),
+                                                            __builtin_fmaf(p1, s1, -static_cast<float>(hi[1]))));
+}
+
 // Element i of the query tensor, widened to fp32 (bf16 widening is exact).
 template <bool BF16>
 __device__ inline float load_q(const void *q, size_t i) {
@@ -106,6 +116,9 @@ __device__ inline float sum_xor32(float x) {
 // 2^x with the hardware exponential: exact at 0 and -inf; results below the
 // normal range (weights under 2^-126 of the running maximum) may flush to zero.
 __device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Rescaling threshold of the online softmax, log2 units (see the softmax phase).
+constexpr float kLazy = 8.0f;
 
 // One wave's share of one page: its K tile (16 keys x all dims) and its V dim
 // tiles (all 64 keys), with their scales.
@@ -411,26 +424,28 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
         for (int kk = 0; kk < 2; ++kk) {
           const int kt = 2 * ks + kk;
           const float4 pw = *reinterpret_cast<const float4 *>(pb + (16 * nt + c16) * PST + 16 * kt + 4 * q4);
-          float sv[4];
+          const float pp[4] = {pw.x, pw.y, pw.z, pw.w};
           if constexpr (FMT == 0) {
             const uint4 w = pr.vs[ks];
-            f16x2_to_f32(kk ? w.z : w.x, sv[0], sv[1]);
-            f16x2_to_f32(kk ? w.w : w.y, sv[2], sv[3]);
+            f16x2 s01 = __builtin_bit_cast(f16x2, kk ? w.z : w.x), s23 = __builtin_bit_cast(f16x2, kk ? w.w : w.y);
+            if constexpr (MASKED) {  // unwritten slots (weight 0) may hold NaN scales
+              s01 = f16x2{pp[0] != 0.0f ? s01[0] : _Float16(0), pp[1] != 0.0f ? s01[1] : _Float16(0)};
+              s23 = f16x2{pp[2] != 0.0f ? s23[0] : _Float16(0), pp[3] != 0.0f ? s23[1] : _Float16(0)};
+            }
+            split_scaled(pp[0], pp[1], s01, hi[2 * kk], lo[2 * kk]);
+            split_scaled(pp[2], pp[3], s23, hi[2 * kk + 1], lo[2 * kk + 1]);
           } else {
-            sv[0] = __uint_as_float(pr.vs[kt].x);
-            sv[1] = __uint_as_float(pr.vs[kt].y);
-            sv[2] = __uint_as_float(pr.vs[kt].z);
-            sv[3] = __uint_as_float(pr.vs[kt].w);
-          }
-          const float pp[4] = {pw.x, pw.y, pw.z, pw.w};
-          float pv[4];
+            const uint4 w = pr.vs[kt];
+            const float sv[4] = {__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w)};
+            float pv[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pv[i] = pp[i] * sv[i];
-            if constexpr (MASKED) pv[i] = (pp[i] != 0.0f) ? pv[i] : 0.0f;  // unwritten slots: NaN scales
+            for (int i = 0; i < 4; ++i) {
+              pv[i] = pp[i] * sv[i];
+              if constexpr (MASKED) pv[i] = (pp[i] != 0.0f) ? pv[i] : 0.0f;  // unwritten slots: NaN scales
+            }
+            split_f16(pv[0], pv[1], hi[2 * kk], lo[2 * kk]);
+            split_f16(pv[2], pv[3], hi[2 * kk + 1], lo[2 * kk + 1]);
           }
-          split_f16(pv[0], pv[1], hi[2 * kk], lo[2 * kk]);
-          split_f16(pv[2], pv[3], hi[2 * kk + 1], lo[2 * kk + 1]);
         }
         bh[nt] = f16x8{hi[0][0], hi[0][1], hi[1][0], hi[1][1], hi[2][0], hi[2][1], hi[3][0], hi[3][1]};
         bl[nt] = f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]};
@@ -479,18 +494,23 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
       const int r = 16 * nt + c16;
       const float4 mw4 = lds_mx[team][buf][r];
       const float pmax = fmaxf(fmaxf(mw4.x, mw4.y), fmaxf(mw4.z, mw4.w));
-      const float mnew = fmaxf(m[nt], pmax);
-      const float msafe = (mnew == -INFINITY) ? 0.0f : mnew;
-      const float alpha = exp2_hw(m[nt] - msafe);
-      m[nt] = mnew;
-      float pv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pv[i] = exp2_hw(z[nt][i] - msafe);
-      lsum[nt] = lsum[nt] * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
-      if (__any(alpha != 1.0f)) {
+      // the reference maximum m of a row moves only when a page's maximum exceeds it by
+      // more than kLazy (log2 units): weights stay <= 2^kLazy, and o and l are rescaled
+      // only on those (rare) pages
+      const bool up = pmax > m[nt] + kLazy;  // m = -inf: up as soon as the row sees a key
+      if (__any(up)) {
+        const float mnew = up ? pmax : m[nt];
+        const float alpha = up ? exp2_hw(m[nt] - mnew) : 1.0f;  // 0 when m was -inf
+        m[nt] = mnew;
+        lsum[nt] *= alpha;
 #pragma unroll
         for (int j = 0; j < DPW; ++j) o[nt][j] *= alpha;
       }
+      const float msafe = (m[nt] == -INFINITY) ? 0.0f : m[nt];
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[i] = exp2_hw(z[nt][i] - msafe);
+      lsum[nt] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
       *reinterpret_cast<float4 *>(pb + r * PST + 16 * wave + 4 * q4) = make_float4(pv[0], pv[1], pv[2], pv[3]);
     }
     __syncthreads();

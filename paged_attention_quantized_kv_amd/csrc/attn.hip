@@ -143,31 +143,49 @@ __device__ inline uint4 ld_stream(const uint4 *p) {
 #endif
 }
 
+// The K half of one wave's share of a page (its key tile and the tile's scales) and
+// the V half (its dim tiles and all 64 keys' scales), issued separately so the loads of
+// the next page spread over the current one.
 template <int D, int FMT>
-__device__ inline void load_page(PageRegs<D, FMT> &r, const AttnArgs &a, int pg_any, int wave, int lane, int q4) {
-  constexpr int G64 = D / 64, NCH = D / 16, DPW = D / 64;
+__device__ inline void load_k_part(PageRegs<D, FMT> &r, const AttnArgs &a, int pg_any, int wave, int lane, int q4) {
+  constexpr int G64 = D / 64, NCH = D / 16;
   const size_t pg = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pg_any));  // wave-uniform page
   const uint4 *kp = reinterpret_cast<const uint4 *>(a.k_codes + pg * kPage * D);
-  const uint4 *vp = reinterpret_cast<const uint4 *>(a.v_codes + pg * kPage * D);
 #pragma unroll
   for (int cg = 0; cg < G64; ++cg) r.k[cg] = ld_stream(kp + (wave * NCH + 4 * cg) * 16 + lane);
+  if constexpr (FMT == 0) {
+    const uint4 *ksp = reinterpret_cast<const uint4 *>(static_cast<const _Float16 *>(a.k_scales) + pg * D);
+#pragma unroll
+    for (int j = 0; j < PageRegs<D, FMT>::KSN; ++j) r.ks[j] = ksp[(q4 * 4 + wave) * PageRegs<D, FMT>::KSN + j];
+  } else {
+    const uint4 *ksp = reinterpret_cast<const uint4 *>(static_cast<const float *>(a.k_scales) + pg * kPage);
+    r.ks[0] = ksp[q4 * 4 + wave];
+  }
+}
+
+template <int D, int FMT>
+__device__ inline void load_v_part(PageRegs<D, FMT> &r, const AttnArgs &a, int pg_any, int wave, int lane, int q4) {
+  constexpr int G64 = D / 64, DPW = D / 64;
+  const size_t pg = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pg_any));
+  const uint4 *vp = reinterpret_cast<const uint4 *>(a.v_codes + pg * kPage * D);
 #pragma unroll
   for (int j = 0; j < DPW; ++j) r.v[j] = ld_stream(vp + (wave * DPW + j) * 64 + lane);
   if constexpr (FMT == 0) {
-    const uint4 *ksp = reinterpret_cast<const uint4 *>(static_cast<const _Float16 *>(a.k_scales) + pg * D);
     const uint4 *vsp = reinterpret_cast<const uint4 *>(static_cast<const _Float16 *>(a.v_scales) + pg * D);
     const int g = (wave * DPW) / 4;  // the 64-dim group of this wave's dims
 #pragma unroll
-    for (int j = 0; j < PageRegs<D, FMT>::KSN; ++j) r.ks[j] = ksp[(q4 * 4 + wave) * PageRegs<D, FMT>::KSN + j];
-#pragma unroll
     for (int j = 0; j < 2; ++j) r.vs[j] = vsp[(q4 * G64 + g) * 2 + j];
   } else {
-    const uint4 *ksp = reinterpret_cast<const uint4 *>(static_cast<const float *>(a.k_scales) + pg * kPage);
     const uint4 *vsp = reinterpret_cast<const uint4 *>(static_cast<const float *>(a.v_scales) + pg * kPage);
-    r.ks[0] = ksp[q4 * 4 + wave];
 #pragma unroll
     for (int j = 0; j < 4; ++j) r.vs[j] = vsp[q4 * 4 + j];
   }
+}
+
+template <int D, int FMT>
+__device__ inline void load_page(PageRegs<D, FMT> &r, const AttnArgs &a, int pg_any, int wave, int lane, int q4) {
+  load_k_part<D, FMT>(r, a, pg_any, wave, lane, q4);
+  load_v_part<D, FMT>(r, a, pg_any, wave, lane, q4);
 }
 
 __device__ inline void f16x2_to_f32(uint32_t w, float &x, float &y) {
@@ -462,7 +480,9 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     }
   };
 
-  auto step = [&](PageRegs<D, FMT> &pr, int it) {
+  // one page: pr holds it; the next page's K half is already in flight in nx, and its
+  // V half is issued once the page maxima are exchanged
+  auto step = [&](PageRegs<D, FMT> &pr, PageRegs<D, FMT> &nx, int pg_next, int it) {
     const int p = page0 + it * NTEAM + team;
     const bool valid = p < page1;                              // uniform per team
     const bool full = (p * kPage + kPage - 1) <= (L - a.T);   // every real row sees every key of the page
@@ -486,6 +506,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
       for (int nt = 0; nt < NT; ++nt) reinterpret_cast<float *>(&lds_mx[team][buf][16 * nt + c16])[wave] = mloc[nt];
     }
     __syncthreads();
+    load_v_part<D, FMT>(nx, a, pg_next, wave, lane, q4);
 
     // ---- phase 2: online softmax over the page (identical in the 4 waves of the team)
     float *pb = pbuf + (team * 2 + buf) * ROWS * PST;
@@ -537,11 +558,13 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 
   if (n_it > 0) {
     for (int it = 0;; it += 2) {
-      load_page<D, FMT>(rB, a, page_of(min(it + 1, n_it - 1)), wave, lane, q4);
-      step(rA, it);
+      const int pgB = page_of(min(it + 1, n_it - 1));
+      load_k_part<D, FMT>(rB, a, pgB, wave, lane, q4);
+      step(rA, rB, pgB, it);
       if (it + 1 >= n_it) break;
-      load_page<D, FMT>(rA, a, page_of(min(it + 2, n_it - 1)), wave, lane, q4);
-      step(rB, it + 1);
+      const int pgA = page_of(min(it + 2, n_it - 1));
+      load_k_part<D, FMT>(rA, a, pgA, wave, lane, q4);
+      step(rB, rA, pgA, it + 1);
       if (it + 2 >= n_it) break;
     }
   }

@@ -257,13 +257,14 @@ def test_fused_step_mtp128k_and_cohort(K):
 
 @pytest.mark.parametrize("fmt", [S.FMT_INT8_G64, S.FMT_FP8_ROW])
 def test_fused_step_late_rows_straddling_pages(K, fmt):
-    """Sequence 0's new rows straddle a page boundary deep inside its chunk, where the
-    fused step quantizes them while the chunk's first page is processed; sequence 1's
-    rows fall in the first pages of their chunk, where they are written up front."""
-    shp = S.tiny_shape(B=2, T=4, Hq=24, Hkv=4, D=128, lens=(64 * 227 + 2, 64 * 256 + 2), src=S.SRC_BF16,
-                       fmt=fmt, outliers=True, name="late_rows")
+    """New rows deep inside a chunk (the last page of a 16-page chunk), where the fused
+    step quantizes them while the chunk's first page is processed, and rows that straddle
+    into the first page of the next chunk, which that chunk writes up front."""
+    L0 = 64 * 336 + 2  # rows 21502..21505: page 335 (last of chunk 20) and page 336 (first of chunk 21)
+    shp = S.tiny_shape(B=2, T=4, Hq=24, Hkv=4, D=128, lens=(L0, 32768), src=S.SRC_BF16, fmt=fmt, outliers=True,
+                       name="late_rows")
     n_splits, tps = K.num_splits(shp.B, shp.T, shp.Hq, shp.Hkv, shp.D, max(shp.lens))
-    assert tps == 640, tps  # 10 pages per chunk at this shape
-    first_new_page = (shp.lens[0] - shp.T) // 64
-    assert (first_new_page % 10) // 2 >= 3 and (shp.lens[0] - 1) // 64 != first_new_page
-    _fused_check(K, S.make(shp, seed=S.seed_of("tiny") + 300 + fmt))
+    assert tps == 16 * 64, tps
+    assert (L0 - shp.T) // 64 == 16 * 20 + 15 and (L0 - 1) // 64 == 16 * 21
+    w = S.make(shp, seed=S.seed_of("tiny") + 300 + fmt)
+    _fused_check(K, w, rows=_sample_rows(w, 6))

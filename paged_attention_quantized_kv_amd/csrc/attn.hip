@@ -75,6 +75,15 @@ __device__ inline void split_f16(float x0, float x1, f16x2 &hi, f16x2 &lo) {
                                                             x1 - static_cast<float>(hi[1])));
 }
 
+// The products p * s as an f16 hi+lo pair when p itself arrives as an f16 hi+lo pair
+// (ph, pl) and s is fp16: hi = f16(ph*s); the residual ph*s - hi is exact in f16, and
+// lo = f16(pl*s + residual).  Three packed f16 operations per pair of keys.
+__device__ inline void scale_pair(f16x2 ph, f16x2 pl, f16x2 s, f16x2 &hi, f16x2 &lo) {
+  hi = ph * s;
+  const f16x2 r = __builtin_elementwise_fma(ph, s, -hi);
+  lo = __builtin_elementwise_fma(pl, s, r);
+}
+
 // The same split of the products p * s (s in fp16): hi = f16(p*s) toward zero, lo =
 // f16(p*s - hi) with the residual taken from the unrounded product; each product and
 // residual is one mixed-precision fma.
@@ -363,17 +372,37 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 #pragma unroll
       for (int i = 0; i < 4; ++i) z[nt][i] = 0.0f;
     }
+    // the query fragments of 64-dim group cg, read from LDS two groups ahead of their use
+    // (bf16 queries; fp32 queries, with twice the fragments, read them at their use)
+    constexpr int QPF = QLO ? 1 : 2;  // groups of fragments in flight
+    f16x8 qf[QPF][2][NT][QP];
+    auto read_q = [&](f16x8 (&dst)[2][NT][QP], int cg) {
+#pragma unroll
+      for (int hk = 0; hk < 2; ++hk)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int hl = 0; hl < QP; ++hl) dst[hk][nt][hl] = lds_f16x8(&qs[(((nt * G64 + cg) * 2 + hk) * QP + hl) * 64 + lane]);
+    };
+#pragma unroll
+    for (int c = 0; c < QPF && c < G64; ++c) read_q(qf[c], c);
 #pragma unroll
     for (int cg = 0; cg < G64; ++cg) {
+      f16x8 (&qc)[2][NT][QP] = qf[cg % QPF];
+      if constexpr (QPF == 1) {
+        if (cg > 0) read_q(qc, cg);
+      }
 #pragma unroll
       for (int hk = 0; hk < 2; ++hk) {
         const f16x8 ka = hk ? codes_to_f16<FMT>(pr.k[cg].z, pr.k[cg].w) : codes_to_f16<FMT>(pr.k[cg].x, pr.k[cg].y);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const int idx = ((nt * G64 + cg) * 2 + hk) * QP * 64 + lane;
-          acc[nt] = mfma16(ka, lds_f16x8(&qs[idx]), acc[nt]);
-          if constexpr (QLO) acc[nt] = mfma16(ka, lds_f16x8(&qs[idx + 64]), acc[nt]);
+          acc[nt] = mfma16(ka, qc[hk][nt][0], acc[nt]);
+          if constexpr (QLO) acc[nt] = mfma16(ka, qc[hk][nt][QP - 1], acc[nt]);
         }
+      }
+      if constexpr (QPF == 2) {
+        if (cg + 2 < G64) read_q(qc, cg + 2);
       }
       if constexpr (FMT == 0) {  // fold each key's fp16 group scale, restart the group sum
         const uint4 w = pr.ks[cg >> 1];
@@ -441,18 +470,21 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           const int kt = 2 * ks + kk;
-          const float4 pw = *reinterpret_cast<const float4 *>(pb + (16 * nt + c16) * PST + 16 * kt + 4 * q4);
-          const float pp[4] = {pw.x, pw.y, pw.z, pw.w};
           if constexpr (FMT == 0) {
+            const uint4 pw = *reinterpret_cast<const uint4 *>(pb + (16 * nt + c16) * PST + 16 * kt + 4 * q4);
+            const f16x2 h01 = __builtin_bit_cast(f16x2, pw.x), h23 = __builtin_bit_cast(f16x2, pw.y);
+            const f16x2 l01 = __builtin_bit_cast(f16x2, pw.z), l23 = __builtin_bit_cast(f16x2, pw.w);
             const uint4 w = pr.vs[ks];
             f16x2 s01 = __builtin_bit_cast(f16x2, kk ? w.z : w.x), s23 = __builtin_bit_cast(f16x2, kk ? w.w : w.y);
             if constexpr (MASKED) {  // unwritten slots (weight 0) may hold NaN scales
-              s01 = f16x2{pp[0] != 0.0f ? s01[0] : _Float16(0), pp[1] != 0.0f ? s01[1] : _Float16(0)};
-              s23 = f16x2{pp[2] != 0.0f ? s23[0] : _Float16(0), pp[3] != 0.0f ? s23[1] : _Float16(0)};
+              s01 = f16x2{h01[0] != _Float16(0) ? s01[0] : _Float16(0), h01[1] != _Float16(0) ? s01[1] : _Float16(0)};
+              s23 = f16x2{h23[0] != _Float16(0) ? s23[0] : _Float16(0), h23[1] != _Float16(0) ? s23[1] : _Float16(0)};
             }
-            split_scaled(pp[0], pp[1], s01, hi[2 * kk], lo[2 * kk]);
-            split_scaled(pp[2], pp[3], s23, hi[2 * kk + 1], lo[2 * kk + 1]);
+            scale_pair(h01, l01, s01, hi[2 * kk], lo[2 * kk]);
+            scale_pair(h23, l23, s23, hi[2 * kk + 1], lo[2 * kk + 1]);
           } else {
+            const float4 pw = *reinterpret_cast<const float4 *>(pb + (16 * nt + c16) * PST + 16 * kt + 4 * q4);
+            const float pp[4] = {pw.x, pw.y, pw.z, pw.w};
             const uint4 w = pr.vs[kt];
             const float sv[4] = {__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w)};
             float pv[4];
@@ -532,7 +564,18 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 #pragma unroll
       for (int i = 0; i < 4; ++i) pv[i] = exp2_hw(z[nt][i] - msafe);
       lsum[nt] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-      *reinterpret_cast<float4 *>(pb + r * PST + 16 * wave + 4 * q4) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+      if constexpr (FMT == 0) {
+        // INT8: the weights go out as f16 hi+lo pairs (the V scales, fp16, are applied by the
+        // accumulating wave with packed f16 arithmetic)
+        f16x2 h01, l01, h23, l23;
+        split_f16(pv[0], pv[1], h01, l01);
+        split_f16(pv[2], pv[3], h23, l23);
+        *reinterpret_cast<uint4 *>(pb + r * PST + 16 * wave + 4 * q4) =
+            make_uint4(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23),
+                       __builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23));
+      } else {
+        *reinterpret_cast<float4 *>(pb + r * PST + 16 * wave + 4 * q4) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+      }
     }
     __syncthreads();
 

@@ -223,6 +223,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   __shared__ uint4 qs[SM::QS];
   __shared__ float4 pbuf4[SM::PBF / 4];
   __shared__ float4 lds_mx[NTEAM][2][ROWS];  // per row: the 4 waves' page maxima
+  __shared__ int32_t lds_over[2][4 * NTEAM];  // per wave: a page maximum passed the reference by > kLazy
   __shared__ float lds_l[NTEAM][4][ROWS];
   __shared__ float lds_m[NTEAM][ROWS];
   __shared__ int32_t lds_pg[kMaxChunkPages];  // pool page (block * Hkv + kvh) of each page of the chunk
@@ -537,21 +538,55 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) reinterpret_cast<float *>(&lds_mx[team][buf][16 * nt + c16])[wave] = mloc[nt];
     }
-    __syncthreads();
     load_v_part<D, FMT>(nx, a, pg_next, wave, lane, q4);
 
-    // ---- phase 2: online softmax over the page (identical in the 4 waves of the team)
+    // ---- phase 2: softmax weights against the team's reference maxima m (one per row,
+    // identical in the 4 waves).  m moves only when a page maximum passes it by more than
+    // kLazy (log2 units), so weights stay <= 2^kLazy.  Each wave first assumes that no
+    // maximum of the page passes m by that much and writes its weights with the current
+    // m; if any wave of the workgroup saw such a maximum, all waves move m to the page
+    // maxima exchanged beside the weights, rescale o and l, and rewrite their weights.
     float *pb = pbuf + (team * 2 + buf) * ROWS * PST;
+    float psum[NT];
+    auto write_weights = [&]() {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int r = 16 * nt + c16;
-      const float4 mw4 = lds_mx[team][buf][r];
-      const float pmax = fmaxf(fmaxf(mw4.x, mw4.y), fmaxf(mw4.z, mw4.w));
-      // the reference maximum m of a row moves only when a page's maximum exceeds it by
-      // more than kLazy (log2 units): weights stay <= 2^kLazy, and o and l are rescaled
-      // only on those (rare) pages
-      const bool up = pmax > m[nt] + kLazy;  // m = -inf: up as soon as the row sees a key
-      if (__any(up)) {
+      for (int nt = 0; nt < NT; ++nt) {
+        const int r = 16 * nt + c16;
+        const float msafe = (m[nt] == -INFINITY) ? 0.0f : m[nt];
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[i] = exp2_hw(z[nt][i] - msafe);
+        psum[nt] = (pv[0] + pv[1]) + (pv[2] + pv[3]);
+        if constexpr (FMT == 0) {
+          // INT8: the weights go out as f16 hi+lo pairs (the V scales, fp16, are applied by
+          // the accumulating wave with packed f16 arithmetic)
+          f16x2 h01, l01, h23, l23;
+          split_f16(pv[0], pv[1], h01, l01);
+          split_f16(pv[2], pv[3], h23, l23);
+          *reinterpret_cast<uint4 *>(pb + r * PST + 16 * wave + 4 * q4) =
+              make_uint4(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23),
+                         __builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23));
+        } else {
+          *reinterpret_cast<float4 *>(pb + r * PST + 16 * wave + 4 * q4) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+        }
+      }
+    };
+    bool over = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) over |= mloc[nt] > m[nt] + kLazy;  // m = -inf: any visible key
+    const bool wave_over = __any(over);
+    if (!wave_over) write_weights();  // a wave that is over rewrites below anyway
+    if (lane == 0) lds_over[buf][(tid >> 6)] = wave_over ? 1 : 0;
+    __syncthreads();
+    int any_over = 0;
+#pragma unroll
+    for (int w = 0; w < 4 * NTEAM; ++w) any_over |= lds_over[buf][w];
+    if (any_over) {  // uniform over the workgroup
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float4 mw4 = lds_mx[team][buf][16 * nt + c16];
+        const float pmax = fmaxf(fmaxf(mw4.x, mw4.y), fmaxf(mw4.z, mw4.w));
+        const bool up = pmax > m[nt] + kLazy;
         const float mnew = up ? pmax : m[nt];
         const float alpha = up ? exp2_hw(m[nt] - mnew) : 1.0f;  // 0 when m was -inf
         m[nt] = mnew;
@@ -559,25 +594,11 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 #pragma unroll
         for (int j = 0; j < DPW; ++j) o[nt][j] *= alpha;
       }
-      const float msafe = (m[nt] == -INFINITY) ? 0.0f : m[nt];
-      float pv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pv[i] = exp2_hw(z[nt][i] - msafe);
-      lsum[nt] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-      if constexpr (FMT == 0) {
-        // INT8: the weights go out as f16 hi+lo pairs (the V scales, fp16, are applied by the
-        // accumulating wave with packed f16 arithmetic)
-        f16x2 h01, l01, h23, l23;
-        split_f16(pv[0], pv[1], h01, l01);
-        split_f16(pv[2], pv[3], h23, l23);
-        *reinterpret_cast<uint4 *>(pb + r * PST + 16 * wave + 4 * q4) =
-            make_uint4(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23),
-                       __builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23));
-      } else {
-        *reinterpret_cast<float4 *>(pb + r * PST + 16 * wave + 4 * q4) = make_float4(pv[0], pv[1], pv[2], pv[3]);
-      }
+      write_weights();
+      __syncthreads();
     }
-    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) lsum[nt] += psum[nt];
 
     if constexpr (APP != 0) {
       if (defer && it == 0) {  // the deferred rows of the fused step (see above)

@@ -705,10 +705,10 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   }
 }
 
-// Merge kernel: one workgroup of 256 threads per output row (b, t, h).  Every
-// load is issued up front: thread (slice, c4) holds 4 dims of up to MPER
-// chunks of its slice, and the chunk maxima and sums are read beside them;
-// block reductions give the log-sum-exp weights; the slices are summed in a
+// Merge kernel: one workgroup of 256 threads per 64-dim slice of an output row
+// (b, t, h).  Every load is issued up front: thread (sl, c4) holds 4 dims of up to
+// MPER chunks of chunk slice sl, and the chunk maxima and sums are read beside them;
+// block reductions give the log-sum-exp weights; the chunk slices are summed in a
 // fixed order (deterministic).
 __device__ inline float block_max(float v, float *red) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -727,32 +727,33 @@ __device__ inline float block_sum(float v, float *red) {
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  constexpr int C4 = D / 4;        // float4 columns of one row
-  constexpr int NSL = 256 / C4;    // chunk slices (4 for D=256, 8 for D=128)
-  constexpr int MPER = 16;         // chunks per slice kept in registers
+  constexpr int NQ = D / 64;       // 64-dim slices of a row, one workgroup each
+  constexpr int CS = 16;           // float4 columns of a slice
+  constexpr int NSL = 256 / CS;    // chunk slices
+  constexpr int MPER = 8;          // chunks per thread kept in registers
   constexpr int MAXS = kMergeMaxSplits;
   __shared__ float w_s[MAXS];
   __shared__ float red[4];
-  __shared__ float4 acc_s[NSL][C4];
-  const int row = blockIdx.x, tid = threadIdx.x;
+  __shared__ float4 acc_s[NSL][CS];
+  const int row = blockIdx.x / NQ, qs = blockIdx.x % NQ, tid = threadIdx.x;
   const int h = row % a.num_q_heads, t = (row / a.num_q_heads) % a.T, b = row / (a.num_q_heads * a.T);
-  float *dst = a.out + static_cast<size_t>(row) * D;
+  float *dst = a.out + static_cast<size_t>(row) * D + 64 * qs;
   const int L = a.seq_lens[b];
   if (L < a.T || L > a.max_seq_len || L > a.max_blocks * kPage) {
-    if (tid < D) dst[tid] = NAN;
+    if (tid < 64) dst[tid] = NAN;
     return;
   }
   const int kvh = h / a.group, r = t * a.group + h % a.group;
   const int ns = (L + a.tokens_per_split - 1) / a.tokens_per_split;
   const size_t part0 = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits;
-  const int c4 = tid % C4, slice = tid / C4;
+  const int c4 = tid % CS, sl = tid / CS, col = qs * CS + c4;
 
-  // ---- issue the first MPER partial-output loads of this slice and the chunk statistics
+  // ---- issue the first MPER partial-output loads of this thread and the chunk statistics
   float4 x[MPER];
 #pragma unroll
   for (int k = 0; k < MPER; ++k) {
-    const int s = min(slice + k * NSL, ns - 1);
-    x[k] = reinterpret_cast<const float4 *>(a.ws_o + ((part0 + s) * a.rows + r) * D)[c4];
+    const int s = min(sl + k * NSL, ns - 1);
+    x[k] = reinterpret_cast<const float4 *>(a.ws_o + ((part0 + s) * a.rows + r) * D)[col];
   }
   float mx = -INFINITY;
   for (int s = tid; s < ns; s += 256) mx = fmaxf(mx, a.ws_ml[((part0 + s) * a.rows + r) * 2]);
@@ -772,28 +773,28 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   float4 acc = make_float4(0, 0, 0, 0);
 #pragma unroll
   for (int k = 0; k < MPER; ++k) {
-    const int s = slice + k * NSL;
+    const int s = sl + k * NSL;
     const float w = (s < ns) ? weight(s) : 0.0f;
     acc.x += w * x[k].x;
     acc.y += w * x[k].y;
     acc.z += w * x[k].z;
     acc.w += w * x[k].w;
   }
-  for (int s = slice + MPER * NSL; s < ns; s += NSL) {  // long contexts with many chunks
+  for (int s = sl + MPER * NSL; s < ns; s += NSL) {  // long contexts with many chunks
     const float w = weight(s);
-    const float4 y = reinterpret_cast<const float4 *>(a.ws_o + ((part0 + s) * a.rows + r) * D)[c4];
+    const float4 y = reinterpret_cast<const float4 *>(a.ws_o + ((part0 + s) * a.rows + r) * D)[col];
     acc.x += w * y.x;
     acc.y += w * y.y;
     acc.z += w * y.z;
     acc.w += w * y.w;
   }
-  acc_s[slice][c4] = acc;
+  acc_s[sl][c4] = acc;
   __syncthreads();
-  if (tid < C4) {
+  if (tid < CS) {
     float4 v = acc_s[0][tid];
 #pragma unroll
-    for (int sl = 1; sl < NSL; ++sl) {
-      const float4 y = acc_s[sl][tid];
+    for (int k = 1; k < NSL; ++k) {
+      const float4 y = acc_s[k][tid];
       v.x += y.x;
       v.y += y.y;
       v.z += y.z;
@@ -817,7 +818,7 @@ hipError_t split_one(const AttnArgs &a, hipStream_t s) {
 
 template <int D>
 hipError_t merge_one(const AttnArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(a.num_seqs * a.T * a.num_q_heads), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(a.num_seqs * a.T * a.num_q_heads * (D / 64)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

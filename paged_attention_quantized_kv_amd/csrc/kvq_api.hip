@@ -51,6 +51,8 @@ int attn_shape(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_
   if (T > 8 || num_seqs > 1024 || num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
   const int32_t group = num_q_heads / num_kv_heads;
   if (static_cast<long>(T) * group > 32) return KVQ_ERR_UNSUPPORTED;
+  // the merge launches one workgroup per 64-dim slice of every output row
+  if (static_cast<long>(num_seqs) * T * num_q_heads * (head_dim / 64) > 0x7FFFFFFFL) return KVQ_ERR_UNSUPPORTED;
   if (max_seq_len < T) return KVQ_ERR_INVALID_ARG;
   s->group = group;
   s->rows = T * group;

@@ -515,7 +515,8 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 
   // one page: pr holds it; the next page's K half is already in flight in nx, and its
   // V half is issued once the page maxima are exchanged
-  auto step = [&](PageRegs<D, FMT> &pr, PageRegs<D, FMT> &nx, int pg_next, int it) {
+  auto step = [&](PageRegs<D, FMT> &pr, PageRegs<D, FMT> &nx, int pg_next, int it, auto more_tag) {
+    constexpr bool MORE = decltype(more_tag)::value;  // a next page exists: load its V half here
     const int p = page0 + it * NTEAM + team;
     const bool valid = p < page1;                              // uniform per team
     const bool full = (p * kPage + kPage - 1) <= (L - a.T);   // every real row sees every key of the page
@@ -538,7 +539,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) reinterpret_cast<float *>(&lds_mx[team][buf][16 * nt + c16])[wave] = mloc[nt];
     }
-    load_v_part<D, FMT>(nx, a, pg_next, wave, lane, q4);
+    if constexpr (MORE) load_v_part<D, FMT>(nx, a, pg_next, wave, lane, q4);
 
     // ---- phase 2: softmax weights against the team's reference maxima m (one per row,
     // identical in the 4 waves).  m moves only when a page maximum passes it by more than
@@ -620,17 +621,24 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     }
   };
 
-  if (n_it > 0) {
-    for (int it = 0;; it += 2) {
-      const int pgB = page_of(min(it + 1, n_it - 1));
-      load_k_part<D, FMT>(rB, a, pgB, wave, lane, q4);
-      step(rA, rB, pgB, it);
-      if (it + 1 >= n_it) break;
-      const int pgA = page_of(min(it + 2, n_it - 1));
-      load_k_part<D, FMT>(rA, a, pgA, wave, lane, q4);
-      step(rB, rA, pgA, it + 1);
-      if (it + 2 >= n_it) break;
-    }
+  // pages in pairs while a next page exists for both; the last page (or two) peeled off
+  // so that no load is issued past the team's pages
+  int it = 0;
+  for (; it + 2 < n_it; it += 2) {
+    const int pgB = page_of(it + 1);
+    load_k_part<D, FMT>(rB, a, pgB, wave, lane, q4);
+    step(rA, rB, pgB, it, std::true_type{});
+    const int pgA = page_of(it + 2);
+    load_k_part<D, FMT>(rA, a, pgA, wave, lane, q4);
+    step(rB, rA, pgA, it + 1, std::true_type{});
+  }
+  if (it + 1 < n_it) {
+    const int pgB = page_of(it + 1);
+    load_k_part<D, FMT>(rB, a, pgB, wave, lane, q4);
+    step(rA, rB, pgB, it, std::true_type{});
+    step(rB, rA, 0, it + 1, std::false_type{});
+  } else if (it < n_it) {
+    step(rA, rB, 0, it, std::false_type{});
   }
 
   // ---- per-wave row sums, then the team's and the workgroup's totals

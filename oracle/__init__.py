@@ -18,6 +18,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvq_oracle.so")
 SRC_PATH = os.path.join(_HERE, "kvq_oracle.c")
+# the pin suite's mutation check loads deliberately broken builds of the oracle through
+# this variable (tests/test_oracle_mutations.py); unset, the oracle is the one above
+_LIB_OVERRIDE = os.environ.get("KVQ_ORACLE_LIB")
 
 FMT_INT8_G64 = 0
 FMT_FP8_ROW = 1
@@ -46,8 +49,11 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        build()
-        L = C.CDLL(LIB_PATH)
+        if _LIB_OVERRIDE:
+            L = C.CDLL(_LIB_OVERRIDE)
+        else:
+            build()
+            L = C.CDLL(LIB_PATH)
         vp, i64, i32 = C.c_void_p, C.c_int64, C.c_int
         for name in ("orc_f32_to_f16_n", "orc_f16_to_f32_n", "orc_bf16_to_f32_n",
                      "orc_f32_to_e4m3fn_n", "orc_e4m3fn_to_f32_n"):

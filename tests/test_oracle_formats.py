@@ -138,16 +138,21 @@ def test_int8_g64_round_trip_bound_and_absmax_code():
 
 
 def test_int8_g64_zero_and_subnormal_groups():
-    x = np.zeros((2, 128), np.float32)
+    x = np.zeros((3, 128), np.float32)
     x[1, 64:] = np.float32(3e-5)  # a/127 is below fp16's normal range
     x[1, 64] = np.float32(4e-5)
+    x[2] = -x[1]
     codes, scales = O.quant_rows(O.FMT_INT8_G64, x)
     assert scales[0].tolist() == [0, 0] and not codes[0].any()
     assert scales[1, 0] == 0 and not codes[1, :64].any()
     s = O.f16_bits_to_f32(scales[1, 1:2])[0]
     assert 0 < s < 2.0 ** -14  # subnormal fp16 scale
-    assert np.all(np.abs(codes[1, 64:].astype(int)) <= 127)
-    assert abs(int(codes[1, 64])) == 127  # clamp reached through the coarse subnormal scale
+    # 4e-5 / s = 134.2 with the subnormal scale 5 * 2^-24: the code clamps to +-127 (the
+    # range is symmetric, -128 never appears)
+    assert abs(4e-5 / s - 134.2) < 0.1
+    assert int(codes[1, 64]) == 127 and int(codes[2, 64]) == -127
+    assert np.all(np.abs(codes[1:, 64:].astype(int)) <= 127)
+    assert np.array_equal(codes[2].astype(int), -codes[1].astype(int)) and np.array_equal(scales[2], scales[1])
 
 
 # ------------------------------------------------------------------ FP8 row
@@ -189,6 +194,31 @@ def _golden_table():
             if line:
                 rows[line[0]] = [float(v) for v in line[1:]]
     return rows
+
+
+def test_page_layout_matches_the_worked_examples():
+    """tests/golden/page_layout.txt: offsets worked by hand from the layout in include/kvq.h."""
+    path = os.path.join(os.path.dirname(__file__), "golden", "page_layout.txt")
+    n = 0
+    for line in open(path):
+        if not line.strip() or line.startswith("#"):
+            continue
+        kind, D, sl, dg, off = line.split()
+        D, sl, dg, off = int(D), int(sl), int(dg), int(off)
+        if kind == "k":
+            got = O.k_byte(sl, dg, D)
+        elif kind == "v":
+            got = O.v_byte(sl, dg, D)
+        elif kind == "ks_int8":
+            got = O.scale_elem(O.FMT_INT8_G64, 0, sl, dg, D)
+        elif kind == "vs_int8":
+            got = O.scale_elem(O.FMT_INT8_G64, 1, sl, dg, D)
+        else:
+            got = O.scale_elem(O.FMT_FP8_ROW, 0, sl, 0, D)
+            assert O.scale_elem(O.FMT_FP8_ROW, 1, sl, 0, D) == got
+        assert got == off, line
+        n += 1
+    assert n >= 40
 
 
 def test_bytes_per_token_match_the_pages_table():

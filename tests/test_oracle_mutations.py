@@ -1,0 +1,73 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a copy of oracle/kvq_oracle.c (a wrong constant, a
+dropped term, a wrong sign, index or operand order), builds it with gcc, and runs the
+oracle pin suite against it: the suite must fail.  The unmodified copy must pass.
+CPU only; the oracle itself is never modified.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "kvq_oracle.c")
+PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_attention.py"]
+
+# (name, original text, planted mistake)
+MUTATIONS = [
+    ("int8_divisor_128", "float s32 = a / 127.0f;", "float s32 = a / 128.0f;"),
+    ("int8_clamp_128", "if (r < -127.0f) r = -127.0f;", "if (r < -128.0f) r = -128.0f;"),
+    ("int8_truncates", "float r = rintf(xg[i] / s);", "float r = truncf(xg[i] / s);"),
+    ("int8_unrounded_scale", "float s = orc_f16_to_f32(h);", "float s = s32;"),
+    ("fp8_divisor_240", "float s = a / 448.0f;", "float s = a / 240.0f;"),
+    ("f16_ties_away", "if (rest > 0x1000u || (rest == 0x1000u && (h & 1u))) h += 1u;",
+     "if (rest >= 0x1000u) h += 1u;"),
+    ("f16_exponent_bias", "v = ldexp((double)(1024 + m), e - 25);", "v = ldexp((double)(1024 + m), e - 24);"),
+    ("bf16_fraction_bits", "v = ldexp((double)(128 + m), e - 134);", "v = ldexp((double)(128 + m), e - 135);"),
+    ("e4m3_exponent_bias", "v = ldexp((double)(8 + m), e - 10);", "v = ldexp((double)(8 + m), e - 11);"),
+    ("e4m3_ties_odd", "pick = (up % 2 == 0) ? up : dn;", "pick = (up % 2 == 1) ? up : dn;"),
+    ("k_layout_transposed", "* 256 + (s % 16) * 16 + (d % 16);", "* 256 + (d % 16) * 16 + (s % 16);"),
+    ("v_layout_swapped", "(d % 16) * 16 + (s / 16) * 4 + (s % 4);", "(d % 16) * 16 + (s % 4) * 4 + (s / 16);"),
+    ("k_scale_index", "if (which == 0) return (((int64_t)r * 4 + j) * (D / 64) + g) * 4 + i;",
+     "if (which == 0) return (((int64_t)j * 4 + r) * (D / 64) + g) * 4 + i;"),
+    ("gqa_interleaved", "int kvh = h / G;", "int kvh = h % Hkv;"),
+    ("causal_bound_dropped", "int last = seq_lens[b] - T + t;", "int last = seq_lens[b] - 1;"),
+    ("softmax_scale_dropped", "z[j] = (double)softmax_scale * acc;", "z[j] = acc;"),
+    ("no_max_shift", "double w = exp(z[j] - m);\n      l += w;\n      for (int d = 0; d < D; ++d) o[d]",
+     "double w = exp(z[j]);\n      l += w;\n      for (int d = 0; d < D; ++d) o[d]"),
+    ("dense_unnormalized", "for (int d = 0; d < D; ++d) o[d] /= l;", "for (int d = 0; d < D; ++d) o[d] /= 1.0;"),
+    ("paged_v_read_as_k", "row[d] += w * orc_dequant(p, 1, block, kvh, j % 64, d);",
+     "row[d] += w * orc_dequant(p, 0, block, kvh, j % 64, d);"),
+    ("append_slot_index", "int slot = (int)(pos % 64);", "int slot = (int)((pos + 1) % 64);"),
+]
+
+
+def _build(tmp_path, text, name):
+    src = tmp_path / f"{name}.c"
+    src.write_text(text)
+    so = tmp_path / f"lib_{name}.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+                    "-I", os.path.join(ROOT, "oracle"), "-o", str(so), str(src), "-lm"], check=True)
+    return so
+
+
+def _pins_pass(so):
+    env = dict(os.environ, KVQ_ORACLE_LIB=str(so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", "-m", "not gpu"] + PINS,
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return r.returncode == 0, r.stdout[-2000:]
+
+
+def test_unmodified_copy_passes(tmp_path):
+    ok, out = _pins_pass(_build(tmp_path, open(SRC).read(), "clean"))
+    assert ok, out
+
+
+@pytest.mark.parametrize("name,orig,bad", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmp_path, name, orig, bad):
+    text = open(SRC).read()
+    assert text.count(orig) == 1, f"mutation site of {name} not found exactly once"
+    ok, out = _pins_pass(_build(tmp_path, text.replace(orig, bad), name))
+    assert not ok, f"the pins did not catch {name}"

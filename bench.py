@@ -107,6 +107,13 @@ class Run:
         self.start = torch.from_numpy(w.seq_lens - s.T).to(device)
         self.sl = torch.from_numpy(w.seq_lens).to(device)
         self.out = torch.empty(self.q.shape, dtype=torch.float32, device=device)
+        if s.chunk and s.B == 1:
+            # the last prefill chunk (s.chunk rows before the T decode rows), for the append measurement
+            L = int(w.seq_lens[0])
+            c0 = L - s.T - s.chunk
+            self.chunk_k = H.src_tensor(w.rows("k", 0, c0, c0 + s.chunk), s.src, device)
+            self.chunk_v = H.src_tensor(w.rows("v", 0, c0, c0 + s.chunk), s.src, device)
+            self.chunk_start = torch.tensor([c0], dtype=torch.int32, device=device)
         self.ws = K.alloc_workspace(cache, s.B, s.T, s.Hq, w.max_seq_len, device=device)
         self.n_splits, self.tps = K.num_splits(s.B, s.T, s.Hq, s.Hkv, s.D, w.max_seq_len)
         torch.cuda.synchronize()
@@ -225,6 +232,30 @@ class Run:
         two_ms = self._events(self.g_all_two, reps, self.n_copies)
         return gpu_ms / steps, split_ms, two_ms
 
+    def measure_chunk_append(self, reps=20):
+        """kv_append_quant of the last prefill chunk (rewriting the same rows with the same
+        values), events around a graph of one append per pool copy.  Returns (ms per call,
+        bytes read + written by definition)."""
+        if not hasattr(self, "chunk_k"):
+            return None, None
+        K, torch = self.K, self.torch
+
+        def app(i):
+            K.kv_append_quant(self.caches[i % self.n_copies], self.chunk_k, self.chunk_v, self.bt, self.chunk_start)
+
+        for i in range(self.n_copies):
+            app(i)
+        torch.cuda.synchronize()
+        g = self._graph(app, range(self.n_copies))
+        g.replay()
+        torch.cuda.synchronize()
+        ms = self._events(g, reps, self.n_copies)[1]
+        s = self.w.shape
+        rows = self.chunk_k.shape[1] * s.Hkv
+        src = 2 * rows * s.D * self.chunk_k.element_size()
+        dst = 2 * rows * (s.D + (2 * s.D // 64 if s.fmt == 0 else 4))
+        return ms, src + dst
+
     def algorithmic_split_bytes(self):
         """Bytes the split kernel must move by definition: every visible key and value
         (codes + scales), the block-table entries and the queries."""
@@ -307,6 +338,7 @@ def main():
         w = run.w
         s = w.shape
         split_avg = sum(split_ms) / len(split_ms)
+        chunk_ms, chunk_bytes = (None, None) if args.eager else run.measure_chunk_append()
         alg = run.algorithmic_split_bytes()
         results[name] = {
             "ms_per_step": ms,
@@ -323,6 +355,8 @@ def main():
             "tokens_per_split": run.tps,
             "two_call_ms": (sum(two_ms) / len(two_ms)) if two_ms else None,
             "wall_ms": getattr(run, "wall_ms", None),
+            "chunk_ms": chunk_ms,
+            "chunk_bytes": chunk_bytes,
         }
         print(f"[bench] {name}: {ms * 1e3:.1f} us/step, split {split_avg * 1e3:.1f} us "
               f"({results[name]['split_gbs']:.0f} GB/s), {run.n_copies} pool copies", file=sys.stderr, flush=True)
@@ -363,7 +397,10 @@ def main():
                        "split_us": round(r["split_ms_avg"] * 1e3, 2), "split_gbs": round(r["split_gbs"], 1),
                        "us_per_step_two_calls": round(r["two_call_ms"] * 1e3, 2) if r["two_call_ms"] else None,
                        "us_per_step_host_wall": round(r["wall_ms"] * 1e3, 2) if r["wall_ms"] else None,
-                       "n_splits": r["n_splits"], "pool_copies": r["n_copies"]} for n, r in results.items()},
+                       "n_splits": r["n_splits"], "pool_copies": r["n_copies"],
+                       **({"append_chunk_rows": 4096, "append_chunk_us": round(r["chunk_ms"] * 1e3, 2),
+                           "append_chunk_gbs": round(r["chunk_bytes"] / (r["chunk_ms"] * 1e-3) / 1e9, 1)}
+                          if r["chunk_ms"] else {})} for n, r in results.items()},
         "host": {"cpu": model, "nproc": ncpu},
     }
     if not args.no_cpu_baseline:

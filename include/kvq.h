@@ -192,6 +192,21 @@ int paged_decode_step(const kvq_cache_t *cache, const void *k_new, const void *v
                       int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t max_seq_len, float softmax_scale,
                       float *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * kvq_check_tables -- debug checker of the device-resident tables that the calls above
+ * take as preconditions (the pages require no particular checker; this one exists
+ * because block ids and lengths live on the device, where the host cannot read them
+ * without a synchronization).  Counts, on `stream`:
+ *   result[0]  sequences whose length is outside [T, max_seq_len];
+ *   result[1]  block-table entries, among the pages each sequence's length uses
+ *              (length clamped to [0, max_seq_len]), outside [0, cache->num_blocks).
+ *   result     [2] int32, device memory, overwritten (no initialization needed).
+ * Costs one small launch; meant for debugging and tests, not for the decode loop.
+ */
+int kvq_check_tables(const kvq_cache_t *cache, int32_t num_seqs, int32_t T, const int32_t *block_table,
+                     int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t max_seq_len, int32_t *result,
+                     void *stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *kvq_status_string(int status);
 

@@ -23,7 +23,7 @@ PAGE = 64
 
 _EXPORTS = ("kv_append_quant", "paged_decode_attn", "paged_decode_attn_split", "paged_decode_attn_merge",
             "paged_decode_step", "paged_decode_attn_workspace_bytes", "paged_decode_attn_num_splits",
-            "kvq_status_string")
+            "kvq_check_tables", "kvq_status_string")
 
 
 class KvqError(RuntimeError):
@@ -58,6 +58,8 @@ def _load():
     L.paged_decode_attn_workspace_bytes.restype = C.c_size_t
     L.paged_decode_attn_num_splits.argtypes = [i32] * 6 + [C.POINTER(i32)]
     L.paged_decode_attn_num_splits.restype = i32
+    L.kvq_check_tables.argtypes = [P, i32, i32, vp, i32, vp, i32, vp, vp]
+    L.kvq_check_tables.restype = C.c_int
     L.kvq_status_string.argtypes = [C.c_int]
     L.kvq_status_string.restype = C.c_char_p
     return L
@@ -222,3 +224,15 @@ def paged_decode_step(cache, k_new, v_new, q, block_table, seq_lens, max_seq_len
                                  float(softmax_scale), _ptr(out), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+def check_tables(cache, T, block_table, seq_lens, max_seq_len, stream=None):
+    """Debug check of the device tables: returns a device int32 tensor [bad lengths,
+    bad block ids among the used pages] (read it after the stream is synchronized)."""
+    B = seq_lens.shape[0]
+    _check_table(block_table, B, "block_table", 2)
+    _check_table(seq_lens, B, "seq_lens", 1)
+    result = torch.empty(2, dtype=torch.int32, device=seq_lens.device)
+    _check(lib.kvq_check_tables(cache.desc, B, int(T), _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+                                int(max_seq_len), _ptr(result), _stream(stream)))
+    return result

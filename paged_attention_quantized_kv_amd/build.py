@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kvq_api.hip", "append.hip", "attn.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kvq_api.hip", "append.hip", "attn.hip", "check.hip")]
 HEADERS = [os.path.join(HERE, "csrc", "internal.h"), os.path.join(ROOT, "include", "kvq.h")]
 
 HIPCC_FLAGS = [

@@ -46,6 +46,15 @@ struct AttnArgs {
   float qk_scale_log2;  // softmax_scale * log2(e)
 };
 
+// Launch arguments of kvq_check_tables, validated on the host.
+struct CheckArgs {
+  const int32_t *block_table;
+  const int32_t *seq_lens;
+  int32_t *result;
+  int32_t num_seqs, T, max_blocks, max_seq_len, num_blocks;
+};
+
+hipError_t launch_check_tables(const CheckArgs &a, hipStream_t s);
 hipError_t launch_append(int format, int head_dim, int src_dtype, const AppendArgs &a, hipStream_t s);
 hipError_t launch_attn_split(int format, int head_dim, int q_dtype, const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_merge(int head_dim, const AttnArgs &a, hipStream_t s);

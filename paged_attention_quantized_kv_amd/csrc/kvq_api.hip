@@ -218,4 +218,26 @@ int paged_decode_step(const kvq_cache_t *cache, const void *k_new, const void *v
                    max_seq_len, softmax_scale, out, workspace, workspace_bytes, stream, k_new, v_new);
 }
 
+int kvq_check_tables(const kvq_cache_t *cache, int32_t num_seqs, int32_t T, const int32_t *block_table,
+                     int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t max_seq_len, int32_t *result,
+                     void *stream) {
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  if (num_seqs < 1 || T < 1 || max_blocks_per_seq < 1 || max_seq_len < 1) return KVQ_ERR_INVALID_ARG;
+  if (!block_table || !aligned4(block_table) || !seq_lens || !aligned4(seq_lens) || !result || !aligned4(result))
+    return KVQ_ERR_INVALID_ARG;
+  if (static_cast<long>(max_seq_len) > static_cast<long>(max_blocks_per_seq) * kvq::kPage) return KVQ_ERR_CAPACITY;
+  kvq::CheckArgs a;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.result = result;
+  a.num_seqs = num_seqs;
+  a.T = T;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_seq_len = max_seq_len;
+  a.num_blocks = cache->num_blocks;
+  if (kvq::launch_check_tables(a, static_cast<hipStream_t>(stream)) != hipSuccess) return KVQ_ERR_LAUNCH;
+  return KVQ_OK;
+}
+
 }  // extern "C"

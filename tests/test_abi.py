@@ -105,3 +105,19 @@ def test_workspace_and_chunking_are_pure_functions_of_the_shape(K):
     for L in (32768, 131072, 262144):
         n, _ = K.num_splits(1, 1, 24, 4, 256, L)
         assert n * 4 == 256
+
+
+def test_check_tables_validation(K):
+    d = _desc(K)
+
+    def chk(d=d, B=1, T=4, bt=0x7000, mb=4, sl=0x8000, L=256, res=0x9000):
+        return K.lib.kvq_check_tables(C.byref(d), B, T, C.c_void_p(bt), mb, C.c_void_p(sl), L, C.c_void_p(res), None)
+
+    assert chk(B=0) == -1
+    assert chk(T=0) == -1
+    assert chk(bt=0) == -1
+    assert chk(sl=0x8002) == -1
+    assert chk(res=0) == -1
+    assert chk(L=257) == -4
+    assert chk(d=_desc(K, D=192)) == -2
+    assert chk() == -5  # valid: reaches the runtime, which has no device here

@@ -268,3 +268,24 @@ def test_fused_step_late_rows_straddling_pages(K, fmt):
     assert (L0 - shp.T) // 64 == 16 * 20 + 15 and (L0 - 1) // 64 == 16 * 21
     w = S.make(shp, seed=S.seed_of("tiny") + 300 + fmt)
     _fused_check(K, w, rows=_sample_rows(w, 6))
+
+
+def test_check_tables_counts_bad_lengths_and_block_ids(K):
+    w = S.make(SMALL["ragged_b3_t4"], seed=S.seed_of("tiny") + 400)
+    s = w.shape
+    cache = H.new_cache(K, w, DEV)
+    bt = torch.from_numpy(w.block_table).to(DEV)
+    sl = torch.from_numpy(w.seq_lens).to(DEV)
+    res = K.check_tables(cache, s.T, bt, sl, w.max_seq_len)
+    torch.cuda.synchronize()
+    assert res.tolist() == [0, 0]
+    bad_bt = w.block_table.copy()
+    bad_bt[2, 0] = -1                      # used page of sequence 2
+    bad_bt[2, 1] = w.num_blocks            # used page of sequence 2
+    bad_bt[0, bad_bt.shape[1] - 1] = -7    # beyond sequence 0's 4 keys: unused, not counted
+    bad_sl = w.seq_lens.copy()
+    bad_sl[1] = s.T - 1                    # fewer keys than query rows
+    res = K.check_tables(cache, s.T, torch.from_numpy(bad_bt).to(DEV), torch.from_numpy(bad_sl).to(DEV),
+                         w.max_seq_len)
+    torch.cuda.synchronize()
+    assert res.tolist() == [1, 2]

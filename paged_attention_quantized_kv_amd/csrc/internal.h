@@ -19,6 +19,7 @@ constexpr int kTeams = KVQ_TEAMS;           // 4-wave teams per attention workgr
 constexpr int kTargetWgs = 512 / KVQ_TEAMS; // 8 waves per compute unit of the 256-CU chip
 constexpr int kMaxChunkPages = 256;   // pages of one attention chunk (block ids staged in LDS)
 constexpr int kMergeMaxSplits = 1024; // chunk weights the merge keeps in LDS
+constexpr int kBulkAppendRows = 64;   // appends of at least this many rows per sequence go page by page
 
 // Launch arguments of kv_append_quant, validated on the host.
 struct AppendArgs {

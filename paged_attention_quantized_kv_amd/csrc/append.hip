@@ -30,18 +30,19 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   quant_row<FMT, D, SRC>(a, b, t, h, which, pos, blk, lane);
 }
 
-// Bulk appends (prefill chunks): one workgroup of 256 threads per (page, KV head, K|V,
-// sequence).  Thread (slot s, quarter q) quantizes dims q*D/4 .. q*D/4 + D/4 - 1 of the
-// row at slot s with the same arithmetic as quant_row (so the codes are identical).  K
-// codes leave as 16-byte tile rows (one slot each); V codes are staged in LDS and leave
-// as 16-byte runs of the dim-major layout, or byte by byte on a page the chunk covers
-// only in part.  Slots outside [start_pos, start_pos + n_new) are never written.
+// Bulk appends (prefill chunks): one workgroup per (page, KV head, K|V, sequence), one
+// thread per (slot, 16 dims): 64 * D/16 threads.  Each thread quantizes its 16 values
+// with the same arithmetic as quant_row (so the codes are identical), the group or row
+// maximum coming from the neighbouring threads of the slot.  K codes leave as 16-byte
+// tile rows (one slot each); V codes are staged in LDS and leave as 16-byte runs of the
+// dim-major layout, or byte by byte on a page the chunk covers only in part.  Slots
+// outside [start_pos, start_pos + n_new) are never written.
 template <int FMT, int D, int SRC>
-__global__ __launch_bounds__(256) void append_page_kernel(AppendArgs a) {
-  constexpr int DT = D / 4;                      // dims per thread
+__global__ __launch_bounds__(kPage * D / 16) void append_page_kernel(AppendArgs a) {
+  constexpr int NC = D / 16;  // threads per slot
   constexpr int G64 = D / 64;
   __shared__ __align__(16) uint8_t vstage[kPage * D];  // V codes, row-major [slot][dim]
-  const int tid = threadIdx.x, sl = tid >> 2, q = tid & 3;
+  const int tid = threadIdx.x, sl = tid / NC, c16 = tid % NC;
   const int h = blockIdx.y, which = blockIdx.z & 1, b = blockIdx.z >> 1;
   const long pos0 = a.start_pos[b];
   if (pos0 < 0) return;
@@ -58,100 +59,101 @@ __global__ __launch_bounds__(256) void append_page_kernel(AppendArgs a) {
   uint8_t *codes = (which ? a.v_codes : a.k_codes) + page * kPage * D;
   const int run = (sl % 16) / 4, spos = (sl / 16) * 4 + sl % 4;
 
-  // ---- this thread's DT source values (zeros for slots outside the chunk)
-  float x[DT];
+  // ---- this thread's 16 source values (zeros for slots outside the chunk)
+  float x[16];
   if (mine) {
     const void *src = which ? a.v_new : a.k_new;
     const long row = pg * kPage + sl - pos0;
-    const size_t base = ((static_cast<size_t>(b) * a.n_new + row) * a.num_kv_heads + h) * D + q * DT;
+    const size_t base = ((static_cast<size_t>(b) * a.n_new + row) * a.num_kv_heads + h) * D + 16 * c16;
+    if constexpr (SRC == 1) {  // bf16: two 16-byte loads, exact widening
+      const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(src) + base);
 #pragma unroll
-    for (int e = 0; e < DT; ++e) x[e] = load_src<SRC>(src, base + e);
+      for (int k = 0; k < 2; ++k) {
+        const uint4 u = p[k];
+        const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[8 * k + 2 * j] = __uint_as_float(wv[j] << 16);
+          x[8 * k + 2 * j + 1] = __uint_as_float(wv[j] & 0xFFFF0000u);
+        }
+      }
+    } else {  // fp32: four 16-byte loads
+      const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(src) + base);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 f = p[k];
+        x[4 * k] = f.x;
+        x[4 * k + 1] = f.y;
+        x[4 * k + 2] = f.z;
+        x[4 * k + 3] = f.w;
+      }
+    }
   } else {
 #pragma unroll
-    for (int e = 0; e < DT; ++e) x[e] = 0.0f;
+    for (int e = 0; e < 16; ++e) x[e] = 0.0f;
   }
-  uint32_t c[DT];
-  if constexpr (FMT == 0) {  // INT8, one fp16 scale per 64 dims
-    float amax = 0.0f;
+  uint32_t c[16];
+  float amax = 0.0f;
 #pragma unroll
-    for (int e = 0; e < DT; ++e) amax = fmaxf(amax, fabsf(x[e]));
-    if constexpr (DT < 64) amax = fmaxf(amax, __shfl_xor(amax, 1));  // D = 128: two threads per group
+  for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  if constexpr (FMT == 0) {  // INT8, one fp16 scale per 64 dims: 4 neighbouring threads
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
     const _Float16 s16 = static_cast<_Float16>(amax / 127.0f);
     const float sc = static_cast<float>(s16);
 #pragma unroll
-    for (int e = 0; e < DT; ++e) {
+    for (int e = 0; e < 16; ++e) {
       float r = 0.0f;
       if (sc != 0.0f) r = fminf(fmaxf(rintf(x[e] / sc), -127.0f), 127.0f);
       c[e] = static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu;
     }
-    if (mine && (DT >= 64 || (q & 1) == 0)) {
-      const int g = (q * DT) / 64;
+    if (mine && (c16 & 3) == 0) {
+      const int g = c16 / 4;
       _Float16 *scales = static_cast<_Float16 *>(which ? a.v_scales : a.k_scales) + page * D;
       scales[which ? (run * G64 + g) * 16 + spos : ((run * 4 + sl / 16) * G64 + g) * 4 + sl % 4] = s16;
     }
-  } else {  // FP8 E4M3FN, one fp32 scale per row
-    float amax = 0.0f;
+  } else {  // FP8 E4M3FN, one fp32 scale per row: the NC threads of the slot
 #pragma unroll
-    for (int e = 0; e < DT; ++e) amax = fmaxf(amax, fabsf(x[e]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    for (int off = 1; off < NC; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     const float sc = amax / 448.0f;
 #pragma unroll
-    for (int e = 0; e < DT; ++e) c[e] = (sc != 0.0f) ? e4m3fn_rne_sat(x[e] / sc) : 0u;
-    if (mine && q == 0) static_cast<float *>(which ? a.v_scales : a.k_scales)[page * kPage + run * 16 + spos] = sc;
+    for (int e = 0; e < 16; ++e) c[e] = (sc != 0.0f) ? e4m3fn_rne_sat(x[e] / sc) : 0u;
+    if (mine && c16 == 0) static_cast<float *>(which ? a.v_scales : a.k_scales)[page * kPage + run * 16 + spos] = sc;
   }
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = c[4 * k] | (c[4 * k + 1] << 8) | (c[4 * k + 2] << 16) | (c[4 * k + 3] << 24);
 
-  if (which == 0) {
-    // K: 16x16-byte tiles; each 16 dims of this slot are one 16-byte tile row
+  if (which == 0) {  // K: the 16 dims of this slot are one 16-byte tile row
     if (mine) {
-#pragma unroll
-      for (int t16 = 0; t16 < DT / 16; ++t16) {
-        const int d0 = q * DT + 16 * t16;
-        uint32_t w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          w[k] = c[16 * t16 + 4 * k] | (c[16 * t16 + 4 * k + 1] << 8) | (c[16 * t16 + 4 * k + 2] << 16) |
-                 (c[16 * t16 + 4 * k + 3] << 24);
-        const size_t off = (static_cast<size_t>(sl / 16) * (D / 16) + d0 / 16) * 256 + (sl % 16) * 16;
-        *reinterpret_cast<uint4 *>(codes + off) = make_uint4(w[0], w[1], w[2], w[3]);
-      }
+      const size_t off = (static_cast<size_t>(sl / 16) * NC + c16) * 256 + (sl % 16) * 16;
+      *reinterpret_cast<uint4 *>(codes + off) = make_uint4(w[0], w[1], w[2], w[3]);
     }
     return;
   }
-  // V: stage the page's codes row-major, then write the dim-major runs
-#pragma unroll
-  for (int t16 = 0; t16 < DT / 16; ++t16) {
-    uint32_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      w[k] = c[16 * t16 + 4 * k] | (c[16 * t16 + 4 * k + 1] << 8) | (c[16 * t16 + 4 * k + 2] << 16) |
-             (c[16 * t16 + 4 * k + 3] << 24);
-    *reinterpret_cast<uint4 *>(vstage + sl * D + q * DT + 16 * t16) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
+  // V: stage the page's codes row-major, then write the dim-major runs: run k (one per
+  // thread) is dim d = (k/64)*16 + k%16, run r = (k/16)%4, whose byte 4j+i holds slot 16j+4r+i
+  *reinterpret_cast<uint4 *>(vstage + sl * D + 16 * c16) = make_uint4(w[0], w[1], w[2], w[3]);
   __syncthreads();
-  // 16-byte run k (k = 0 .. 64*D/16-1): dim d = (k/64)*16 + k%16, run r = (k/16)%4; byte 4j+i
-  // holds slot 16j + 4r + i
-  for (int k = tid; k < kPage * D / 16; k += 256) {
-    const int d = (k / 64) * 16 + (k % 16), r = (k / 16) % 4;
-    if (full) {
-      uint32_t w[4];
+  const int k = tid, d = (k / 64) * 16 + (k % 16), r = (k / 16) % 4;
+  if (full) {
+    uint32_t v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s0 = 16 * j + 4 * r;
-        w[j] = static_cast<uint32_t>(vstage[s0 * D + d]) | (static_cast<uint32_t>(vstage[(s0 + 1) * D + d]) << 8) |
-               (static_cast<uint32_t>(vstage[(s0 + 2) * D + d]) << 16) |
-               (static_cast<uint32_t>(vstage[(s0 + 3) * D + d]) << 24);
-      }
-      *reinterpret_cast<uint4 *>(codes + static_cast<size_t>(k) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int sj = 16 * j + 4 * r + i;
-          if (sj >= s_lo && sj < s_hi) codes[static_cast<size_t>(k) * 16 + 4 * j + i] = vstage[sj * D + d];
-        }
+    for (int j = 0; j < 4; ++j) {
+      const int s0 = 16 * j + 4 * r;
+      v[j] = static_cast<uint32_t>(vstage[s0 * D + d]) | (static_cast<uint32_t>(vstage[(s0 + 1) * D + d]) << 8) |
+             (static_cast<uint32_t>(vstage[(s0 + 2) * D + d]) << 16) |
+             (static_cast<uint32_t>(vstage[(s0 + 3) * D + d]) << 24);
     }
+    *reinterpret_cast<uint4 *>(codes + static_cast<size_t>(k) * 16) = make_uint4(v[0], v[1], v[2], v[3]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int sj = 16 * j + 4 * r + i;
+        if (sj >= s_lo && sj < s_hi) codes[static_cast<size_t>(k) * 16 + 4 * j + i] = vstage[sj * D + d];
+      }
   }
 }
 
@@ -161,7 +163,7 @@ hipError_t launch_one(const AppendArgs &a, hipStream_t s) {
     // pages a chunk of n_new rows can touch, whatever its start
     const long pages = (a.n_new + kPage - 1) / kPage + 1;
     hipLaunchKernelGGL((append_page_kernel<FMT, D, SRC>), dim3(static_cast<unsigned>(pages), a.num_kv_heads,
-                                                               2 * a.num_seqs), dim3(256), 0, s, a);
+                                                               2 * a.num_seqs), dim3(kPage * D / 16), 0, s, a);
     return hipGetLastError();
   }
   const long nrows = 2L * a.num_seqs * a.n_new * a.num_kv_heads;

@@ -43,7 +43,8 @@
  *
  * Supported shapes: block_size 64; head_dim 128 or 256; 1 <= T <= 8;
  * num_q_heads a multiple of num_kv_heads with T * (num_q_heads/num_kv_heads)
- * <= 32; 1 <= num_seqs <= 1024.  Anything else returns KVQ_ERR_UNSUPPORTED.
+ * <= 32; 1 <= num_seqs <= 1024 (paged_prefill_attn takes any T, see there).
+ * Anything else returns KVQ_ERR_UNSUPPORTED.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -191,6 +192,31 @@ int paged_decode_step(const kvq_cache_t *cache, const void *k_new, const void *v
                       int32_t num_seqs, int32_t T, int32_t num_q_heads, const int32_t *block_table,
                       int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t max_seq_len, float softmax_scale,
                       float *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * paged_prefill_attn -- the same attention for a prefill chunk: T query rows per sequence
+ * with any T (1 <= T <= max_seq_len; T * (num_q_heads / num_kv_heads) rows per KV head),
+ * causal among themselves exactly as in paged_decode_attn (row t sees keys 0 ..
+ * seq_lens[b] - T + t).  The chunk's own K/V rows are appended first with
+ * kv_append_quant.  This is the step that follows a prefill chunk's append in an
+ * engine that prefills in chunks (NInfer-4090 README, "What this fork changes" and
+ * "Known limits": chunked prefill attention over the same cache).
+ * Arguments as for paged_decode_attn; the workspace is
+ * paged_prefill_attn_workspace_bytes() bytes (never 0 for a supported shape).  Rows are
+ * handled in blocks of 32 (query row r = t * G + g of a KV head); each (sequence, KV
+ * head, row block) streams its context once.  When one chunk per row block fills the
+ * chip, the rows are written directly and no merge runs.
+ * Supported: head_dim 128 or 256; num_seqs <= 1024; 32-row blocks * num_kv_heads <= 65535.
+ * A row's keys are read chunk by chunk up to its last visible key; a block id out of
+ * range among the pages of a row's chunks (or a bad seq_lens value) makes the row NaN.
+ */
+size_t paged_prefill_attn_workspace_bytes(int32_t num_seqs, int32_t T, int32_t num_q_heads,
+                                          int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len);
+int paged_prefill_attn(const kvq_cache_t *cache, const void *q, int32_t q_dtype, int32_t num_seqs,
+                       int32_t T, int32_t num_q_heads, const int32_t *block_table,
+                       int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t max_seq_len,
+                       float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                       void *stream);
 
 /*
  * kvq_check_tables -- debug checker of the device-resident tables that the calls above

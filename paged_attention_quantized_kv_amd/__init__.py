@@ -23,7 +23,7 @@ PAGE = 64
 
 _EXPORTS = ("kv_append_quant", "paged_decode_attn", "paged_decode_attn_split", "paged_decode_attn_merge",
             "paged_decode_step", "paged_decode_attn_workspace_bytes", "paged_decode_attn_num_splits",
-            "kvq_check_tables", "kvq_status_string")
+            "paged_prefill_attn", "paged_prefill_attn_workspace_bytes", "kvq_check_tables", "kvq_status_string")
 
 
 class KvqError(RuntimeError):
@@ -48,7 +48,7 @@ def _load():
     L.kv_append_quant.argtypes = [P, vp, vp, i32, i32, i32, vp, i32, vp, vp]
     L.kv_append_quant.restype = C.c_int
     attn = [P, vp, i32, i32, i32, i32, vp, i32, vp, i32, C.c_float, vp, vp, C.c_size_t, vp]
-    for name in ("paged_decode_attn", "paged_decode_attn_split", "paged_decode_attn_merge"):
+    for name in ("paged_decode_attn", "paged_decode_attn_split", "paged_decode_attn_merge", "paged_prefill_attn"):
         getattr(L, name).argtypes = attn
         getattr(L, name).restype = C.c_int
     L.paged_decode_step.argtypes = [P, vp, vp, vp, i32, i32, i32, i32, vp, i32, vp, i32, C.c_float, vp, vp,
@@ -56,6 +56,8 @@ def _load():
     L.paged_decode_step.restype = C.c_int
     L.paged_decode_attn_workspace_bytes.argtypes = [i32] * 6
     L.paged_decode_attn_workspace_bytes.restype = C.c_size_t
+    L.paged_prefill_attn_workspace_bytes.argtypes = [i32] * 6
+    L.paged_prefill_attn_workspace_bytes.restype = C.c_size_t
     L.paged_decode_attn_num_splits.argtypes = [i32] * 6 + [C.POINTER(i32)]
     L.paged_decode_attn_num_splits.restype = i32
     L.kvq_check_tables.argtypes = [P, i32, i32, vp, i32, vp, i32, vp, vp]
@@ -169,6 +171,18 @@ def alloc_workspace(cache: Cache, num_seqs: int, T: int, num_q_heads: int, max_s
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def prefill_workspace_bytes(num_seqs: int, T: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                            max_seq_len: int) -> int:
+    return int(lib.paged_prefill_attn_workspace_bytes(num_seqs, T, num_q_heads, num_kv_heads, head_dim, max_seq_len))
+
+
+def alloc_prefill_workspace(cache: Cache, num_seqs: int, T: int, num_q_heads: int, max_seq_len: int, device="cuda"):
+    n = prefill_workspace_bytes(num_seqs, T, num_q_heads, cache.num_kv_heads, cache.head_dim, max_seq_len)
+    if n == 0:
+        raise KvqError(-2, "unsupported shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
 def _check_attn(cache, q, block_table, seq_lens, out, workspace):
     if q.dim() != 4 or q.shape[3] != cache.head_dim:
         raise ValueError(f"q must be [B, T, Hq, {cache.head_dim}]")
@@ -204,6 +218,13 @@ def paged_decode_attn_split(cache, q, block_table, seq_lens, max_seq_len, softma
 def paged_decode_attn_merge(cache, q, block_table, seq_lens, max_seq_len, softmax_scale, out, workspace, stream=None):
     return _attn(lib.paged_decode_attn_merge, cache, q, block_table, seq_lens, max_seq_len, softmax_scale, out,
                  workspace, stream)
+
+
+def paged_prefill_attn(cache, q, block_table, seq_lens, max_seq_len, softmax_scale, out, workspace, stream=None):
+    """Attention of a prefill chunk: q [B, T, Hq, D] with any T, the chunk's rows already
+    appended at seq_lens - T .. seq_lens - 1; row t sees keys 0 .. seq_lens - T + t."""
+    return _attn(lib.paged_prefill_attn, cache, q, block_table, seq_lens, max_seq_len, softmax_scale, out, workspace,
+                 stream)
 
 
 def paged_decode_step(cache, k_new, v_new, q, block_table, seq_lens, max_seq_len, softmax_scale, out, workspace,

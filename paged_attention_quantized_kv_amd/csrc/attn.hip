@@ -213,7 +213,10 @@ struct Smem {
 };
 
 // APP: 1 = also quantize and append the T new rows of each sequence (the fused
-// decode step; the source dtype is the query dtype), 0 = the cache is complete.
+// decode step; the source dtype is the query dtype), 0 = the cache is complete,
+// 2 = prefill: the query rows come in blocks of 16*NT rows (grid y = row block * Hkv
+// + KV head), chunks hold up to kMaxPrefillChunkPages pages, and with one chunk per
+// row block the normalized rows go straight to out.
 template <int D, int NT, int FMT, int QLO, int NTEAM, int APP>
 __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) {
   constexpr int G64 = D / 64, NCH = D / 16, DPW = D / 64;
@@ -226,19 +229,36 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   __shared__ int32_t lds_over[2][4 * NTEAM];  // per wave: a page maximum passed the reference by > kLazy
   __shared__ float lds_l[NTEAM][4][ROWS];
   __shared__ float lds_m[NTEAM][ROWS];
-  __shared__ int32_t lds_pg[kMaxChunkPages];  // pool page (block * Hkv + kvh) of each page of the chunk
+  constexpr int MAXPG = (APP == 2) ? kMaxPrefillChunkPages : kMaxChunkPages;
+  __shared__ int32_t lds_pg[MAXPG];  // pool page (block * Hkv + kvh) of each page of the chunk
   float *pbuf = reinterpret_cast<float *>(pbuf4);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = (tid >> 6) & 3, team = tid >> 8;
   const int q4 = lane >> 4, c16 = lane & 15;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, kvh = blockIdx.y % a.num_kv_heads, b = blockIdx.z;
+  const int row0 = (blockIdx.y / a.num_kv_heads) * ROWS;  // first query row (t*G + g) of this block
   const int L = a.seq_lens[b];
-  if (L < a.T || L > a.max_seq_len || L > a.max_blocks * kPage) return;  // merge writes NaN
+  if (L < a.T || L > a.max_seq_len || L > a.max_blocks * kPage) {  // the merge writes NaN rows
+    if constexpr (APP == 2) {
+      if (a.direct_out != 0 && split == 0) {  // no merge: write them here
+        for (int e = threadIdx.x; e < ROWS * D; e += blockDim.x) {
+          const int r = row0 + e / D;
+          if (r < a.rows)
+            a.out[((static_cast<size_t>(b) * a.T + r / a.group) * a.num_q_heads + kvh * a.group + r % a.group) * D +
+                  e % D] = NAN;
+        }
+      }
+    }
+    return;
+  }
+  const int R = a.rows;  // query rows of the KV head; this block holds rows row0 .. row0 + ROWS - 1
+  // keys this block's rows can see: row r = t*G + g sees positions 0 .. L - T + t
+  const int lim = (APP == 2) ? L - a.T + (min(row0 + ROWS, R) - 1) / a.group + 1 : L;
+  const int lo_last = L - a.T + row0 / a.group;  // the last key the block's first row sees
   const int tok0 = split * a.tokens_per_split;
-  if (tok0 >= L) return;  // chunk past the end of this sequence: the merge skips it
-  const int tok1 = min(tok0 + a.tokens_per_split, L);
+  if (tok0 >= lim) return;  // chunk past every key of these rows: the merge skips it
+  const int tok1 = min(tok0 + a.tokens_per_split, lim);
   const int page0 = tok0 / kPage, page1 = (tok1 + kPage - 1) / kPage;
-  const int R = a.rows;
 
   // ---- the chunk's block ids -> pool pages in LDS (an invalid id reads block 0 and flags the chunk)
   bool bad = false;
@@ -268,7 +288,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   [[maybe_unused]] int blk_r[RPW];
   int t_lo = 0, n_rows = 0;
   bool defer = false;
-  if constexpr (APP != 0) {
+  if constexpr (APP == 1) {
     aa.k_new = a.k_new;
     aa.v_new = a.v_new;
     aa.k_codes = const_cast<uint8_t *>(a.k_codes);
@@ -300,14 +320,14 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   }
   // the first pages load while the queries are staged (and, for the fused step, the new
   // rows read) -- unless one of them holds new rows, which must be written first
-  const bool early = (APP == 0) || (page0 + NTEAM - 1 < (L - a.T) / kPage);
+  const bool early = (APP != 1) || (page0 + NTEAM - 1 < (L - a.T) / kPage);
   if (early && n_it > 0) load_page<D, FMT>(rA, a, page_of(0), wave, lane, q4);
 
   // ---- queries -> LDS in B-operand order: entry (nt, cg, hk, hl, lane) holds dims
   // 64cg + 16(lane/16) + 8hk + 0..7 of row 16nt + lane%16, as f16 hi (hl=0) or lo (hl=1).
   for (int e = tid; e < NT * G64 * 2 * 64; e += 256 * NTEAM) {
     const int ln = e & 63, hk = (e >> 6) & 1, cg = (e >> 7) % G64, nt = (e >> 7) / G64;
-    const int r = 16 * nt + (ln & 15);
+    const int r = row0 + 16 * nt + (ln & 15);
     const int d0 = 64 * cg + 16 * (ln >> 4) + 8 * hk;
     f16x2 hi[4], lo[4];
     if (r < R) {
@@ -333,7 +353,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     if constexpr (QLO)
       qs[idx + 64] = __builtin_bit_cast(uint4, f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]});
   }
-  if constexpr (APP != 0) {
+  if constexpr (APP == 1) {
     if (!defer) {
       for (int r = (tid >> 6); r < n_rows; r += NW) {
         const int t = t_lo + (r >> 1);
@@ -357,7 +377,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   for (int nt = 0; nt < NT; ++nt) {
     m[nt] = -INFINITY;
     lsum[nt] = 0.0f;
-    const int r = 16 * nt + c16;
+    const int r = row0 + 16 * nt + c16;
     last[nt] = (r < R) ? (L - a.T + r / a.group) : -1;  // -1: padding row, sees nothing
 #pragma unroll
     for (int j = 0; j < DPW; ++j) o[nt][j] = f32x4{0, 0, 0, 0};
@@ -519,7 +539,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     constexpr bool MORE = decltype(more_tag)::value;  // a next page exists: load its V half here
     const int p = page0 + it * NTEAM + team;
     const bool valid = p < page1;                              // uniform per team
-    const bool full = (p * kPage + kPage - 1) <= (L - a.T);   // every real row sees every key of the page
+    const bool full = (p * kPage + kPage - 1) <= lo_last;      // every real row sees every key of the page
     const int buf = it & 1;
     float z[NT][4];
     float mloc[NT];
@@ -601,7 +621,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) lsum[nt] += psum[nt];
 
-    if constexpr (APP != 0) {
+    if constexpr (APP == 1) {
       if (defer && it == 0) {  // the deferred rows of the fused step (see above)
 #pragma unroll
         for (int k = 0; k < RPW; ++k) {
@@ -616,7 +636,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     } else if (valid) {
       accumulate(std::true_type{}, pr, p, pb);
     }
-    if constexpr (APP != 0) {
+    if constexpr (APP == 1) {
       if (defer && it == 0 && (tid >> 6) < n_rows) __builtin_amdgcn_s_waitcnt(0);
     }
   };
@@ -691,20 +711,29 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     const size_t part = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits + split;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int r = 16 * nt + c16;
+      const int rl = 16 * nt + c16, r = row0 + rl;
       if (r < R) {
+        // prefill with one chunk: the normalized row goes to out[b][t][h] (t*G + g = r)
+        const bool direct = (APP == 2) && (a.direct_out != 0);
+        const size_t orow = ((static_cast<size_t>(b) * a.T + r / a.group) * a.num_q_heads + kvh * a.group +
+                             r % a.group) * D;
 #pragma unroll
         for (int j = 0; j < DPW; ++j) {
           f32x4 v = o[nt][j] * fown[nt];
           const int d = 16 * (wave * DPW + j) + 4 * q4;
 #pragma unroll
           for (int t = 1; t < NTEAM; ++t) {
-            const float4 x = *reinterpret_cast<const float4 *>(fin + ((t - 1) * ROWS + r) * (D + 4) + d);
+            const float4 x = *reinterpret_cast<const float4 *>(fin + ((t - 1) * ROWS + rl) * (D + 4) + d);
             v += f32x4{x.x, x.y, x.z, x.w};
           }
-          *reinterpret_cast<float4 *>(a.ws_o + (part * R + r) * D + d) = make_float4(v[0], v[1], v[2], v[3]);
+          if (direct) {
+            const float l = Lrow[nt];
+            *reinterpret_cast<float4 *>(a.out + orow + d) = make_float4(v[0] / l, v[1] / l, v[2] / l, v[3] / l);
+          } else {
+            *reinterpret_cast<float4 *>(a.ws_o + (part * R + r) * D + d) = make_float4(v[0], v[1], v[2], v[3]);
+          }
         }
-        if (wave == 0 && q4 == 0) {
+        if (!direct && wave == 0 && q4 == 0) {
           a.ws_ml[(part * R + r) * 2 + 0] = Mrow[nt];
           a.ws_ml[(part * R + r) * 2 + 1] = Lrow[nt];
         }
@@ -752,7 +781,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     return;
   }
   const int kvh = h / a.group, r = t * a.group + h % a.group;
-  const int ns = (L + a.tokens_per_split - 1) / a.tokens_per_split;
+  // chunks holding keys this row sees (later chunks were skipped or hold none of them)
+  const int ns = (L - a.T + t + a.tokens_per_split) / a.tokens_per_split;
   const size_t part0 = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits;
   const int c4 = tid % CS, sl = tid / CS, col = qs * CS + c4;
 
@@ -824,6 +854,14 @@ hipError_t split_one(const AttnArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, int FMT, int QDT>
+hipError_t prefill_one(const AttnArgs &a, hipStream_t s) {
+  constexpr int QLO = QDT == 0 ? 1 : 0;
+  const dim3 grid(a.n_splits, a.num_kv_heads * a.row_blocks, a.num_seqs);
+  hipLaunchKernelGGL((attn_split_kernel<D, 2, FMT, QLO, kTeams, 2>), grid, dim3(256 * kTeams), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t merge_one(const AttnArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(a.num_seqs * a.T * a.num_q_heads * (D / 64)), dim3(256), 0, s, a);
@@ -844,6 +882,15 @@ hipError_t launch_attn_split(int format, int head_dim, int q_dtype, const AttnAr
   KVQ_SPLIT_DQ(256, 2)
 #undef KVQ_SPLIT_DQ
 #undef KVQ_SPLIT_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_prefill(int format, int head_dim, int q_dtype, const AttnArgs &a, hipStream_t s) {
+#define KVQ_PF_CASE(DD, F, Q) \
+  if (head_dim == DD && format == F && q_dtype == Q) return prefill_one<DD, F, Q>(a, s);
+  KVQ_PF_CASE(128, 0, 0) KVQ_PF_CASE(128, 0, 1) KVQ_PF_CASE(128, 1, 0) KVQ_PF_CASE(128, 1, 1)
+  KVQ_PF_CASE(256, 0, 0) KVQ_PF_CASE(256, 0, 1) KVQ_PF_CASE(256, 1, 0) KVQ_PF_CASE(256, 1, 1)
+#undef KVQ_PF_CASE
   return hipErrorInvalidValue;
 }
 

@@ -17,7 +17,8 @@ namespace kvq {
 constexpr int kPage = 64;                   // token slots per page
 constexpr int kTeams = KVQ_TEAMS;           // 4-wave teams per attention workgroup
 constexpr int kTargetWgs = 512 / KVQ_TEAMS; // 8 waves per compute unit of the 256-CU chip
-constexpr int kMaxChunkPages = 256;   // pages of one attention chunk (block ids staged in LDS)
+constexpr int kMaxChunkPages = 256;   // pages of one decode attention chunk (block ids staged in LDS)
+constexpr int kMaxPrefillChunkPages = 4096;  // the same for prefill (262,144 tokens per chunk)
 constexpr int kMergeMaxSplits = 1024; // chunk weights the merge keeps in LDS
 constexpr int kBulkAppendRows = 64;   // appends of at least this many rows per sequence go page by page
 
@@ -44,6 +45,8 @@ struct AttnArgs {
   const void *k_new, *v_new;  // fused decode step: [B][T][Hkv][D] rows to append first (else null)
   int32_t num_seqs, num_blocks, num_kv_heads, num_q_heads, group, T, rows;
   int32_t max_blocks, max_seq_len, tokens_per_split, n_splits;
+  int32_t row_blocks;   // blocks of 16*NT query rows per KV head (grid y = row_blocks * num_kv_heads)
+  int32_t direct_out;   // one chunk per row block: write normalized rows to out, no merge
   float qk_scale_log2;  // softmax_scale * log2(e)
 };
 
@@ -59,5 +62,6 @@ hipError_t launch_check_tables(const CheckArgs &a, hipStream_t s);
 hipError_t launch_append(int format, int head_dim, int src_dtype, const AppendArgs &a, hipStream_t s);
 hipError_t launch_attn_split(int format, int head_dim, int q_dtype, const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_merge(int head_dim, const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_prefill(int format, int head_dim, int q_dtype, const AttnArgs &a, hipStream_t s);
 
 }  // namespace kvq

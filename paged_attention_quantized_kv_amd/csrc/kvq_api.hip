@@ -64,6 +64,49 @@ int attn_shape(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_
   return KVQ_OK;
 }
 
+// Prefill: any number of query rows T*G per KV head, in blocks of 32 rows (two 16-row
+// tiles); the context of each (sequence, KV head, row block) is cut into as few chunks
+// as give about one workgroup per compute unit (at most kMaxPrefillChunkPages pages
+// each).  With one chunk the split kernel writes the rows itself (no merge, no partials).
+struct PrefillShape {
+  int32_t group, rows, row_blocks, tokens_per_split, n_splits;
+  bool direct;
+  size_t ml_bytes, o_bytes;
+};
+
+int prefill_shape(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t max_seq_len, PrefillShape *s) {
+  if (num_seqs < 1 || T < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_seq_len < 1) return KVQ_ERR_INVALID_ARG;
+  if (head_dim != 128 && head_dim != 256) return KVQ_ERR_UNSUPPORTED;
+  if (num_q_heads % num_kv_heads != 0) return KVQ_ERR_UNSUPPORTED;
+  if (num_seqs > 1024 || num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (max_seq_len < T) return KVQ_ERR_INVALID_ARG;
+  const int32_t group = num_q_heads / num_kv_heads;
+  const long rows = static_cast<long>(T) * group;
+  const long row_blocks = (rows + 31) / 32;
+  if (rows > 0x7FFFFFFFL || row_blocks * num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (static_cast<long>(num_seqs) * T * num_q_heads * (head_dim / 64) > 0x7FFFFFFFL) return KVQ_ERR_UNSUPPORTED;
+  const long pages = (static_cast<long>(max_seq_len) + kvq::kPage - 1) / kvq::kPage;
+  const long units = static_cast<long>(num_seqs) * num_kv_heads * row_blocks;
+  long n = (kvq::kTargetWgs + units - 1) / units;
+  const long nmin = (pages + kvq::kMaxPrefillChunkPages - 1) / kvq::kMaxPrefillChunkPages;
+  if (n < nmin) n = nmin;
+  long pps = (pages + n - 1) / n;
+  pps = ((pps + kvq::kTeams - 1) / kvq::kTeams) * kvq::kTeams;
+  if (pps > kvq::kMaxPrefillChunkPages) pps = kvq::kMaxPrefillChunkPages;
+  s->group = group;
+  s->rows = static_cast<int32_t>(rows);
+  s->row_blocks = static_cast<int32_t>(row_blocks);
+  s->tokens_per_split = static_cast<int32_t>(pps * kvq::kPage);
+  s->n_splits = static_cast<int32_t>((pages + pps - 1) / pps);
+  s->direct = (s->n_splits == 1);
+  const size_t parts = s->direct ? 0 : static_cast<size_t>(num_seqs) * num_kv_heads * s->n_splits * s->rows;
+  s->ml_bytes = ((parts * 2 * sizeof(float)) + 255) & ~static_cast<size_t>(255);
+  if (s->ml_bytes == 0) s->ml_bytes = 256;
+  s->o_bytes = parts * head_dim * sizeof(float);
+  return KVQ_OK;
+}
+
 enum class Phase { kBoth, kSplit, kMerge };
 
 int attn_call(Phase phase, const kvq_cache_t *cache, const void *q, int32_t q_dtype, int32_t num_seqs, int32_t T,
@@ -109,6 +152,8 @@ int attn_call(Phase phase, const kvq_cache_t *cache, const void *q, int32_t q_dt
   a.max_seq_len = max_seq_len;
   a.tokens_per_split = s.tokens_per_split;
   a.n_splits = s.n_splits;
+  a.row_blocks = 1;
+  a.direct_out = 0;
   a.qk_scale_log2 = softmax_scale * 1.4426950408889634f;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -216,6 +261,64 @@ int paged_decode_step(const kvq_cache_t *cache, const void *k_new, const void *v
   if (!k_new || !v_new) return KVQ_ERR_INVALID_ARG;
   return attn_call(Phase::kBoth, cache, q, dtype, num_seqs, T, num_q_heads, block_table, max_blocks_per_seq, seq_lens,
                    max_seq_len, softmax_scale, out, workspace, workspace_bytes, stream, k_new, v_new);
+}
+
+size_t paged_prefill_attn_workspace_bytes(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t max_seq_len) {
+  PrefillShape s;
+  if (prefill_shape(num_seqs, T, num_q_heads, num_kv_heads, head_dim, max_seq_len, &s) != KVQ_OK) return 0;
+  return s.ml_bytes + s.o_bytes;
+}
+
+int paged_prefill_attn(const kvq_cache_t *cache, const void *q, int32_t q_dtype, int32_t num_seqs, int32_t T,
+                       int32_t num_q_heads, const int32_t *block_table, int32_t max_blocks_per_seq,
+                       const int32_t *seq_lens, int32_t max_seq_len, float softmax_scale, float *out, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARG;
+  if (!q || !aligned16(q) || !out || !aligned16(out) || !workspace || !aligned16(workspace)) return KVQ_ERR_INVALID_ARG;
+  if (!block_table || !aligned4(block_table) || !seq_lens || !aligned4(seq_lens)) return KVQ_ERR_INVALID_ARG;
+  if (max_blocks_per_seq < 1) return KVQ_ERR_INVALID_ARG;
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVQ_ERR_INVALID_ARG;
+  PrefillShape s;
+  rc = prefill_shape(num_seqs, T, num_q_heads, cache->num_kv_heads, cache->head_dim, max_seq_len, &s);
+  if (rc) return rc;
+  if (static_cast<long>(max_seq_len) > static_cast<long>(max_blocks_per_seq) * kvq::kPage) return KVQ_ERR_CAPACITY;
+  if (workspace_bytes < s.ml_bytes + s.o_bytes) return KVQ_ERR_WORKSPACE;
+
+  kvq::AttnArgs a;
+  a.k_codes = static_cast<const uint8_t *>(cache->k_codes);
+  a.v_codes = static_cast<const uint8_t *>(cache->v_codes);
+  a.k_scales = cache->k_scales;
+  a.v_scales = cache->v_scales;
+  a.q = q;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.ws_ml = static_cast<float *>(workspace);
+  a.ws_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + s.ml_bytes);
+  a.out = out;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
+  a.num_seqs = num_seqs;
+  a.num_blocks = cache->num_blocks;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.group = s.group;
+  a.T = T;
+  a.rows = s.rows;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_seq_len = max_seq_len;
+  a.tokens_per_split = s.tokens_per_split;
+  a.n_splits = s.n_splits;
+  a.row_blocks = s.row_blocks;
+  a.direct_out = s.direct ? 1 : 0;
+  a.qk_scale_log2 = softmax_scale * 1.4426950408889634f;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (kvq::launch_attn_prefill(cache->format, cache->head_dim, q_dtype, a, st) != hipSuccess) return KVQ_ERR_LAUNCH;
+  if (!s.direct && kvq::launch_attn_merge(cache->head_dim, a, st) != hipSuccess) return KVQ_ERR_LAUNCH;
+  return KVQ_OK;
 }
 
 int kvq_check_tables(const kvq_cache_t *cache, int32_t num_seqs, int32_t T, const int32_t *block_table,

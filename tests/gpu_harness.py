@@ -91,11 +91,16 @@ def pool_equal(cache, pool) -> dict:
     return res
 
 
-def run_attn(K, w: S.Workload, cache, bt, device, q=None, stream=None):
+def run_attn(K, w: S.Workload, cache, bt, device, q=None, stream=None, prefill=False):
+    """paged_decode_attn (or paged_prefill_attn) of the workload's queries."""
     s = w.shape
     q = src_tensor(w.q, s.src, device) if q is None else q
     sl = torch.from_numpy(w.seq_lens).to(device)
     out = torch.empty(q.shape, dtype=torch.float32, device=device)
-    ws = K.alloc_workspace(cache, s.B, s.T, s.Hq, w.max_seq_len, device=device)
-    K.paged_decode_attn(cache, q, bt, sl, w.max_seq_len, w.softmax_scale, out, ws, stream=stream)
+    if prefill:
+        ws = K.alloc_prefill_workspace(cache, s.B, s.T, s.Hq, w.max_seq_len, device=device)
+        K.paged_prefill_attn(cache, q, bt, sl, w.max_seq_len, w.softmax_scale, out, ws, stream=stream)
+    else:
+        ws = K.alloc_workspace(cache, s.B, s.T, s.Hq, w.max_seq_len, device=device)
+        K.paged_decode_attn(cache, q, bt, sl, w.max_seq_len, w.softmax_scale, out, ws, stream=stream)
     return out

@@ -121,3 +121,40 @@ def test_check_tables_validation(K):
     assert chk(L=257) == -4
     assert chk(d=_desc(K, D=192)) == -2
     assert chk() == -5  # valid: reaches the runtime, which has no device here
+
+
+def test_prefill_validation(K):
+    d = _desc(K)
+    fn = "paged_prefill_attn"
+    assert _attn(K, d, qdt=5, fn=fn) == -1
+    assert _attn(K, d, q=0x5001, fn=fn) == -1
+    assert _attn(K, d, out=0, fn=fn) == -1
+    assert _attn(K, d, ws=0, fn=fn) == -1
+    assert _attn(K, d, sl=0x8001, fn=fn) == -1
+    assert _attn(K, d, scale=float("inf"), fn=fn) == -1
+    assert _attn(K, d, Hq=25, fn=fn) == -2
+    assert _attn(K, d, B=0, fn=fn) == -1
+    assert _attn(K, d, T=0, fn=fn) == -1
+    assert _attn(K, d, L=99, T=100, fn=fn) == -1  # fewer keys than query rows
+    assert _attn(K, d, L=257, mb=4, fn=fn) == -4
+    assert _attn(K, d, wsb=16, T=100, Hq=8, L=256, fn=fn) == -3
+    assert _attn(K, _desc(K, D=64), fn=fn) == -2
+    assert _attn(K, d, B=1025, fn=fn) == -2
+    # 32-row blocks x KV heads beyond the grid's y limit
+    assert _attn(K, d, T=100000, Hq=24, L=100000, mb=1563, fn=fn) == -2
+    # any T, and T x group beyond the decode limit: valid, reaches the runtime (no device here)
+    assert _attn(K, d, T=9, fn=fn) == -5
+    assert _attn(K, d, T=4096, Hq=24, L=4096, mb=64, fn=fn) == -5
+    assert _attn(K, d, T=8, Hq=32, fn=fn) == -5
+
+
+def test_prefill_workspace(K):
+    # 4096-row chunk at 262,144 tokens: 768 row blocks x 4 KV heads fill the chip with one
+    # chunk each, written directly (the workspace is the minimum 256 bytes)
+    assert K.prefill_workspace_bytes(1, 4096, 24, 4, 256, 262144) == 256
+    # 100 rows x group 4 = 400 rows (13 blocks) x 2 KV heads: chunks of 2 pages over 5 pages
+    parts = 1 * 2 * 3 * 400
+    ml = (parts * 2 * 4 + 255) // 256 * 256
+    assert K.prefill_workspace_bytes(1, 100, 8, 2, 128, 300) == ml + parts * 128 * 4
+    assert K.prefill_workspace_bytes(1, 100, 8, 2, 128, 99) == 0  # fewer keys than rows
+    assert K.prefill_workspace_bytes(1, 4, 24, 4, 192, 4096) == 0

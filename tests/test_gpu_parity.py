@@ -33,12 +33,13 @@ def K():
     return K
 
 
-def check(K, w, rows=None, chunk=8192):
+def check(K, w, rows=None, chunk=8192, prefill=False):
     s = w.shape
-    say(f"[parity] {s.name} B={s.B} T={s.T} Hq={s.Hq} Hkv={s.Hkv} D={s.D} lens={s.lens[:8]} fmt={s.fmt} src={s.src}")
+    say(f"[parity] {s.name} B={s.B} T={s.T} Hq={s.Hq} Hkv={s.Hkv} D={s.D} lens={s.lens[:8]} fmt={s.fmt} src={s.src}"
+        f" prefill={prefill}")
     cache = H.new_cache(K, w, DEV)
     bt = H.fill_gpu(K, w, cache, DEV, chunk=chunk)
-    out = H.run_attn(K, w, cache, bt, DEV)
+    out = H.run_attn(K, w, cache, bt, DEV, prefill=prefill)
     torch.cuda.synchronize()
     pool = H.oracle_pool(O, w)
     mism = H.pool_equal(cache, pool)

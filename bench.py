@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
 HEADLINE = "mtp128k"
 DEPTHS = ["qwen32k", "mtp128k", "full256k_int8", "full256k_fp8"]
 SETTLE_S = 0.2  # seconds of untimed back-to-back steps before the warmup steps
@@ -256,6 +257,37 @@ class Run:
         dst = 2 * rows * (s.D + (2 * s.D // 64 if s.fmt == 0 else 4))
         return ms, src + dst
 
+    def measure_prefill_chunk(self, reps=2):
+        """paged_prefill_attn of the last prefill chunk where it sits in the context: its
+        rows (seeded queries, N(0,1) in the source dtype) see every earlier key and the
+        chunk's own rows up to themselves.  Events around a graph of one call per pool copy.
+        Returns (ms per call, flops by definition: 4 * D per visible (row, key) pair)."""
+        if not hasattr(self, "chunk_k"):
+            return None, None
+        K, torch, S = self.K, self.torch, self.S
+        s = self.w.shape
+        n = s.chunk
+        Lc = int(self.chunk_start.item()) + n
+        g = torch.Generator().manual_seed(S.seed_of(self.name) + 77)
+        q = torch.randn((1, n, s.Hq, s.D), generator=g, dtype=torch.float32)
+        q = q.to(self.dev).to(torch.bfloat16 if s.src == S.SRC_BF16 else torch.float32)
+        sl = torch.tensor([Lc], dtype=torch.int32, device=self.dev)
+        out = torch.empty(q.shape, dtype=torch.float32, device=self.dev)
+        ws = K.alloc_prefill_workspace(self.caches[0], 1, n, s.Hq, Lc, device=self.dev)
+
+        def pf(i):
+            K.paged_prefill_attn(self.caches[i % self.n_copies], q, self.bt, sl, Lc, self.w.softmax_scale, out, ws)
+
+        for i in range(self.n_copies):
+            pf(i)
+        torch.cuda.synchronize()
+        gr = self._graph(pf, range(self.n_copies))
+        gr.replay()
+        torch.cuda.synchronize()
+        ms = self._events(gr, reps, self.n_copies)[1]
+        pairs = n * (Lc - n) + n * (n + 1) // 2
+        return ms, 4 * s.D * s.Hq * pairs
+
     def algorithmic_split_bytes(self):
         """Bytes the split kernel must move by definition: every visible key and value
         (codes + scales), the block-table entries and the queries."""
@@ -339,6 +371,7 @@ def main():
         s = w.shape
         split_avg = sum(split_ms) / len(split_ms)
         chunk_ms, chunk_bytes = (None, None) if args.eager else run.measure_chunk_append()
+        pf_ms, pf_flops = (None, None) if args.eager else run.measure_prefill_chunk()
         alg = run.algorithmic_split_bytes()
         results[name] = {
             "ms_per_step": ms,
@@ -357,6 +390,8 @@ def main():
             "wall_ms": getattr(run, "wall_ms", None),
             "chunk_ms": chunk_ms,
             "chunk_bytes": chunk_bytes,
+            "prefill_ms": pf_ms,
+            "prefill_flops": pf_flops,
         }
         print(f"[bench] {name}: {ms * 1e3:.1f} us/step, split {split_avg * 1e3:.1f} us "
               f"({results[name]['split_gbs']:.0f} GB/s), {run.n_copies} pool copies", file=sys.stderr, flush=True)
@@ -400,7 +435,12 @@ def main():
                        "n_splits": r["n_splits"], "pool_copies": r["n_copies"],
                        **({"append_chunk_rows": 4096, "append_chunk_us": round(r["chunk_ms"] * 1e3, 2),
                            "append_chunk_gbs": round(r["chunk_bytes"] / (r["chunk_ms"] * 1e-3) / 1e9, 1)}
-                          if r["chunk_ms"] else {})} for n, r in results.items()},
+                          if r["chunk_ms"] else {}),
+                       **({"prefill_chunk_us": round(r["prefill_ms"] * 1e3, 1),
+                           "prefill_chunk_tflops": round(r["prefill_flops"] / (r["prefill_ms"] * 1e-3) / 1e12, 1),
+                           "prefill_chunk_frac_f16_mfma": round(r["prefill_flops"] / (r["prefill_ms"] * 1e-3)
+                                                                / (MFMA_F16_PEAK_TFLOPS * 1e12), 4)}
+                          if r["prefill_ms"] else {})} for n, r in results.items()},
         "host": {"cpu": model, "nproc": ncpu},
     }
     if not args.no_cpu_baseline:

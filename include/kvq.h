@@ -203,10 +203,10 @@ int paged_decode_step(const kvq_cache_t *cache, const void *k_new, const void *v
  * "Known limits": chunked prefill attention over the same cache).
  * Arguments as for paged_decode_attn; the workspace is
  * paged_prefill_attn_workspace_bytes() bytes (never 0 for a supported shape).  Rows are
- * handled in blocks of 32 (query row r = t * G + g of a KV head); each (sequence, KV
+ * handled in blocks of 64 (query row r = t * G + g of a KV head); each (sequence, KV
  * head, row block) streams its context once.  When one chunk per row block fills the
  * chip, the rows are written directly and no merge runs.
- * Supported: head_dim 128 or 256; num_seqs <= 1024; 32-row blocks * num_kv_heads <= 65535.
+ * Supported: head_dim 128 or 256; num_seqs <= 1024; 64-row blocks * num_kv_heads <= 65535.
  * A row's keys are read chunk by chunk up to its last visible key; a block id out of
  * range among the pages of a row's chunks (or a bad seq_lens value) makes the row NaN.
  */

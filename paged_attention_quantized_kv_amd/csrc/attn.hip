@@ -395,7 +395,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     }
     // the query fragments of 64-dim group cg, read from LDS two groups ahead of their use
     // (bf16 queries; fp32 queries, with twice the fragments, read them at their use)
-    constexpr int QPF = QLO ? 1 : 2;  // groups of fragments in flight
+    constexpr int QPF = (QLO || NT > 2) ? 1 : 2;  // groups of fragments in flight
     f16x8 qf[QPF][2][NT][QP];
     auto read_q = [&](f16x8 (&dst)[2][NT][QP], int cg) {
 #pragma unroll
@@ -858,7 +858,8 @@ template <int D, int FMT, int QDT>
 hipError_t prefill_one(const AttnArgs &a, hipStream_t s) {
   constexpr int QLO = QDT == 0 ? 1 : 0;
   const dim3 grid(a.n_splits, a.num_kv_heads * a.row_blocks, a.num_seqs);
-  hipLaunchKernelGGL((attn_split_kernel<D, 2, FMT, QLO, kTeams, 2>), grid, dim3(256 * kTeams), 0, s, a);
+  hipLaunchKernelGGL((attn_split_kernel<D, kPrefillNT, FMT, QLO, kPrefillTeams, 2>), grid, dim3(256 * kPrefillTeams),
+                     0, s, a);
   return hipGetLastError();
 }
 

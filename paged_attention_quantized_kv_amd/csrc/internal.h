@@ -19,6 +19,15 @@ constexpr int kTeams = KVQ_TEAMS;           // 4-wave teams per attention workgr
 constexpr int kTargetWgs = 512 / KVQ_TEAMS; // 8 waves per compute unit of the 256-CU chip
 constexpr int kMaxChunkPages = 256;   // pages of one decode attention chunk (block ids staged in LDS)
 constexpr int kMaxPrefillChunkPages = 4096;  // the same for prefill (262,144 tokens per chunk)
+#ifndef KVQ_PREFILL_NT
+#define KVQ_PREFILL_NT 4
+#endif
+#ifndef KVQ_PREFILL_TEAMS
+#define KVQ_PREFILL_TEAMS KVQ_TEAMS
+#endif
+constexpr int kPrefillNT = KVQ_PREFILL_NT;        // 16-row tiles of a prefill row block
+constexpr int kPrefillTeams = KVQ_PREFILL_TEAMS;  // 4-wave teams of a prefill workgroup
+constexpr int kPrefillRows = 16 * kPrefillNT;   // query rows (t*G + g) of a prefill row block
 constexpr int kMergeMaxSplits = 1024; // chunk weights the merge keeps in LDS
 constexpr int kBulkAppendRows = 64;   // appends of at least this many rows per sequence go page by page
 

@@ -64,7 +64,7 @@ int attn_shape(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_
   return KVQ_OK;
 }
 
-// Prefill: any number of query rows T*G per KV head, in blocks of 32 rows (two 16-row
+// Prefill: any number of query rows T*G per KV head, in blocks of kPrefillRows (16-row
 // tiles); the context of each (sequence, KV head, row block) is cut into as few chunks
 // as give about one workgroup per compute unit (at most kMaxPrefillChunkPages pages
 // each).  With one chunk the split kernel writes the rows itself (no merge, no partials).
@@ -83,7 +83,7 @@ int prefill_shape(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_
   if (max_seq_len < T) return KVQ_ERR_INVALID_ARG;
   const int32_t group = num_q_heads / num_kv_heads;
   const long rows = static_cast<long>(T) * group;
-  const long row_blocks = (rows + 31) / 32;
+  const long row_blocks = (rows + kvq::kPrefillRows - 1) / kvq::kPrefillRows;
   if (rows > 0x7FFFFFFFL || row_blocks * num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
   if (static_cast<long>(num_seqs) * T * num_q_heads * (head_dim / 64) > 0x7FFFFFFFL) return KVQ_ERR_UNSUPPORTED;
   const long pages = (static_cast<long>(max_seq_len) + kvq::kPage - 1) / kvq::kPage;
@@ -92,7 +92,7 @@ int prefill_shape(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_
   const long nmin = (pages + kvq::kMaxPrefillChunkPages - 1) / kvq::kMaxPrefillChunkPages;
   if (n < nmin) n = nmin;
   long pps = (pages + n - 1) / n;
-  pps = ((pps + kvq::kTeams - 1) / kvq::kTeams) * kvq::kTeams;
+  pps = ((pps + kvq::kPrefillTeams - 1) / kvq::kPrefillTeams) * kvq::kPrefillTeams;
   if (pps > kvq::kMaxPrefillChunkPages) pps = kvq::kMaxPrefillChunkPages;
   s->group = group;
   s->rows = static_cast<int32_t>(rows);

@@ -140,8 +140,8 @@ def test_prefill_validation(K):
     assert _attn(K, d, wsb=16, T=100, Hq=8, L=256, fn=fn) == -3
     assert _attn(K, _desc(K, D=64), fn=fn) == -2
     assert _attn(K, d, B=1025, fn=fn) == -2
-    # 32-row blocks x KV heads beyond the grid's y limit
-    assert _attn(K, d, T=100000, Hq=24, L=100000, mb=1563, fn=fn) == -2
+    # 64-row blocks x KV heads beyond the grid's y limit
+    assert _attn(K, d, T=200000, Hq=24, L=200000, mb=3125, fn=fn) == -2
     # any T, and T x group beyond the decode limit: valid, reaches the runtime (no device here)
     assert _attn(K, d, T=9, fn=fn) == -5
     assert _attn(K, d, T=4096, Hq=24, L=4096, mb=64, fn=fn) == -5
@@ -149,10 +149,10 @@ def test_prefill_validation(K):
 
 
 def test_prefill_workspace(K):
-    # 4096-row chunk at 262,144 tokens: 768 row blocks x 4 KV heads fill the chip with one
+    # 4096-row chunk at 262,144 tokens: 384 row blocks x 4 KV heads fill the chip with one
     # chunk each, written directly (the workspace is the minimum 256 bytes)
     assert K.prefill_workspace_bytes(1, 4096, 24, 4, 256, 262144) == 256
-    # 100 rows x group 4 = 400 rows (13 blocks) x 2 KV heads: chunks of 2 pages over 5 pages
+    # 100 rows x group 4 = 400 rows (7 blocks) x 2 KV heads: chunks of 2 pages over 5 pages
     parts = 1 * 2 * 3 * 400
     ml = (parts * 2 * 4 + 255) // 256 * 256
     assert K.prefill_workspace_bytes(1, 100, 8, 2, 128, 300) == ml + parts * 128 * 4

@@ -60,7 +60,7 @@ def test_prefill_small(K, name):
 
 @pytest.mark.parametrize("fmt", [S.FMT_INT8_G64, S.FMT_FP8_ROW])
 def test_prefill_direct_rows(K, fmt):
-    """4096 query rows per KV head: 128 row blocks x 2 KV heads x 2 sequences fill the
+    """4096 query rows per KV head: 64 row blocks x 2 KV heads x 2 sequences fill the
     chip with one chunk each, so the split kernel writes the rows itself."""
     shp = S.tiny_shape(B=2, T=512, Hq=16, Hkv=2, D=128, lens=(700, 1500), src=S.SRC_BF16, fmt=fmt,
                        outliers=True, name="pf_direct")

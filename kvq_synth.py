@@ -15,6 +15,8 @@ tokens; shapes after NInfer-4090 README "What this fork changes", d256-h24-kv4):
               interleaved in one pool by a shuffled block table
   full256k    B=1 T=1 L=262144, INT8 (A) or row-scaled FP8 (B); the last
               4096 context rows form one prefill chunk
+  mtp128k_rk8v4  mtp128k's data in the rk8v4 format (rotated INT8 keys,
+              4-bit group-32 values)
 
 Every pool starts filled with poison (code bytes 0x7F, NaN scales), so a read of
 a slot that was never appended shows up as NaN in the output.  Block-table
@@ -31,11 +33,13 @@ import torch
 PAGE = 64
 FMT_INT8_G64 = 0
 FMT_FP8_ROW = 1
+FMT_RK8V4 = 2
 SRC_F32 = 0
 SRC_BF16 = 1
 
 CONFIG_NAMES = ["tiny", "qwen32k", "mtp128k", "c8", "full256k_int8", "full256k_fp8"]
-_SEED_INDEX = {"tiny": 0, "qwen32k": 1, "mtp128k": 2, "c8": 3, "full256k_int8": 4, "full256k_fp8": 4}
+_SEED_INDEX = {"tiny": 0, "qwen32k": 1, "mtp128k": 2, "c8": 3, "full256k_int8": 4, "full256k_fp8": 4,
+               "mtp128k_rk8v4": 2}
 
 
 @dataclasses.dataclass
@@ -66,6 +70,8 @@ def shape(name: str, **over) -> Shape:
         s = Shape(name, 8, 4, 24, 4, 256, lens, SRC_BF16, FMT_INT8_G64, True)
     elif name == "full256k_int8":
         s = Shape(name, 1, 1, 24, 4, 256, [262144], SRC_BF16, FMT_INT8_G64, True, chunk=4096)
+    elif name == "mtp128k_rk8v4":
+        s = Shape(name, 1, 4, 24, 4, 256, [131072], SRC_BF16, FMT_RK8V4, True)
     elif name == "full256k_fp8":
         s = Shape(name, 1, 1, 24, 4, 256, [262144], SRC_BF16, FMT_FP8_ROW, True, chunk=4096)
     else:
@@ -117,7 +123,10 @@ class Workload:
     def kv_bytes(self) -> int:
         """Algorithmic KV bytes one decode call reads: every visible key and value, codes + scales."""
         s = self.shape
-        per_tok_head = 2 * (s.D + (2 * (s.D // 64) if s.fmt == FMT_INT8_G64 else 4))
+        if s.fmt == FMT_RK8V4:  # INT8 keys with fp16 group-64 scales, 4-bit values with fp16 group-32 scales
+            per_tok_head = (s.D + 2 * (s.D // 64)) + (s.D // 2 + 2 * (s.D // 32))
+        else:
+            per_tok_head = 2 * (s.D + (2 * (s.D // 64) if s.fmt == FMT_INT8_G64 else 4))
         return int(self.seq_lens.sum()) * s.Hkv * per_tok_head
 
 

@@ -24,6 +24,7 @@ _LIB_OVERRIDE = os.environ.get("KVQ_ORACLE_LIB")
 
 FMT_INT8_G64 = 0
 FMT_FP8_ROW = 1
+FMT_RK8V4 = 2
 SRC_F32 = 0
 SRC_BF16 = 1
 
@@ -61,6 +62,12 @@ def lib():
             getattr(L, name).restype = None
         L.orc_quant_rows.argtypes = [i32, vp, i64, i32, vp, vp]
         L.orc_quant_rows.restype = None
+        L.orc_h64_rotate_n.argtypes = [vp, vp, i64]
+        L.orc_h64_rotate_n.restype = None
+        L.orc_quant_int4_rows.argtypes = [vp, i64, i32, vp, vp]
+        L.orc_quant_int4_rows.restype = None
+        L.orc_v4_bit.argtypes = [i32, i32, i32]
+        L.orc_v4_bit.restype = i64
         L.orc_k_byte.argtypes = [i32, i32, i32]
         L.orc_k_byte.restype = i64
         L.orc_v_byte.argtypes = [i32, i32, i32]
@@ -123,17 +130,38 @@ def e4m3fn_to_f32(c) -> np.ndarray:
 
 # ---------------------------------------------------------------- quantizers
 def quant_rows(fmt: int, x) -> tuple[np.ndarray, np.ndarray]:
-    """x: float32 [..., D] -> (codes [..., D] (int8 | uint8), scales [..., D/64] uint16 | [...] float32)."""
+    """x: float32 [..., D] -> (codes [..., D] (int8 | uint8), scales [..., D/64] uint16 | [...] float32).
+    FMT_RK8V4 gives the key encoding (rotated, then INT8 group-64)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     D = x.shape[-1]
     n = x.size // D
-    if fmt == FMT_INT8_G64:
+    if fmt in (FMT_INT8_G64, FMT_RK8V4):
         codes = np.empty(x.shape, np.int8)
         scales = np.empty(x.shape[:-1] + (D // 64,), np.uint16)
     else:
         codes = np.empty(x.shape, np.uint8)
         scales = np.empty(x.shape[:-1], np.float32)
     lib().orc_quant_rows(fmt, _ptr(x), n, D, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def h64_rotate(x) -> np.ndarray:
+    """x: float32 [..., 64*k] -> each 64-element group rotated by the Sylvester Hadamard / 8."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert x.shape[-1] % 64 == 0
+    y = np.empty(x.shape, np.float32)
+    lib().orc_h64_rotate_n(_ptr(x), _ptr(y), x.size // 64)
+    return y
+
+
+def quant_int4_g32(x) -> tuple[np.ndarray, np.ndarray]:
+    """rk8v4 values: x float32 [..., D] -> (codes [..., D] int8 in -7..7, scales [..., D/32] uint16)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    D = x.shape[-1]
+    n = x.size // D
+    codes = np.empty(x.shape, np.int8)
+    scales = np.empty(x.shape[:-1] + (D // 32,), np.uint16)
+    lib().orc_quant_int4_rows(_ptr(x), n, D, _ptr(codes), _ptr(scales))
     return codes, scales
 
 
@@ -144,6 +172,10 @@ def k_byte(s: int, d: int, D: int) -> int:
 
 def v_byte(s: int, d: int, D: int) -> int:
     return lib().orc_v_byte(s, d, D)
+
+
+def v4_bit(s: int, d: int, D: int) -> int:
+    return lib().orc_v4_bit(s, d, D)
 
 
 def scale_elem(fmt: int, which: int, s: int, g: int, D: int) -> int:
@@ -158,8 +190,11 @@ class Pool:
         self.fmt, self.num_blocks, self.num_kv_heads, self.head_dim = fmt, num_blocks, num_kv_heads, head_dim
         n = num_blocks * num_kv_heads * 64
         self.k_codes = np.full(n * head_dim, fill, np.uint8)
-        self.v_codes = np.full(n * head_dim, fill, np.uint8)
-        if fmt == FMT_INT8_G64:
+        self.v_codes = np.full(n * head_dim // (2 if fmt == FMT_RK8V4 else 1), fill, np.uint8)
+        if fmt == FMT_RK8V4:
+            self.k_scales = np.zeros(n * (head_dim // 64), np.uint16)
+            self.v_scales = np.zeros(n * (head_dim // 32), np.uint16)
+        elif fmt == FMT_INT8_G64:
             self.k_scales = np.zeros(n * (head_dim // 64), np.uint16)
             self.v_scales = np.zeros(n * (head_dim // 64), np.uint16)
         else:

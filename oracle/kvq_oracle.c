@@ -183,6 +183,57 @@ void orc_quant_fp8_row(const float *x, int D, uint8_t *codes, float *scale) {
   for (int i = 0; i < D; ++i) codes[i] = (s != 0.0f) ? orc_f32_to_e4m3fn(x[i] / s) : 0;
 }
 
+/* RotorQuant rk8v4 keys.  The 64-point Hadamard matrix in Sylvester order has
+ * entry (-1)^popcount(i & j) at row j, column i; divided by 8 = sqrt(64) it is
+ * orthonormal and its own inverse.  The sum runs in binary64 in index order: for
+ * bf16 sources (8 significant bits) it is exact unless the 64 magnitudes span more
+ * than 2^39, so the single rounding to binary32 gives the correctly rounded rotation. */
+void orc_h64_rotate(const float *x, float *y) {
+  for (int j = 0; j < 64; ++j) {
+    double acc = 0.0;
+    for (int i = 0; i < 64; ++i) {
+      int odd = __builtin_popcount((unsigned)(i & j)) & 1;
+      acc += odd ? -(double)x[i] : (double)x[i];
+    }
+    y[j] = (float)(acc / 8.0);
+  }
+}
+
+/* Rotate each 64-dim group, then the INT8 group-64 encoding of the rotated row. */
+void orc_quant_rk8v4_k(const float *x, int D, int8_t *codes, uint16_t *scales) {
+  float *y = (float *)malloc(sizeof(float) * D);
+  for (int g = 0; g < D / 64; ++g) orc_h64_rotate(x + 64 * g, y + 64 * g);
+  orc_quant_int8_g64(y, D, codes, scales);
+  free(y);
+}
+
+/* Per 32-dim group: a = max|x|; s = fp16(a / 7) (fp32 division, RNE to fp16);
+ * c = clamp(rint(x / s), -7, 7) with the stored scale widened to fp32; s == 0
+ * gives all-zero codes.  Four bits hold the 15 levels -7..7. */
+void orc_quant_int4_g32(const float *x, int D, int8_t *codes, uint16_t *scales) {
+  for (int g = 0; g < D / 32; ++g) {
+    const float *xg = x + 32 * g;
+    float a = 0.0f;
+    for (int i = 0; i < 32; ++i) {
+      float v = fabsf(xg[i]);
+      if (v > a) a = v;
+    }
+    uint16_t h = orc_f32_to_f16_rne(a / 7.0f);
+    float step = orc_f16_to_f32(h);
+    scales[g] = h;
+    for (int i = 0; i < 32; ++i) {
+      int c = 0;
+      if (step != 0.0f) {
+        float q = rintf(xg[i] / step);
+        if (q > 7.0f) q = 7.0f;
+        if (q < -7.0f) q = -7.0f;
+        c = (int)q;
+      }
+      codes[32 * g + i] = (int8_t)c;
+    }
+  }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Page layout (one page = 64 token slots of one KV head in one block)       */
 /* ------------------------------------------------------------------------ */
@@ -202,15 +253,31 @@ int64_t orc_v_byte(int s, int d, int D) {
   return ((int64_t)(d / 16) * 4 + r) * 256 + (d % 16) * 16 + (s / 16) * 4 + (s % 4);
 }
 
+/* rk8v4 V: 4-bit codes, 64*D/2 bytes per page.  The 16 slots of run r of dim d
+ * take 8 bytes, two 32-bit little-endian words: word w holds the slots
+ * 16*j + 4*r + i with j in {2w, 2w+1}; with k = 4*(j % 2) + i, the code of k sits
+ * at bit 16*(k % 2) + 4*(k / 2) of the word (codes k, k+1 in the two 16-bit halves).
+ * The 8-byte chunks are ordered (d/32, r, d%16, (d/16)%2): the two 16-dim tiles
+ * of a 32-dim pair sit side by side. */
+int64_t orc_v4_bit(int s, int d, int D) {
+  (void)D;
+  int r = (s % 16) / 4, j = s / 16, i = s % 4;
+  int dt = d / 16;
+  int64_t word = (((int64_t)(dt / 2) * 64 + r * 16 + d % 16) * 16 + (dt % 2) * 8 + (j / 2) * 4);
+  int k = (j % 2) * 4 + i;
+  return word * 8 + 16 * (k % 2) + 4 * (k / 2);
+}
+
 /* Scales follow the same slot runs: run r = (s % 16) / 4 is the slowest index.
- * INT8 K scales: (run, s/16, group, s%4); INT8 V scales: (run, group, s/16, s%4);
- * FP8 scales (K and V): (run, s/16, s%4). */
+ * INT8 (and rk8v4) K scales: (run, s/16, group, s%4); INT8 V scales: (run, group, s/16, s%4);
+ * rk8v4 V scales: (run, 32-dim group, s/16, s%4); FP8 scales (K and V): (run, s/16, s%4). */
 int64_t orc_scale_elem(int fmt, int which, int s, int g, int D) {
   int r = (s % 16) / 4, j = s / 16, i = s % 4;
-  if (fmt == ORC_FMT_INT8_G64) {
+  if (fmt == ORC_FMT_INT8_G64 || (fmt == ORC_FMT_RK8V4 && which == 0)) {
     if (which == 0) return (((int64_t)r * 4 + j) * (D / 64) + g) * 4 + i;
     return ((int64_t)r * (D / 64) + g) * 16 + j * 4 + i;
   }
+  if (fmt == ORC_FMT_RK8V4) return ((int64_t)r * (D / 32) + g) * 16 + j * 4 + i;
   return (int64_t)r * 16 + j * 4 + i;
 }
 
@@ -228,7 +295,7 @@ int orc_append(const orc_pool *p, const void *k_new, const void *v_new, int src_
   const int H = p->num_kv_heads, D = p->head_dim, G = D / 64;
   float *x = (float *)malloc(sizeof(float) * D);
   uint8_t *codes = (uint8_t *)malloc(D);
-  uint16_t *s16 = (uint16_t *)malloc(sizeof(uint16_t) * (G > 0 ? G : 1));
+  uint16_t *s16 = (uint16_t *)malloc(sizeof(uint16_t) * (D / 32 > 0 ? D / 32 : 1));
   int rc = 0;
   for (int b = 0; b < B && rc == 0; ++b) {
     for (int t = 0; t < n_new && rc == 0; ++t) {
@@ -251,8 +318,26 @@ int orc_append(const orc_pool *p, const void *k_new, const void *v_new, int src_
           int64_t row = (((int64_t)b * n_new + t) * H + h) * D;
           for (int d = 0; d < D; ++d) x[d] = load_src(src, src_dtype, row + d);
           int64_t pg = page_index(p, block, h);
+          if (p->format == ORC_FMT_RK8V4 && which == 1) {
+            uint8_t *page4 = pool_codes + pg * 64 * (D / 2);
+            orc_quant_int4_g32(x, D, (int8_t *)codes, s16);
+            uint16_t *sc = (uint16_t *)pool_scales + pg * 64 * (D / 32);
+            for (int g = 0; g < D / 32; ++g) sc[orc_scale_elem(p->format, which, slot, g, D)] = s16[g];
+            for (int d = 0; d < D; ++d) {
+              int64_t bit = orc_v4_bit(slot, d, D);
+              uint8_t nib = (uint8_t)(codes[d] & 0x0F); /* two's complement nibble */
+              uint8_t *byte = page4 + bit / 8;
+              int sh = (int)(bit % 8);
+              *byte = (uint8_t)((*byte & ~(0x0F << sh)) | (nib << sh));
+            }
+            continue;
+          }
           uint8_t *page = pool_codes + pg * 64 * D;
-          if (p->format == ORC_FMT_INT8_G64) {
+          if (p->format == ORC_FMT_RK8V4) {
+            orc_quant_rk8v4_k(x, D, (int8_t *)codes, s16);
+            uint16_t *sc = (uint16_t *)pool_scales + pg * 64 * G;
+            for (int g = 0; g < G; ++g) sc[orc_scale_elem(p->format, which, slot, g, D)] = s16[g];
+          } else if (p->format == ORC_FMT_INT8_G64) {
             orc_quant_int8_g64(x, D, (int8_t *)codes, s16);
             uint16_t *sc = (uint16_t *)pool_scales + pg * 64 * G;
             for (int g = 0; g < G; ++g) sc[orc_scale_elem(p->format, which, slot, g, D)] = s16[g];
@@ -274,14 +359,23 @@ int orc_append(const orc_pool *p, const void *k_new, const void *v_new, int src_
   return rc;
 }
 
-/* Dequantized value: code * scale, exact in binary64. */
+/* Dequantized value: code * scale, exact in binary64.  rk8v4 keys stay in the
+ * rotated domain; rk8v4 values are the sign-extended nibble times its group scale. */
 double orc_dequant(const orc_pool *p, int which, int block, int kvh, int slot, int d) {
   const int D = p->head_dim;
   int64_t pg = page_index(p, block, kvh);
+  if (p->format == ORC_FMT_RK8V4 && which == 1) {
+    const uint8_t *page4 = p->v_codes + pg * 64 * (D / 2);
+    int64_t bit = orc_v4_bit(slot, d, D);
+    int nib = (page4[bit / 8] >> (bit % 8)) & 0x0F;
+    int c = nib >= 8 ? nib - 16 : nib;
+    uint16_t h = ((const uint16_t *)p->v_scales)[pg * 64 * (D / 32) + orc_scale_elem(p->format, 1, slot, d / 32, D)];
+    return (double)c * (double)orc_f16_to_f32(h);
+  }
   const uint8_t *page = (which ? p->v_codes : p->k_codes) + pg * 64 * D;
   uint8_t byte = page[which ? orc_v_byte(slot, d, D) : orc_k_byte(slot, d, D)];
   const void *scales = which ? p->v_scales : p->k_scales;
-  if (p->format == ORC_FMT_INT8_G64) {
+  if (p->format == ORC_FMT_INT8_G64 || p->format == ORC_FMT_RK8V4) {
     uint16_t h = ((const uint16_t *)scales)[pg * 64 * (D / 64) + orc_scale_elem(p->format, which, slot, d / 64, D)];
     return (double)(int8_t)byte * (double)orc_f16_to_f32(h);
   }
@@ -357,6 +451,21 @@ int orc_paged_attn(const orc_pool *p, const void *q, int q_dtype, int B, int T, 
       break;
     }
     for (int d = 0; d < D; ++d) qd[d] = (double)load_src(q, q_dtype, (int64_t)flat * D + d);
+    if (p->format == ORC_FMT_RK8V4) {
+      /* the keys are stored rotated: rotate the query by the same orthonormal
+       * matrix (in binary64), so that <H q, H k> / 64 = <q, k> */
+      for (int g = 0; g < D / 64; ++g) {
+        for (int j = 0; j < 64; ++j) {
+          double acc = 0.0;
+          for (int i = 0; i < 64; ++i) {
+            int odd = __builtin_popcount((unsigned)(i & j)) & 1;
+            acc += odd ? -qd[64 * g + i] : qd[64 * g + i];
+          }
+          row[64 * g + j] = acc / 8.0;
+        }
+      }
+      for (int d = 0; d < D; ++d) qd[d] = row[d];
+    }
     double m = -INFINITY;
     for (int j = 0; j <= last; ++j) {
       int block = block_table[(int64_t)b * max_blocks + j / 64];
@@ -401,12 +510,21 @@ void orc_f32_to_e4m3fn_n(const float *x, uint8_t *y, int64_t n) {
 void orc_e4m3fn_to_f32_n(const uint8_t *x, float *y, int64_t n) {
   for (int64_t i = 0; i < n; ++i) y[i] = orc_e4m3fn_to_f32(x[i]);
 }
-/* rows of D values -> codes [n][D] and scales [n][D/64] (INT8) or [n] (FP8) */
+/* rows of D values -> codes [n][D] and scales [n][D/64] (INT8, rk8v4 keys) or [n] (FP8) */
 void orc_quant_rows(int fmt, const float *x, int64_t n, int D, uint8_t *codes, void *scales) {
   for (int64_t r = 0; r < n; ++r) {
-    if (fmt == ORC_FMT_INT8_G64)
+    if (fmt == ORC_FMT_RK8V4)
+      orc_quant_rk8v4_k(x + r * D, D, (int8_t *)codes + r * D, (uint16_t *)scales + r * (D / 64));
+    else if (fmt == ORC_FMT_INT8_G64)
       orc_quant_int8_g64(x + r * D, D, (int8_t *)codes + r * D, (uint16_t *)scales + r * (D / 64));
     else
       orc_quant_fp8_row(x + r * D, D, codes + r * D, (float *)scales + r);
   }
+}
+void orc_h64_rotate_n(const float *x, float *y, int64_t ngroups) {
+  for (int64_t g = 0; g < ngroups; ++g) orc_h64_rotate(x + 64 * g, y + 64 * g);
+}
+/* rk8v4 value rows: codes [n][D] (-7..7) and scales [n][D/32] */
+void orc_quant_int4_rows(const float *x, int64_t n, int D, int8_t *codes, uint16_t *scales) {
+  for (int64_t r = 0; r < n; ++r) orc_quant_int4_g32(x + r * D, D, codes + r * D, scales + r * (D / 32));
 }

@@ -15,6 +15,15 @@
  *  - Row-scaled FP8 E4M3 KV: NInfer-3090 README, intro and "Current limits"
  *    (row-scaled FP8 E4M3 among the seven KV formats); one fp32 scale per token
  *    per KV head = absmax / 448.
+ *  - RotorQuant rk8v4 KV: keys rotated per 64-dim group by an orthonormal
+ *    64-point Hadamard matrix, then stored in the INT8 group-64 encoding;
+ *    values not rotated, stored as signed 4-bit codes (15 levels), two per
+ *    byte, with one FP16 scale per 32 dimensions.  NInfer-3090 README,
+ *    "RotorQuant KV (rk8v4)" (format, value group 32, no value rotation) and
+ *    "Choosing a KV format" (26,112 B/token).  The pages name the rotation H64
+ *    without printing it; the reading taken is the Sylvester-order Hadamard
+ *    matrix scaled by 1/8 (entry (j, i) = (-1)^popcount(i & j) / 8), and the
+ *    query is rotated by the same matrix in attention.
  *  - Quantization happens when rows are appended, in the append op:
  *    NInfer-3090 README, intro and "RotorQuant KV (rk8v4)".
  *  - Each decode step reads the whole cache: NInfer-3090 README, "Choosing a
@@ -33,7 +42,7 @@
 extern "C" {
 #endif
 
-enum { ORC_FMT_INT8_G64 = 0, ORC_FMT_FP8_ROW = 1 };
+enum { ORC_FMT_INT8_G64 = 0, ORC_FMT_FP8_ROW = 1, ORC_FMT_RK8V4 = 2 };
 enum { ORC_SRC_F32 = 0, ORC_SRC_BF16 = 1 };
 
 /* Scalar conversions, written from the IEEE-754 binary16, bfloat16 and OCP
@@ -49,12 +58,22 @@ void orc_quant_int8_g64(const float *x, int D, int8_t *codes, uint16_t *scales);
 /* One row of D values -> D E4M3FN codes and one fp32 scale. */
 void orc_quant_fp8_row(const float *x, int D, uint8_t *codes, float *scale);
 
+/* rk8v4.  y = (H64 / 8) x for one 64-dim group: y[j] = sum_i (-1)^popcount(i & j) x[i] / 8,
+ * summed in binary64 and rounded once to binary32. */
+void orc_h64_rotate(const float *x, float *y);
+/* One key row of D values -> rotated per 64-dim group, then INT8 group-64 codes and scales. */
+void orc_quant_rk8v4_k(const float *x, int D, int8_t *codes, uint16_t *scales);
+/* One value row of D values -> D signed 4-bit codes (-7..7, one per int8) and D/32 fp16 scales. */
+void orc_quant_int4_g32(const float *x, int D, int8_t *codes, uint16_t *scales);
+
 /* Byte offset of (token slot s, dim d) inside one (block, kv head) page. */
 int64_t orc_k_byte(int s, int d, int D);
 int64_t orc_v_byte(int s, int d, int D);
+/* rk8v4 values: bit offset of the 4-bit code of (slot s, dim d) inside a page of 64*D/2 bytes. */
+int64_t orc_v4_bit(int s, int d, int D);
 /* Element index of the scale of K (which=0) or V (which=1) for (slot s,
  * 64-group g) inside one page (INT8: D/64 scales per slot), or of slot s (FP8:
- * one per slot, pass g=0). */
+ * one per slot, pass g=0).  rk8v4: K as INT8; V per 32-dim group g (D/32 per slot). */
 int64_t orc_scale_elem(int fmt, int which, int s, int g, int D);
 
 typedef struct {
@@ -64,7 +83,7 @@ typedef struct {
   int32_t head_dim;
   uint8_t *k_codes;
   uint8_t *v_codes;
-  void *k_scales; /* uint16 fp16 bits (INT8) or float (FP8) */
+  void *k_scales; /* uint16 fp16 bits (INT8, rk8v4) or float (FP8) */
   void *v_scales;
 } orc_pool;
 
@@ -75,7 +94,8 @@ int orc_append(const orc_pool *pool, const void *k_new, const void *v_new, int s
                int B, int n_new, const int32_t *block_table, int max_blocks,
                const int32_t *start_pos);
 
-/* Dequantized value of K (which=0) or V (which=1) at (block, kv head, slot, dim). */
+/* Dequantized value of K (which=0) or V (which=1) at (block, kv head, slot, dim).
+ * rk8v4 keys come back in the rotated domain (code * scale). */
 double orc_dequant(const orc_pool *pool, int which, int block, int kvh, int slot, int d);
 
 /* Dense attention in fp64: for each query row r, keys 0..last[r] are visible.
@@ -99,6 +119,8 @@ void orc_bf16_to_f32_n(const uint16_t *x, float *y, int64_t n);
 void orc_f32_to_e4m3fn_n(const float *x, uint8_t *y, int64_t n);
 void orc_e4m3fn_to_f32_n(const uint8_t *x, float *y, int64_t n);
 void orc_quant_rows(int fmt, const float *x, int64_t n, int D, uint8_t *codes, void *scales);
+void orc_h64_rotate_n(const float *x, float *y, int64_t ngroups);
+void orc_quant_int4_rows(const float *x, int64_t n, int D, int8_t *codes, uint16_t *scales);
 
 #ifdef __cplusplus
 }

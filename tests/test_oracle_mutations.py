@@ -13,7 +13,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "kvq_oracle.c")
-PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_attention.py"]
+PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_attention.py", "tests/test_oracle_rk8v4.py"]
 
 # (name, original text, planted mistake)
 MUTATIONS = [
@@ -41,6 +41,12 @@ MUTATIONS = [
     ("paged_v_read_as_k", "row[d] += w * orc_dequant(p, 1, block, kvh, j % 64, d);",
      "row[d] += w * orc_dequant(p, 0, block, kvh, j % 64, d);"),
     ("append_slot_index", "int slot = (int)(pos % 64);", "int slot = (int)((pos + 1) % 64);"),
+    ("rk8v4_rotation_norm", "y[j] = (float)(acc / 8.0);", "y[j] = (float)(acc / 64.0);"),
+    ("rk8v4_rotation_sign", "acc += odd ? -(double)x[i] : (double)x[i];", "acc += odd ? (double)x[i] : -(double)x[i];"),
+    ("rk8v4_query_not_rotated", "for (int d = 0; d < D; ++d) qd[d] = row[d];", "for (int d = 0; d < D; ++d) (void)row[d];"),
+    ("int4_divisor_8", "uint16_t h = orc_f32_to_f16_rne(a / 7.0f);", "uint16_t h = orc_f32_to_f16_rne(a / 8.0f);"),
+    ("v4_nibble_order", "return word * 8 + 16 * (k % 2) + 4 * (k / 2);", "return word * 8 + 4 * k;"),
+    ("v4_scale_group_64", "orc_scale_elem(p->format, 1, slot, d / 32, D)", "orc_scale_elem(p->format, 1, slot, d / 64, D)"),
 ]
 
 

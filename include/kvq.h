@@ -23,6 +23,17 @@
  *                     code = clamp(rint(x / scale), -127, 127).
  *   KVQ_FP8_E4M3_ROW  OCP FP8 E4M3FN code per element, one fp32 scale per token
  *                     per KV head = absmax / 448; code = E4M3FN_rne_sat(x / scale).
+ *   KVQ_RK8V4         RotorQuant (NInfer-3090 README, "RotorQuant KV (rk8v4)";
+ *                     26,112 B/token on the 27B): each 64-dim group of a key row
+ *                     is rotated by H64/8, the Sylvester-order Hadamard matrix
+ *                     (entry (j, i) = (-1)^popcount(i & j)) over 8, and stored as
+ *                     KVQ_INT8_G64; the attention rotates the query by the same
+ *                     matrix.  The rotation sums run in binary64 and are rounded
+ *                     once to fp32 (exact, so bit-reproducible, for bf16 rows
+ *                     unless a group's magnitudes span more than 2^39).  Values are
+ *                     not rotated: a signed 4-bit code (-7..7, two's complement)
+ *                     per element with one fp16 scale per 32 dims:
+ *                     scale = fp16_rne(absmax / 7), code = clamp(rint(x / scale), -7, 7).
  *   A group (or row) whose absmax is 0 stores scale 0 and all-zero codes.
  *
  * Conventions for every call:
@@ -65,7 +76,7 @@ enum {
   KVQ_ERR_LAUNCH = -5       /* the HIP runtime refused a launch (no device, bad stream, ...) */
 };
 
-typedef enum { KVQ_INT8_G64 = 0, KVQ_FP8_E4M3_ROW = 1 } kvq_format_t;
+typedef enum { KVQ_INT8_G64 = 0, KVQ_FP8_E4M3_ROW = 1, KVQ_RK8V4 = 2 } kvq_format_t;
 typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype_t;
 
 /*
@@ -74,10 +85,12 @@ typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype_t;
  *
  *   k_codes, v_codes   num_blocks * num_kv_heads * 64 * head_dim bytes; page p
  *                      starts at byte p * 64 * head_dim.  int8 (INT8_G64) or
- *                      E4M3FN bytes (FP8_E4M3_ROW).
+ *                      E4M3FN bytes (FP8_E4M3_ROW).  RK8V4: k_codes as INT8_G64;
+ *                      v_codes 64 * head_dim / 2 bytes per page (4-bit codes).
  *   k_scales, v_scales INT8_G64: fp16, 64 * head_dim/64 per page, page p at
  *                      element p * head_dim;  FP8_E4M3_ROW: fp32, 64 per page,
- *                      page p at element p * 64.
+ *                      page p at element p * 64.  RK8V4: k_scales as INT8_G64;
+ *                      v_scales fp16, 64 * head_dim/32 per page (element p * 2 * head_dim).
  *
  * Inside a page (s = token slot 0..63, d = dim, D = head_dim, G64 = D/64,
  * run(s) = (s % 16) / 4, pos(s) = (s / 16) * 4 + s % 4):
@@ -88,6 +101,12 @@ typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype_t;
  *   INT8 K scale of (s, group g)  element ((run(s) * 4 + s/16) * G64 + g) * 4 + s%4
  *   INT8 V scale of (s, group g)  element (run(s) * G64 + g) * 16 + pos(s)
  *   FP8 K or V scale of s         element run(s) * 16 + pos(s)
+ *   RK8V4 K bytes and K scales    as INT8_G64
+ *   RK8V4 V code of (s, d)        4 bits at bit 16*(q%2) + 4*(q/2) of the little-endian
+ *           32-bit word at byte ((d/32)*64 + run(s)*16 + d%16) * 16 + ((d/16)%2) * 8
+ *           + (s/32) * 4, with q = 4 * ((s/16) % 2) + s % 4 (a word holds 8 slots of
+ *           one dim; the two 16-dim tiles of a 32-dim pair sit side by side)
+ *   RK8V4 V scale of (s, 32-dim group g)  element (run(s) * (D/32) + g) * 16 + pos(s)
  * These orders make every 64-lane load of the attention kernel one contiguous
  * 1 KiB segment that lands directly in matrix-core operand registers.
  */

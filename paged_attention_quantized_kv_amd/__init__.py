@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 INT8_G64 = 0
 FP8_E4M3_ROW = 1
+RK8V4 = 2
 F32 = 0
 BF16 = 1
 PAGE = 64
@@ -108,8 +109,11 @@ class Cache:
         n = num_blocks * num_kv_heads * PAGE
         if k_codes is None:
             k_codes = torch.empty(n * head_dim, dtype=torch.uint8, device=device)
-            v_codes = torch.empty(n * head_dim, dtype=torch.uint8, device=device)
-            if fmt == INT8_G64:
+            v_codes = torch.empty(n * head_dim // (2 if fmt == RK8V4 else 1), dtype=torch.uint8, device=device)
+            if fmt == RK8V4:  # INT8 group-64 keys; 4-bit values with one fp16 scale per 32 dims
+                k_scales = torch.empty(n * (head_dim // 64), dtype=torch.float16, device=device)
+                v_scales = torch.empty(n * (head_dim // 32), dtype=torch.float16, device=device)
+            elif fmt == INT8_G64:
                 k_scales = torch.empty(n * (head_dim // 64), dtype=torch.float16, device=device)
                 v_scales = torch.empty(n * (head_dim // 64), dtype=torch.float16, device=device)
             else:

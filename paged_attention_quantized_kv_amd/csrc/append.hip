@@ -30,6 +30,35 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   quant_row<FMT, D, SRC>(a, b, t, h, which, pos, blk, lane);
 }
 
+// rk8v4 keys in the bulk kernel: thread c16 holds dims 16*c16 .. +15 of its slot, so a
+// 64-dim group is 4 neighbouring threads; in-thread butterflies, then two across threads
+// (binary64, as in h64_rotate_lanes).
+__device__ inline void h64_rotate_threads(float (&x)[16], int c16) {
+  double y[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) y[e] = static_cast<double>(x[e]);
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if ((e & h) == 0) {
+        const double u = y[e], v = y[e + h];
+        y[e] = u + v;
+        y[e + h] = u - v;
+      }
+#pragma unroll
+  for (int m = 1; m < 4; m <<= 1) {
+    const bool hi = (c16 & m) != 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const double o = __shfl_xor(y[e], m);
+      y[e] = hi ? (o - y[e]) : (y[e] + o);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) x[e] = static_cast<float>(y[e] * 0.125);
+}
+
 // Bulk appends (prefill chunks): one workgroup per (page, KV head, K|V, sequence), one
 // thread per (slot, 16 dims): 64 * D/16 threads.  Each thread quantizes its 16 values
 // with the same arithmetic as quant_row (so the codes are identical), the group or row
@@ -92,11 +121,26 @@ __global__ __launch_bounds__(kPage * D / 16) void append_page_kernel(AppendArgs 
 #pragma unroll
     for (int e = 0; e < 16; ++e) x[e] = 0.0f;
   }
+  if constexpr (FMT == 2) {
+    if (which == 0) h64_rotate_threads(x, c16);  // rk8v4 keys: rotate each 64-dim group
+  }
   uint32_t c[16];
   float amax = 0.0f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
-  if constexpr (FMT == 0) {  // INT8, one fp16 scale per 64 dims: 4 neighbouring threads
+  if (FMT == 2 && which == 1) {  // rk8v4 values: 4-bit codes, one fp16 scale per 32 dims (2 threads)
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    const _Float16 s16 = static_cast<_Float16>(amax / 7.0f);
+    const float sc = static_cast<float>(s16);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float r = 0.0f;
+      if (sc != 0.0f) r = fminf(fmaxf(rintf(x[e] / sc), -7.0f), 7.0f);
+      c[e] = static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFu;
+    }
+    if (mine && (c16 & 1) == 0)
+      static_cast<_Float16 *>(a.v_scales)[page * (kPage * D / 32) + (run * (D / 32) + c16 / 2) * 16 + spos] = s16;
+  } else if constexpr (FMT == 0 || FMT == 2) {  // INT8, one fp16 scale per 64 dims: 4 neighbouring threads
     amax = fmaxf(amax, __shfl_xor(amax, 1));
     amax = fmaxf(amax, __shfl_xor(amax, 2));
     const _Float16 s16 = static_cast<_Float16>(amax / 127.0f);
@@ -135,6 +179,34 @@ __global__ __launch_bounds__(kPage * D / 16) void append_page_kernel(AppendArgs 
   // thread) is dim d = (k/64)*16 + k%16, run r = (k/16)%4, whose byte 4j+i holds slot 16j+4r+i
   *reinterpret_cast<uint4 *>(vstage + sl * D + 16 * c16) = make_uint4(w[0], w[1], w[2], w[3]);
   __syncthreads();
+  if constexpr (FMT == 2) {
+    // rk8v4: 8-byte chunk k (one per thread) holds dim d = 16*dt + (k/2)%16 with
+    // dt = 2*(k/128) + k%2, run r = (k/32)%4; its word w holds the slots 16*(2w + q/4) +
+    // 4r + q%4 (q = 0..7), code q at bit 16*(q%2) + 4*(q/2)
+    const int k = tid, dt = 2 * (k / 128) + (k % 2), d = 16 * dt + (k / 2) % 16, r = (k / 32) % 4;
+    uint32_t *words = reinterpret_cast<uint32_t *>(a.v_codes + page * kPage * (D / 2)) + 2 * static_cast<size_t>(k);
+    uint32_t v[2], m[2];
+#pragma unroll
+    for (int wv = 0; wv < 2; ++wv) {
+      v[wv] = 0;
+      m[wv] = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int sj = 16 * (2 * wv + q / 4) + 4 * r + q % 4;
+        const int sh = 16 * (q % 2) + 4 * (q / 2);
+        v[wv] |= static_cast<uint32_t>(vstage[sj * D + d]) << sh;
+        if (sj >= s_lo && sj < s_hi) m[wv] |= 0xFu << sh;
+      }
+    }
+    if (full) {
+      *reinterpret_cast<uint2 *>(words) = make_uint2(v[0], v[1]);
+    } else {  // keep the codes of slots outside the chunk (this thread owns the word)
+#pragma unroll
+      for (int wv = 0; wv < 2; ++wv)
+        if (m[wv] != 0) words[wv] = (words[wv] & ~m[wv]) | (v[wv] & m[wv]);
+    }
+    return;
+  }
   const int k = tid, d = (k / 64) * 16 + (k % 16), r = (k / 16) % 4;
   if (full) {
     uint32_t v[4];
@@ -186,6 +258,10 @@ hipError_t launch_append(int format, int head_dim, int src_dtype, const AppendAr
   KVQ_APPEND_CASE(1, 128, 1)
   KVQ_APPEND_CASE(1, 256, 0)
   KVQ_APPEND_CASE(1, 256, 1)
+  KVQ_APPEND_CASE(2, 128, 0)
+  KVQ_APPEND_CASE(2, 128, 1)
+  KVQ_APPEND_CASE(2, 256, 0)
+  KVQ_APPEND_CASE(2, 256, 1)
 #undef KVQ_APPEND_CASE
   return hipErrorInvalidValue;
 }

@@ -67,6 +67,21 @@ __device__ inline f16x8 codes_to_f16(uint32_t w0, uint32_t w1) {
   }
 }
 
+// rk8v4 values: one 32-bit word holds the 4-bit codes (two's complement) of 8 keys,
+// key q at bit 16*(q%2) + 4*(q/2), so masking with 0x000F000F after a shift of 4p
+// gives keys 2p, 2p+1 in the two halves.  Flipping bit 3 of every nibble maps c to
+// n = c + 8; the f16 with bits 0x6400 | n is 1024 + n, so subtracting 1032 leaves c.
+__device__ inline f16x8 v4_to_f16(uint32_t w) {
+  const uint32_t x = w ^ 0x88888888u;
+  const _Float16 bias = static_cast<_Float16>(1032.0f);
+  const f16x2 b2{bias, bias};
+  const f16x2 a = __builtin_bit_cast(f16x2, (x & 0x000F000Fu) | 0x64006400u) - b2;
+  const f16x2 b = __builtin_bit_cast(f16x2, ((x >> 4) & 0x000F000Fu) | 0x64006400u) - b2;
+  const f16x2 c = __builtin_bit_cast(f16x2, ((x >> 8) & 0x000F000Fu) | 0x64006400u) - b2;
+  const f16x2 d = __builtin_bit_cast(f16x2, ((x >> 12) & 0x000F000Fu) | 0x64006400u) - b2;
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // x ~= hi + lo with hi = f16(x) rounded toward zero and lo = f16(x - hi): the
 // pair carries ~21 significant bits.
 __device__ inline void split_f16(float x0, float x1, f16x2 &hi, f16x2 &lo) {
@@ -130,13 +145,16 @@ __device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr float kLazy = 8.0f;
 
 // One wave's share of one page: its K tile (16 keys x all dims) and its V dim
-// tiles (all 64 keys), with their scales.
+// tiles (all 64 keys), with their scales.  rk8v4 (FMT 2): K as INT8; V as 4-bit codes,
+// one 16-byte load per pair of dim tiles, and the fp16 scales of two 32-dim groups.
 template <int D, int FMT>
 struct PageRegs {
   static constexpr int G64 = D / 64, DPW = D / 64;  // dim tiles per wave = D/16/4
-  static constexpr int KSN = (FMT == 0) ? (D / 128) : 1, VSN = (FMT == 0) ? 2 : 4;
+  static constexpr int KSN = (FMT == 1) ? 1 : (D / 128);
+  static constexpr int VN = (FMT == 2) ? DPW / 2 : DPW;
+  static constexpr int VSN = (FMT == 0) ? 2 : (FMT == 1 ? 4 : DPW);
   uint4 k[G64];
-  uint4 v[DPW];
+  uint4 v[VN];
   uint4 ks[KSN];
   uint4 vs[VSN];
 };
@@ -162,7 +180,7 @@ __device__ inline void load_k_part(PageRegs<D, FMT> &r, const AttnArgs &a, int p
   const uint4 *kp = reinterpret_cast<const uint4 *>(a.k_codes + pg * kPage * D);
 #pragma unroll
   for (int cg = 0; cg < G64; ++cg) r.k[cg] = ld_stream(kp + (wave * NCH + 4 * cg) * 16 + lane);
-  if constexpr (FMT == 0) {
+  if constexpr (FMT != 1) {
     const uint4 *ksp = reinterpret_cast<const uint4 *>(static_cast<const _Float16 *>(a.k_scales) + pg * D);
 #pragma unroll
     for (int j = 0; j < PageRegs<D, FMT>::KSN; ++j) r.ks[j] = ksp[(q4 * 4 + wave) * PageRegs<D, FMT>::KSN + j];
@@ -176,6 +194,17 @@ template <int D, int FMT>
 __device__ inline void load_v_part(PageRegs<D, FMT> &r, const AttnArgs &a, int pg_any, int wave, int lane, int q4) {
   constexpr int G64 = D / 64, DPW = D / 64;
   const size_t pg = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pg_any));
+  if constexpr (FMT == 2) {  // 4-bit codes: tile pair p of the wave is one KiB, 16 bytes per lane
+    const uint4 *vp = reinterpret_cast<const uint4 *>(a.v_codes + pg * kPage * (D / 2));
+#pragma unroll
+    for (int p = 0; p < DPW / 2; ++p) r.v[p] = ld_stream(vp + (wave * (DPW / 2) + p) * 64 + lane);
+    const uint4 *vsp = reinterpret_cast<const uint4 *>(static_cast<const _Float16 *>(a.v_scales) + pg * (kPage * D / 32));
+#pragma unroll
+    for (int p = 0; p < DPW / 2; ++p)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) r.vs[2 * p + j] = vsp[(q4 * (D / 32) + wave * (DPW / 2) + p) * 2 + j];
+    return;
+  }
   const uint4 *vp = reinterpret_cast<const uint4 *>(a.v_codes + pg * kPage * D);
 #pragma unroll
   for (int j = 0; j < DPW; ++j) r.v[j] = ld_stream(vp + (wave * DPW + j) * 64 + lane);
@@ -217,10 +246,14 @@ struct Smem {
 // 2 = prefill: the query rows come in blocks of 16*NT rows (grid y = row block * Hkv
 // + KV head), chunks hold up to kMaxPrefillChunkPages pages, and with one chunk per
 // row block the normalized rows go straight to out.
+// QLO: 0 = bf16 queries entering as one f16 each; 1 = fp32 queries as f16 hi + lo;
+// 2 = bf16 queries rotated for rk8v4 keys (FMT 2), which no longer fit one f16: hi + lo.
 template <int D, int NT, int FMT, int QLO, int NTEAM, int APP>
 __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) {
   constexpr int G64 = D / 64, NCH = D / 16, DPW = D / 64;
   constexpr int QP = QLO ? 2 : 1;
+  constexpr int KF = (FMT == 2) ? 0 : FMT;  // key code format: rk8v4 keys are INT8 group-64
+  static_assert(FMT != 2 || QLO != 0, "rotated queries need the lo part");
   using SM = Smem<D, NT, NTEAM, QP>;
   constexpr int ROWS = SM::ROWS, PST = SM::PST;
   __shared__ uint4 qs[SM::QS];
@@ -313,7 +346,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
         if (r < n_rows) {
           const int t = t_lo + (r >> 1);
           blk_r[k] = bt[(L - a.T + t) / kPage];
-          load_row<D, QLO ? 0 : 1>(aa, b, t, kvh, r & 1, lane, xr[k]);
+          load_row<D, QLO == 1 ? 0 : 1>(aa, b, t, kvh, r & 1, lane, xr[k]);
         }
       }
     }
@@ -325,7 +358,43 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 
   // ---- queries -> LDS in B-operand order: entry (nt, cg, hk, hl, lane) holds dims
   // 64cg + 16(lane/16) + 8hk + 0..7 of row 16nt + lane%16, as f16 hi (hl=0) or lo (hl=1).
-  for (int e = tid; e < NT * G64 * 2 * 64; e += 256 * NTEAM) {
+  if constexpr (FMT == 2) {
+    // rk8v4: the keys are stored rotated by H64/8 per 64-dim group, so each 64-dim group
+    // of a query row is rotated by the same matrix (butterflies in fp32, one thread per
+    // (row, group)) before it is split into f16 hi + lo
+    for (int task = tid; task < ROWS * G64; task += 256 * NTEAM) {
+      const int rl = task / G64, cg = task % G64, r = row0 + rl;
+      float v[64];
+      if (r < R) {
+        const int t = r / a.group, hq = kvh * a.group + r % a.group;
+        const size_t qb = ((static_cast<size_t>(b) * a.T + t) * a.num_q_heads + hq) * D + 64 * cg;
+#pragma unroll
+        for (int i = 0; i < 64; ++i) v[i] = load_q<QLO != 1>(a.q, qb + i);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 64; ++i) v[i] = 0.0f;
+      }
+#pragma unroll
+      for (int hh = 1; hh < 64; hh <<= 1)
+#pragma unroll
+        for (int i = 0; i < 64; ++i)
+          if ((i & hh) == 0) {
+            const float u = v[i], w = v[i + hh];
+            v[i] = u + w;
+            v[i + hh] = u - w;
+          }
+#pragma unroll
+      for (int jh = 0; jh < 8; ++jh) {  // dims 8jh .. 8jh+7 of the group: lane 16(jh/2) + rl%16, hk = jh%2
+        f16x2 hi[4], lo[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) split_f16(v[8 * jh + 2 * j] * 0.125f, v[8 * jh + 2 * j + 1] * 0.125f, hi[j], lo[j]);
+        const int idx = (((rl / 16) * G64 + cg) * 2 + (jh & 1)) * QP * 64 + 16 * (jh >> 1) + (rl % 16);
+        qs[idx] = __builtin_bit_cast(uint4, f16x8{hi[0][0], hi[0][1], hi[1][0], hi[1][1], hi[2][0], hi[2][1], hi[3][0], hi[3][1]});
+        qs[idx + 64] = __builtin_bit_cast(uint4, f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]});
+      }
+    }
+  }
+  for (int e = tid; e < ((FMT == 2) ? 0 : NT * G64 * 2 * 64); e += 256 * NTEAM) {
     const int ln = e & 63, hk = (e >> 6) & 1, cg = (e >> 7) % G64, nt = (e >> 7) / G64;
     const int r = row0 + 16 * nt + (ln & 15);
     const int d0 = 64 * cg + 16 * (ln >> 4) + 8 * hk;
@@ -335,8 +404,9 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
       const size_t qb = ((static_cast<size_t>(b) * a.T + t) * a.num_q_heads + hq) * D + d0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        // QLO is set exactly for fp32 queries; bf16 queries need no lo part
-        const float x0 = load_q<!QLO>(a.q, qb + 2 * j), x1 = load_q<!QLO>(a.q, qb + 2 * j + 1);
+        // QLO = 1 for fp32 queries (hi + lo), 2 for rotated bf16 queries (hi + lo), 0 for
+        // bf16 queries (one exact f16)
+        const float x0 = load_q<QLO != 1>(a.q, qb + 2 * j), x1 = load_q<QLO != 1>(a.q, qb + 2 * j + 1);
         if constexpr (QLO) {
           split_f16(x0, x1, hi[j], lo[j]);
         } else {
@@ -359,7 +429,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
         const int t = t_lo + (r >> 1);
         const long pos = static_cast<long>(L) - a.T + t;
         const int blk = bt[pos / kPage];
-        if (blk >= 0 && blk < a.num_blocks) quant_row<FMT, D, QLO ? 0 : 1>(aa, b, t, kvh, r & 1, pos, blk, lane);
+        if (blk >= 0 && blk < a.num_blocks) quant_row<FMT, D, QLO == 1 ? 0 : 1>(aa, b, t, kvh, r & 1, pos, blk, lane);
       }
       // a wave that wrote rows waits until its stores have reached L2, so every wave of this
       // workgroup loads the new rows after the barrier below (no other workgroup reads them)
@@ -415,7 +485,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
       }
 #pragma unroll
       for (int hk = 0; hk < 2; ++hk) {
-        const f16x8 ka = hk ? codes_to_f16<FMT>(pr.k[cg].z, pr.k[cg].w) : codes_to_f16<FMT>(pr.k[cg].x, pr.k[cg].y);
+        const f16x8 ka = hk ? codes_to_f16<KF>(pr.k[cg].z, pr.k[cg].w) : codes_to_f16<KF>(pr.k[cg].x, pr.k[cg].y);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           acc[nt] = mfma16(ka, qc[hk][nt][0], acc[nt]);
@@ -425,7 +495,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
       if constexpr (QPF == 2) {
         if (cg + 2 < G64) read_q(qc, cg + 2);
       }
-      if constexpr (FMT == 0) {  // fold each key's fp16 group scale, restart the group sum
+      if constexpr (KF == 0) {  // fold each key's fp16 group scale, restart the group sum
         const uint4 w = pr.ks[cg >> 1];
         float sk[4];
         f16x2_to_f32((cg & 1) ? w.z : w.x, sk[0], sk[1]);
@@ -466,36 +536,54 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     if constexpr (MASKED) {
       // slots at or past L may hold anything (never written): zero their V codes
       const int kbase = p * kPage + 4 * q4;  // key of (kt, i) is kbase + 16kt + i
-      uint32_t mw[4];
+      if constexpr (FMT == 2) {
+        // word ks holds keys kt = 2ks + q/4, i = q%4 (q = 0..7) at bit 16*(q%2) + 4*(q/2)
+        uint32_t mw[2];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        uint32_t wv = 0;
+        for (int ks = 0; ks < 2; ++ks) {
+          uint32_t wv = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wv |= (kbase + 16 * kt + i < L) ? (0xFFu << (8 * i)) : 0u;
-        mw[kt] = wv;
-      }
+          for (int q = 0; q < 8; ++q)
+            wv |= (kbase + 16 * (2 * ks + q / 4) + q % 4 < L) ? (0xFu << (16 * (q % 2) + 4 * (q / 2))) : 0u;
+          mw[ks] = wv;
+        }
 #pragma unroll
-      for (int j = 0; j < DPW; ++j) {
-        pr.v[j].x &= mw[0];
-        pr.v[j].y &= mw[1];
-        pr.v[j].z &= mw[2];
-        pr.v[j].w &= mw[3];
+        for (int j = 0; j < PageRegs<D, FMT>::VN; ++j) {
+          pr.v[j].x &= mw[0];
+          pr.v[j].y &= mw[1];
+          pr.v[j].z &= mw[0];
+          pr.v[j].w &= mw[1];
+        }
+      } else {
+        uint32_t mw[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          uint32_t wv = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) wv |= (kbase + 16 * kt + i < L) ? (0xFFu << (8 * i)) : 0u;
+          mw[kt] = wv;
+        }
+#pragma unroll
+        for (int j = 0; j < DPW; ++j) {
+          pr.v[j].x &= mw[0];
+          pr.v[j].y &= mw[1];
+          pr.v[j].z &= mw[2];
+          pr.v[j].w &= mw[3];
+        }
       }
     }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      f16x8 bh[NT], bl[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
+    // the B operands (P^T, each key's weight times its V scale, as f16 hi + lo) of key
+    // half ks; w: the fp16 V scales of keys 16(2ks) .. 16(2ks+1)+15 of this lane group
+    auto build_b1 = [&](int ks, const uint4 &w, int nt, f16x8 &bh, f16x8 &bl) {
+      {
         f16x2 hi[4], lo[4];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           const int kt = 2 * ks + kk;
-          if constexpr (FMT == 0) {
+          if constexpr (FMT != 1) {
             const uint4 pw = *reinterpret_cast<const uint4 *>(pb + (16 * nt + c16) * PST + 16 * kt + 4 * q4);
             const f16x2 h01 = __builtin_bit_cast(f16x2, pw.x), h23 = __builtin_bit_cast(f16x2, pw.y);
             const f16x2 l01 = __builtin_bit_cast(f16x2, pw.z), l23 = __builtin_bit_cast(f16x2, pw.w);
-            const uint4 w = pr.vs[ks];
             f16x2 s01 = __builtin_bit_cast(f16x2, kk ? w.z : w.x), s23 = __builtin_bit_cast(f16x2, kk ? w.w : w.y);
             if constexpr (MASKED) {  // unwritten slots (weight 0) may hold NaN scales
               s01 = f16x2{h01[0] != _Float16(0) ? s01[0] : _Float16(0), h01[1] != _Float16(0) ? s01[1] : _Float16(0)};
@@ -506,8 +594,8 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
           } else {
             const float4 pw = *reinterpret_cast<const float4 *>(pb + (16 * nt + c16) * PST + 16 * kt + 4 * q4);
             const float pp[4] = {pw.x, pw.y, pw.z, pw.w};
-            const uint4 w = pr.vs[kt];
-            const float sv[4] = {__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w)};
+            const uint4 sw = pr.vs[kt];
+            const float sv[4] = {__uint_as_float(sw.x), __uint_as_float(sw.y), __uint_as_float(sw.z), __uint_as_float(sw.w)};
             float pv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -518,16 +606,44 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
             split_f16(pv[2], pv[3], hi[2 * kk + 1], lo[2 * kk + 1]);
           }
         }
-        bh[nt] = f16x8{hi[0][0], hi[0][1], hi[1][0], hi[1][1], hi[2][0], hi[2][1], hi[3][0], hi[3][1]};
-        bl[nt] = f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]};
+        bh = f16x8{hi[0][0], hi[0][1], hi[1][0], hi[1][1], hi[2][0], hi[2][1], hi[3][0], hi[3][1]};
+        bl = f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]};
       }
+    };
+    auto build_b = [&](int ks, const uint4 &w, f16x8 (&bh)[NT], f16x8 (&bl)[NT]) {
 #pragma unroll
-      for (int j = 0; j < DPW; ++j) {
-        const f16x8 va = ks ? codes_to_f16<FMT>(pr.v[j].z, pr.v[j].w) : codes_to_f16<FMT>(pr.v[j].x, pr.v[j].y);
+      for (int nt = 0; nt < NT; ++nt) build_b1(ks, w, nt, bh[nt], bl[nt]);
+    };
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          o[nt][j] = mfma16(va, bh[nt], o[nt][j]);
-          o[nt][j] = mfma16(va, bl[nt], o[nt][j]);
+    for (int ks = 0; ks < 2; ++ks) {
+      if constexpr (FMT == 2) {
+        // one 32-dim scale group per pair of dim tiles, with its own B operands (built
+        // one row tile at a time to keep few of them live)
+#pragma unroll
+        for (int gp = 0; gp < DPW / 2; ++gp) {
+          const uint4 &vw = pr.v[gp];
+          const f16x8 va0 = v4_to_f16(ks ? vw.y : vw.x), va1 = v4_to_f16(ks ? vw.w : vw.z);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            f16x8 bh, bl;
+            build_b1(ks, pr.vs[2 * gp + ks], nt, bh, bl);
+            o[nt][2 * gp] = mfma16(va0, bh, o[nt][2 * gp]);
+            o[nt][2 * gp] = mfma16(va0, bl, o[nt][2 * gp]);
+            o[nt][2 * gp + 1] = mfma16(va1, bh, o[nt][2 * gp + 1]);
+            o[nt][2 * gp + 1] = mfma16(va1, bl, o[nt][2 * gp + 1]);
+          }
+        }
+      } else {
+        f16x8 bh[NT], bl[NT];
+        build_b(ks, pr.vs[FMT == 0 ? ks : 0], bh, bl);
+#pragma unroll
+        for (int j = 0; j < DPW; ++j) {
+          const f16x8 va = ks ? codes_to_f16<FMT>(pr.v[j].z, pr.v[j].w) : codes_to_f16<FMT>(pr.v[j].x, pr.v[j].y);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            o[nt][j] = mfma16(va, bh[nt], o[nt][j]);
+            o[nt][j] = mfma16(va, bl[nt], o[nt][j]);
+          }
         }
       }
     }
@@ -578,9 +694,9 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 #pragma unroll
         for (int i = 0; i < 4; ++i) pv[i] = exp2_hw(z[nt][i] - msafe);
         psum[nt] = (pv[0] + pv[1]) + (pv[2] + pv[3]);
-        if constexpr (FMT == 0) {
-          // INT8: the weights go out as f16 hi+lo pairs (the V scales, fp16, are applied by
-          // the accumulating wave with packed f16 arithmetic)
+        if constexpr (FMT != 1) {
+          // INT8 and rk8v4: the weights go out as f16 hi+lo pairs (the V scales, fp16, are
+          // applied by the accumulating wave with packed f16 arithmetic)
           f16x2 h01, l01, h23, l23;
           split_f16(pv[0], pv[1], h01, l01);
           split_f16(pv[2], pv[3], h23, l23);
@@ -844,8 +960,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 
 template <int D, int NT, int FMT, int QDT>
 hipError_t split_one(const AttnArgs &a, hipStream_t s) {
-  // fp32 queries need the hi+lo pair; bf16 queries are one exact f16
-  constexpr int QLO = QDT == 0 ? 1 : 0;
+  // fp32 queries need the hi+lo pair; bf16 queries are one exact f16, unless rotated (rk8v4)
+  constexpr int QLO = QDT == 0 ? 1 : (FMT == 2 ? 2 : 0);
   const dim3 grid(a.n_splits, a.num_kv_heads, a.num_seqs);
   if (a.k_new != nullptr)
     hipLaunchKernelGGL((attn_split_kernel<D, NT, FMT, QLO, kTeams, 1>), grid, dim3(256 * kTeams), 0, s, a);
@@ -856,7 +972,7 @@ hipError_t split_one(const AttnArgs &a, hipStream_t s) {
 
 template <int D, int FMT, int QDT>
 hipError_t prefill_one(const AttnArgs &a, hipStream_t s) {
-  constexpr int QLO = QDT == 0 ? 1 : 0;
+  constexpr int QLO = QDT == 0 ? 1 : (FMT == 2 ? 2 : 0);
   const dim3 grid(a.n_splits, a.num_kv_heads * a.row_blocks, a.num_seqs);
   hipLaunchKernelGGL((attn_split_kernel<D, kPrefillNT, FMT, QLO, kPrefillTeams, 2>), grid, dim3(256 * kPrefillTeams),
                      0, s, a);
@@ -876,7 +992,8 @@ hipError_t launch_attn_split(int format, int head_dim, int q_dtype, const AttnAr
 #define KVQ_SPLIT_CASE(DD, NTT, F, Q) \
   if (head_dim == DD && nt == NTT && format == F && q_dtype == Q) return split_one<DD, NTT, F, Q>(a, s);
 #define KVQ_SPLIT_DQ(DD, NTT) \
-  KVQ_SPLIT_CASE(DD, NTT, 0, 0) KVQ_SPLIT_CASE(DD, NTT, 0, 1) KVQ_SPLIT_CASE(DD, NTT, 1, 0) KVQ_SPLIT_CASE(DD, NTT, 1, 1)
+  KVQ_SPLIT_CASE(DD, NTT, 0, 0) KVQ_SPLIT_CASE(DD, NTT, 0, 1) KVQ_SPLIT_CASE(DD, NTT, 1, 0) KVQ_SPLIT_CASE(DD, NTT, 1, 1) \
+  KVQ_SPLIT_CASE(DD, NTT, 2, 0) KVQ_SPLIT_CASE(DD, NTT, 2, 1)
   KVQ_SPLIT_DQ(128, 1)
   KVQ_SPLIT_DQ(128, 2)
   KVQ_SPLIT_DQ(256, 1)
@@ -891,6 +1008,7 @@ hipError_t launch_attn_prefill(int format, int head_dim, int q_dtype, const Attn
   if (head_dim == DD && format == F && q_dtype == Q) return prefill_one<DD, F, Q>(a, s);
   KVQ_PF_CASE(128, 0, 0) KVQ_PF_CASE(128, 0, 1) KVQ_PF_CASE(128, 1, 0) KVQ_PF_CASE(128, 1, 1)
   KVQ_PF_CASE(256, 0, 0) KVQ_PF_CASE(256, 0, 1) KVQ_PF_CASE(256, 1, 0) KVQ_PF_CASE(256, 1, 1)
+  KVQ_PF_CASE(128, 2, 0) KVQ_PF_CASE(128, 2, 1) KVQ_PF_CASE(256, 2, 0) KVQ_PF_CASE(256, 2, 1)
 #undef KVQ_PF_CASE
   return hipErrorInvalidValue;
 }

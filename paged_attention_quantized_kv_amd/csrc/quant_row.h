@@ -37,6 +37,49 @@ __device__ inline uint32_t e4m3fn_rne_sat(float v) {
   return sign | code;
 }
 
+// rk8v4 keys: the 64-dim groups of a key row are rotated by H64/8 (Sylvester-order
+// Hadamard matrix, entry (j, i) = (-1)^popcount(i & j), over 8) before the INT8
+// encoding (NInfer-3090 README, "RotorQuant KV (rk8v4)").  The butterflies run in
+// binary64, where the sums of bf16 inputs are exact (unless a group's magnitudes
+// span more than 2^39), and the result is rounded once to binary32.
+//   x: the E consecutive elements (lane % (64/E)) * E + 0 .. E-1 of one 64-dim group,
+//   which is spread over 64/E adjacent lanes.
+template <int E>
+__device__ inline void h64_rotate_lanes(float (&x)[E], int lane) {
+  double y[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) y[e] = static_cast<double>(x[e]);
+#pragma unroll
+  for (int h = 1; h < E; h <<= 1)  // in-lane butterflies
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if ((e & h) == 0) {
+        const double u = y[e], v = y[e + h];
+        y[e] = u + v;
+        y[e + h] = u - v;
+      }
+#pragma unroll
+  for (int m = 1; m < 64 / E; m <<= 1) {  // across lanes: partner lane ^ m holds index ^ (m*E)
+    const bool hi = (lane & m) != 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const double o = __shfl_xor(y[e], m);
+      y[e] = hi ? (o - y[e]) : (y[e] + o);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = static_cast<float>(y[e] * 0.125);
+}
+
+// rk8v4 values: bit offset (within the 4-byte-aligned word of a page of 64*D/2 bytes)
+// of the 4-bit code of (slot s, dim d): see kvq.h.  Returns the word index and the shift.
+__device__ inline void v4_place(int s, int d, size_t &word, int &shift) {
+  const int r = (s % 16) / 4, j = s / 16, i = s % 4, dt = d / 16;
+  const int k = (j % 2) * 4 + i;
+  word = (static_cast<size_t>((dt / 2) * 64 + r * 16 + d % 16) * 16 + (dt % 2) * 8 + (j / 2) * 4) / 4;
+  shift = 16 * (k % 2) + 4 * (k / 2);
+}
+
 // Row t of sequence b, KV head h, K (which=0) or V (which=1) of the
 // [B][n_new][Hkv][D] source: this lane's D/64 consecutive elements, widened.
 template <int D, int SRC>
@@ -52,18 +95,55 @@ __device__ inline void load_row(const AppendArgs &a, int b, int t, int h, int wh
 // at position pos of the sequence: slot pos % 64 of block blk, KV head h.
 // Called by all 64 lanes of a wave.
 template <int FMT, int D>
-__device__ inline void store_row(const AppendArgs &a, const float (&x)[D / 64], int h, int which, long pos, int blk,
+__device__ inline void store_row(const AppendArgs &a, const float (&xin)[D / 64], int h, int which, long pos, int blk,
                                  int lane) {
   constexpr int E = D / 64;            // elements per lane
   constexpr int LPG = 64 / E;          // lanes per 64-dim group
   const int slot = static_cast<int>(pos % kPage);
   const int run = (slot % 16) / 4, spos = (slot / 16) * 4 + slot % 4;
+  float x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = xin[e];
+  if constexpr (FMT == 2) {
+    if (which == 0) h64_rotate_lanes<E>(x, lane);
+  }
 
   const size_t page = static_cast<size_t>(blk) * a.num_kv_heads + h;
-  uint8_t *codes = (which ? a.v_codes : a.k_codes) + page * kPage * D;
   uint32_t c[E];
 
-  if constexpr (FMT == 0) {  // INT8, one fp16 scale per 64 dims
+  if constexpr (FMT == 2) {
+    if (which == 1) {  // rk8v4 values: signed 4-bit codes, one fp16 scale per 32 dims
+      constexpr int LPG32 = 32 / E;
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(x[e]));
+#pragma unroll
+      for (int off = 1; off < LPG32; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+      const _Float16 s16 = static_cast<_Float16>(amax / 7.0f);  // IEEE division, RNE to fp16
+      const float s = static_cast<float>(s16);
+      uint32_t *words = reinterpret_cast<uint32_t *>(a.v_codes + page * kPage * (D / 2));
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float r = 0.0f;
+        if (s != 0.0f) r = fminf(fmaxf(rintf(x[e] / s), -7.0f), 7.0f);
+        const uint32_t nib = static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFu;
+        size_t wi;
+        int sh;
+        v4_place(slot, lane * E + e, wi, sh);
+        // other slots share the word (other rows of this launch may write them now)
+        atomicAnd(words + wi, ~(0xFu << sh));
+        atomicOr(words + wi, nib << sh);
+      }
+      if ((lane % LPG32) == 0) {
+        const int g = lane / LPG32;
+        static_cast<_Float16 *>(a.v_scales)[page * (kPage * D / 32) + (run * (D / 32) + g) * 16 + spos] = s16;
+      }
+      return;
+    }
+  }
+  uint8_t *codes = (which ? a.v_codes : a.k_codes) + page * kPage * D;
+
+  if constexpr (FMT == 0 || FMT == 2) {  // INT8 (rk8v4: of the rotated key), one fp16 scale per 64 dims
     float amax = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(x[e]));

@@ -17,6 +17,7 @@ tokens; shapes after NInfer-4090 README "What this fork changes", d256-h24-kv4):
               4096 context rows form one prefill chunk
   mtp128k_rk8v4  mtp128k's data in the rk8v4 format (rotated INT8 keys,
               4-bit group-32 values)
+  mtp128k_rk4v4  the same in the rk4v4 format (4-bit Lloyd-Max keys)
 
 Every pool starts filled with poison (code bytes 0x7F, NaN scales), so a read of
 a slot that was never appended shows up as NaN in the output.  Block-table
@@ -34,12 +35,13 @@ PAGE = 64
 FMT_INT8_G64 = 0
 FMT_FP8_ROW = 1
 FMT_RK8V4 = 2
+FMT_RK4V4 = 3
 SRC_F32 = 0
 SRC_BF16 = 1
 
 CONFIG_NAMES = ["tiny", "qwen32k", "mtp128k", "c8", "full256k_int8", "full256k_fp8"]
 _SEED_INDEX = {"tiny": 0, "qwen32k": 1, "mtp128k": 2, "c8": 3, "full256k_int8": 4, "full256k_fp8": 4,
-               "mtp128k_rk8v4": 2}
+               "mtp128k_rk8v4": 2, "mtp128k_rk4v4": 2}
 
 
 @dataclasses.dataclass
@@ -72,6 +74,8 @@ def shape(name: str, **over) -> Shape:
         s = Shape(name, 1, 1, 24, 4, 256, [262144], SRC_BF16, FMT_INT8_G64, True, chunk=4096)
     elif name == "mtp128k_rk8v4":
         s = Shape(name, 1, 4, 24, 4, 256, [131072], SRC_BF16, FMT_RK8V4, True)
+    elif name == "mtp128k_rk4v4":
+        s = Shape(name, 1, 4, 24, 4, 256, [131072], SRC_BF16, FMT_RK4V4, True)
     elif name == "full256k_fp8":
         s = Shape(name, 1, 1, 24, 4, 256, [262144], SRC_BF16, FMT_FP8_ROW, True, chunk=4096)
     else:
@@ -125,6 +129,8 @@ class Workload:
         s = self.shape
         if s.fmt == FMT_RK8V4:  # INT8 keys with fp16 group-64 scales, 4-bit values with fp16 group-32 scales
             per_tok_head = (s.D + 2 * (s.D // 64)) + (s.D // 2 + 2 * (s.D // 32))
+        elif s.fmt == FMT_RK4V4:  # 4-bit keys with fp16 group-64 scales, rk8v4 values
+            per_tok_head = (s.D // 2 + 2 * (s.D // 64)) + (s.D // 2 + 2 * (s.D // 32))
         else:
             per_tok_head = 2 * (s.D + (2 * (s.D // 64) if s.fmt == FMT_INT8_G64 else 4))
         return int(self.seq_lens.sum()) * s.Hkv * per_tok_head

@@ -25,6 +25,7 @@ _LIB_OVERRIDE = os.environ.get("KVQ_ORACLE_LIB")
 FMT_INT8_G64 = 0
 FMT_FP8_ROW = 1
 FMT_RK8V4 = 2
+FMT_RK4V4 = 3
 SRC_F32 = 0
 SRC_BF16 = 1
 
@@ -68,6 +69,14 @@ def lib():
         L.orc_quant_int4_rows.restype = None
         L.orc_v4_bit.argtypes = [i32, i32, i32]
         L.orc_v4_bit.restype = i64
+        L.orc_k4_bit.argtypes = [i32, i32, i32]
+        L.orc_k4_bit.restype = i64
+        L.orc_lloyd_max16.argtypes = [vp]
+        L.orc_lloyd_max16.restype = None
+        L.orc_rk4_codes.argtypes = [vp]
+        L.orc_rk4_codes.restype = None
+        L.orc_quant_rk4v4_rows.argtypes = [vp, i64, i32, vp, vp]
+        L.orc_quant_rk4v4_rows.restype = None
         L.orc_k_byte.argtypes = [i32, i32, i32]
         L.orc_k_byte.restype = i64
         L.orc_v_byte.argtypes = [i32, i32, i32]
@@ -165,6 +174,31 @@ def quant_int4_g32(x) -> tuple[np.ndarray, np.ndarray]:
     return codes, scales
 
 
+def lloyd_max16() -> np.ndarray:
+    """The 16 Lloyd-Max levels for N(0,1), ascending (the oracle's iteration)."""
+    out = np.empty(16, np.float64)
+    lib().orc_lloyd_max16(_ptr(out))
+    return out
+
+
+def rk4_codes() -> np.ndarray:
+    """The INT8 code of each rk4v4 level."""
+    out = np.empty(16, np.int8)
+    lib().orc_rk4_codes(_ptr(out))
+    return out
+
+
+def quant_rk4v4_keys(x) -> tuple[np.ndarray, np.ndarray]:
+    """rk4v4 keys: x float32 [..., D] -> (level indices [..., D] uint8 0..15, scales [..., D/64] uint16)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    D = x.shape[-1]
+    n = x.size // D
+    idx = np.empty(x.shape, np.uint8)
+    scales = np.empty(x.shape[:-1] + (D // 64,), np.uint16)
+    lib().orc_quant_rk4v4_rows(_ptr(x), n, D, _ptr(idx), _ptr(scales))
+    return idx, scales
+
+
 # ---------------------------------------------------------------- layout
 def k_byte(s: int, d: int, D: int) -> int:
     return lib().orc_k_byte(s, d, D)
@@ -178,6 +212,10 @@ def v4_bit(s: int, d: int, D: int) -> int:
     return lib().orc_v4_bit(s, d, D)
 
 
+def k4_bit(s: int, d: int, D: int) -> int:
+    return lib().orc_k4_bit(s, d, D)
+
+
 def scale_elem(fmt: int, which: int, s: int, g: int, D: int) -> int:
     return lib().orc_scale_elem(fmt, which, s, g, D)
 
@@ -189,9 +227,9 @@ class Pool:
     def __init__(self, fmt: int, num_blocks: int, num_kv_heads: int, head_dim: int, fill: int = 0):
         self.fmt, self.num_blocks, self.num_kv_heads, self.head_dim = fmt, num_blocks, num_kv_heads, head_dim
         n = num_blocks * num_kv_heads * 64
-        self.k_codes = np.full(n * head_dim, fill, np.uint8)
-        self.v_codes = np.full(n * head_dim // (2 if fmt == FMT_RK8V4 else 1), fill, np.uint8)
-        if fmt == FMT_RK8V4:
+        self.k_codes = np.full(n * head_dim // (2 if fmt == FMT_RK4V4 else 1), fill, np.uint8)
+        self.v_codes = np.full(n * head_dim // (2 if fmt in (FMT_RK8V4, FMT_RK4V4) else 1), fill, np.uint8)
+        if fmt in (FMT_RK8V4, FMT_RK4V4):
             self.k_scales = np.zeros(n * (head_dim // 64), np.uint16)
             self.v_scales = np.zeros(n * (head_dim // 32), np.uint16)
         elif fmt == FMT_INT8_G64:

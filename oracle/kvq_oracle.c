@@ -207,6 +207,75 @@ void orc_quant_rk8v4_k(const float *x, int D, int8_t *codes, uint16_t *scales) {
   free(y);
 }
 
+/* rk4v4 keys.  Lloyd's iteration for the minimum-mean-square-error quantizer of a
+ * standard Gaussian with 16 levels: each threshold is the midpoint of its two
+ * neighbouring levels, each level the mean of N(0,1) over its cell,
+ * E[X | a < X <= b] = (phi(a) - phi(b)) / (Phi(b) - Phi(a)).  Started from evenly
+ * spaced levels and run until no level moves (binary64). */
+static double std_pdf(double x) { return isinf(x) ? 0.0 : exp(-0.5 * x * x) / sqrt(2.0 * acos(-1.0)); }
+static double std_cdf(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
+
+void orc_lloyd_max16(double *L) {
+  for (int i = 0; i < 16; ++i) L[i] = -3.0 + 6.0 * i / 15.0;
+  for (int it = 0; it < 100000; ++it) {
+    double t[17], nl[16], moved = 0.0;
+    t[0] = -INFINITY;
+    t[16] = INFINITY;
+    for (int i = 1; i < 16; ++i) t[i] = 0.5 * (L[i - 1] + L[i]);
+    for (int i = 0; i < 16; ++i) {
+      nl[i] = (std_pdf(t[i]) - std_pdf(t[i + 1])) / (std_cdf(t[i + 1]) - std_cdf(t[i]));
+      moved = fmax(moved, fabs(nl[i] - L[i]));
+    }
+    for (int i = 0; i < 16; ++i) L[i] = nl[i];
+    if (moved < 1e-15) break;
+  }
+}
+
+void orc_rk4_codes(int8_t *codes) {
+  double L[16];
+  orc_lloyd_max16(L);
+  for (int i = 0; i < 16; ++i) codes[i] = (int8_t)rint(127.0 * L[i] / L[15]);
+}
+
+static int8_t g_rk4_code[16];
+static int g_rk4_ready = 0;
+static const int8_t *rk4_codes(void) {
+  if (!g_rk4_ready) {
+    orc_rk4_codes(g_rk4_code);
+    g_rk4_ready = 1;
+  }
+  return g_rk4_code;
+}
+
+/* Rotate each 64-dim group; per group a = max|y|, s = fp16(a / 127) (the INT8 scale);
+ * u = y / s in fp32; the index is the number of level midpoints (c_i + c_{i+1}) / 2
+ * strictly below u, i.e. the level whose code is nearest to u, ties to the lower one.
+ * s == 0 gives u = 0 for every element. */
+void orc_quant_rk4v4_k(const float *x, int D, uint8_t *idx, uint16_t *scales) {
+  const int8_t *c = rk4_codes();
+  float *y = (float *)malloc(sizeof(float) * D);
+  for (int g = 0; g < D / 64; ++g) orc_h64_rotate(x + 64 * g, y + 64 * g);
+  for (int g = 0; g < D / 64; ++g) {
+    const float *yg = y + 64 * g;
+    float a = 0.0f;
+    for (int i = 0; i < 64; ++i) {
+      float v = fabsf(yg[i]);
+      if (v > a) a = v;
+    }
+    uint16_t h = orc_f32_to_f16_rne(a / 127.0f);
+    float sc = orc_f16_to_f32(h);
+    scales[g] = h;
+    for (int i = 0; i < 64; ++i) {
+      float u = (sc != 0.0f) ? yg[i] / sc : 0.0f;
+      int k = 0;
+      for (int m = 0; m < 15; ++m)
+        if (0.5f * (float)(c[m] + c[m + 1]) < u) ++k;
+      idx[64 * g + i] = (uint8_t)k;
+    }
+  }
+  free(y);
+}
+
 /* Per 32-dim group: a = max|x|; s = fp16(a / 7) (fp32 division, RNE to fp16);
  * c = clamp(rint(x / s), -7, 7) with the stored scale widened to fp32; s == 0
  * gives all-zero codes.  Four bits hold the 15 levels -7..7. */
@@ -268,16 +337,27 @@ int64_t orc_v4_bit(int s, int d, int D) {
   return word * 8 + 16 * (k % 2) + 4 * (k / 2);
 }
 
+/* rk4v4 K: 4-bit level indices, 64*D/2 bytes per page.  The 16 dims 16*(d/16) .. +15
+ * of slot s take 8 bytes: two 32-bit words (dims 0..7 and 8..15 of the 16), whose
+ * byte b holds dim b (low nibble) and dim b + 4 (high nibble) of its 8.  The 8-byte
+ * chunks of the two 64-dim groups 2p, 2p+1 sit side by side, and the 16-byte units
+ * are ordered (s/16, d/128, (d%64)/16, s%16). */
+int64_t orc_k4_bit(int s, int d, int D) {
+  int64_t unit = ((int64_t)(s / 16) * (D / 128) + d / 128) * 64 + ((d % 64) / 16) * 16 + (s % 16);
+  int64_t byte = unit * 16 + ((d / 64) % 2) * 8 + ((d % 16) / 8) * 4 + (d % 4);
+  return byte * 8 + 4 * ((d % 8) / 4);
+}
+
 /* Scales follow the same slot runs: run r = (s % 16) / 4 is the slowest index.
  * INT8 (and rk8v4) K scales: (run, s/16, group, s%4); INT8 V scales: (run, group, s/16, s%4);
  * rk8v4 V scales: (run, 32-dim group, s/16, s%4); FP8 scales (K and V): (run, s/16, s%4). */
 int64_t orc_scale_elem(int fmt, int which, int s, int g, int D) {
   int r = (s % 16) / 4, j = s / 16, i = s % 4;
-  if (fmt == ORC_FMT_INT8_G64 || (fmt == ORC_FMT_RK8V4 && which == 0)) {
+  if (fmt == ORC_FMT_INT8_G64 || ((fmt == ORC_FMT_RK8V4 || fmt == ORC_FMT_RK4V4) && which == 0)) {
     if (which == 0) return (((int64_t)r * 4 + j) * (D / 64) + g) * 4 + i;
     return ((int64_t)r * (D / 64) + g) * 16 + j * 4 + i;
   }
-  if (fmt == ORC_FMT_RK8V4) return ((int64_t)r * (D / 32) + g) * 16 + j * 4 + i;
+  if (fmt == ORC_FMT_RK8V4 || fmt == ORC_FMT_RK4V4) return ((int64_t)r * (D / 32) + g) * 16 + j * 4 + i;
   return (int64_t)r * 16 + j * 4 + i;
 }
 
@@ -318,7 +398,7 @@ int orc_append(const orc_pool *p, const void *k_new, const void *v_new, int src_
           int64_t row = (((int64_t)b * n_new + t) * H + h) * D;
           for (int d = 0; d < D; ++d) x[d] = load_src(src, src_dtype, row + d);
           int64_t pg = page_index(p, block, h);
-          if (p->format == ORC_FMT_RK8V4 && which == 1) {
+          if ((p->format == ORC_FMT_RK8V4 || p->format == ORC_FMT_RK4V4) && which == 1) {
             uint8_t *page4 = pool_codes + pg * 64 * (D / 2);
             orc_quant_int4_g32(x, D, (int8_t *)codes, s16);
             uint16_t *sc = (uint16_t *)pool_scales + pg * 64 * (D / 32);
@@ -329,6 +409,19 @@ int orc_append(const orc_pool *p, const void *k_new, const void *v_new, int src_
               uint8_t *byte = page4 + bit / 8;
               int sh = (int)(bit % 8);
               *byte = (uint8_t)((*byte & ~(0x0F << sh)) | (nib << sh));
+            }
+            continue;
+          }
+          if (p->format == ORC_FMT_RK4V4) {
+            uint8_t *page4 = pool_codes + pg * 64 * (D / 2);
+            orc_quant_rk4v4_k(x, D, codes, s16);
+            uint16_t *sc = (uint16_t *)pool_scales + pg * 64 * G;
+            for (int g = 0; g < G; ++g) sc[orc_scale_elem(p->format, which, slot, g, D)] = s16[g];
+            for (int d = 0; d < D; ++d) {
+              int64_t bit = orc_k4_bit(slot, d, D);
+              uint8_t *byte = page4 + bit / 8;
+              int sh = (int)(bit % 8);
+              *byte = (uint8_t)((*byte & ~(0x0F << sh)) | ((codes[d] & 0x0F) << sh));
             }
             continue;
           }
@@ -364,7 +457,14 @@ int orc_append(const orc_pool *p, const void *k_new, const void *v_new, int src_
 double orc_dequant(const orc_pool *p, int which, int block, int kvh, int slot, int d) {
   const int D = p->head_dim;
   int64_t pg = page_index(p, block, kvh);
-  if (p->format == ORC_FMT_RK8V4 && which == 1) {
+  if (p->format == ORC_FMT_RK4V4 && which == 0) {
+    const uint8_t *page4 = p->k_codes + pg * 64 * (D / 2);
+    int64_t bit = orc_k4_bit(slot, d, D);
+    int nib = (page4[bit / 8] >> (bit % 8)) & 0x0F;
+    uint16_t h = ((const uint16_t *)p->k_scales)[pg * 64 * (D / 64) + orc_scale_elem(p->format, 0, slot, d / 64, D)];
+    return (double)rk4_codes()[nib] * (double)orc_f16_to_f32(h);
+  }
+  if ((p->format == ORC_FMT_RK8V4 || p->format == ORC_FMT_RK4V4) && which == 1) {
     const uint8_t *page4 = p->v_codes + pg * 64 * (D / 2);
     int64_t bit = orc_v4_bit(slot, d, D);
     int nib = (page4[bit / 8] >> (bit % 8)) & 0x0F;
@@ -451,7 +551,7 @@ int orc_paged_attn(const orc_pool *p, const void *q, int q_dtype, int B, int T, 
       break;
     }
     for (int d = 0; d < D; ++d) qd[d] = (double)load_src(q, q_dtype, (int64_t)flat * D + d);
-    if (p->format == ORC_FMT_RK8V4) {
+    if (p->format == ORC_FMT_RK8V4 || p->format == ORC_FMT_RK4V4) {
       /* the keys are stored rotated: rotate the query by the same orthonormal
        * matrix (in binary64), so that <H q, H k> / 64 = <q, k> */
       for (int g = 0; g < D / 64; ++g) {
@@ -527,4 +627,8 @@ void orc_h64_rotate_n(const float *x, float *y, int64_t ngroups) {
 /* rk8v4 value rows: codes [n][D] (-7..7) and scales [n][D/32] */
 void orc_quant_int4_rows(const float *x, int64_t n, int D, int8_t *codes, uint16_t *scales) {
   for (int64_t r = 0; r < n; ++r) orc_quant_int4_g32(x + r * D, D, codes + r * D, scales + r * (D / 32));
+}
+/* rk4v4 key rows: level indices [n][D] (0..15) and scales [n][D/64] */
+void orc_quant_rk4v4_rows(const float *x, int64_t n, int D, uint8_t *idx, uint16_t *scales) {
+  for (int64_t r = 0; r < n; ++r) orc_quant_rk4v4_k(x + r * D, D, idx + r * D, scales + r * (D / 64));
 }

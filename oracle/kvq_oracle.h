@@ -24,6 +24,16 @@
  *    without printing it; the reading taken is the Sylvester-order Hadamard
  *    matrix scaled by 1/8 (entry (j, i) = (-1)^popcount(i & j) / 8), and the
  *    query is rotated by the same matrix in attention.
+ *  - rk4v4 KV: rk8v4's values; each rotated key dimension becomes a 4-bit index
+ *    into the 16-level Lloyd-Max quantizer for a Gaussian, with one FP16 scale
+ *    per 64 dimensions, and each level has a fixed INT8 code, so an expanded key
+ *    is an INT8 rotated key.  NInfer-3090 README, "Lloyd-Max 4-bit keys (rk4v4)"
+ *    and "Choosing a KV format" (17,920 B/token).  The pages print neither the
+ *    levels nor the scale rule; the readings taken: the levels come from Lloyd's
+ *    iteration on N(0,1) (computed here), level i has INT8 code
+ *    rint(127 * L_i / L_15), the group scale is the INT8 one (fp16(absmax / 127)),
+ *    and a coordinate takes the level whose code is nearest to x / scale (a tie
+ *    goes to the lower level).
  *  - Quantization happens when rows are appended, in the append op:
  *    NInfer-3090 README, intro and "RotorQuant KV (rk8v4)".
  *  - Each decode step reads the whole cache: NInfer-3090 README, "Choosing a
@@ -42,7 +52,7 @@
 extern "C" {
 #endif
 
-enum { ORC_FMT_INT8_G64 = 0, ORC_FMT_FP8_ROW = 1, ORC_FMT_RK8V4 = 2 };
+enum { ORC_FMT_INT8_G64 = 0, ORC_FMT_FP8_ROW = 1, ORC_FMT_RK8V4 = 2, ORC_FMT_RK4V4 = 3 };
 enum { ORC_SRC_F32 = 0, ORC_SRC_BF16 = 1 };
 
 /* Scalar conversions, written from the IEEE-754 binary16, bfloat16 and OCP
@@ -63,6 +73,13 @@ void orc_quant_fp8_row(const float *x, int D, uint8_t *codes, float *scale);
 void orc_h64_rotate(const float *x, float *y);
 /* One key row of D values -> rotated per 64-dim group, then INT8 group-64 codes and scales. */
 void orc_quant_rk8v4_k(const float *x, int D, int8_t *codes, uint16_t *scales);
+/* rk4v4.  The 16 Lloyd-Max levels for N(0,1), ascending (Lloyd's iteration to its fixed
+ * point), and their INT8 codes rint(127 * L_i / L_15). */
+void orc_lloyd_max16(double *levels);
+void orc_rk4_codes(int8_t *codes);
+/* One key row of D values -> rotated per 64-dim group, then D level indices 0..15
+ * (one per byte) and D/64 fp16 scales = fp16(absmax / 127) of the rotated group. */
+void orc_quant_rk4v4_k(const float *x, int D, uint8_t *idx, uint16_t *scales);
 /* One value row of D values -> D signed 4-bit codes (-7..7, one per int8) and D/32 fp16 scales. */
 void orc_quant_int4_g32(const float *x, int D, int8_t *codes, uint16_t *scales);
 
@@ -71,9 +88,11 @@ int64_t orc_k_byte(int s, int d, int D);
 int64_t orc_v_byte(int s, int d, int D);
 /* rk8v4 values: bit offset of the 4-bit code of (slot s, dim d) inside a page of 64*D/2 bytes. */
 int64_t orc_v4_bit(int s, int d, int D);
+/* rk4v4 keys: bit offset of the 4-bit level index of (slot s, dim d) inside a page of 64*D/2 bytes. */
+int64_t orc_k4_bit(int s, int d, int D);
 /* Element index of the scale of K (which=0) or V (which=1) for (slot s,
  * 64-group g) inside one page (INT8: D/64 scales per slot), or of slot s (FP8:
- * one per slot, pass g=0).  rk8v4: K as INT8; V per 32-dim group g (D/32 per slot). */
+ * one per slot, pass g=0).  rk8v4 and rk4v4: K as INT8; V per 32-dim group g (D/32 per slot). */
 int64_t orc_scale_elem(int fmt, int which, int s, int g, int D);
 
 typedef struct {
@@ -95,7 +114,7 @@ int orc_append(const orc_pool *pool, const void *k_new, const void *v_new, int s
                const int32_t *start_pos);
 
 /* Dequantized value of K (which=0) or V (which=1) at (block, kv head, slot, dim).
- * rk8v4 keys come back in the rotated domain (code * scale). */
+ * rk8v4 and rk4v4 keys come back in the rotated domain (code * scale). */
 double orc_dequant(const orc_pool *pool, int which, int block, int kvh, int slot, int d);
 
 /* Dense attention in fp64: for each query row r, keys 0..last[r] are visible.
@@ -121,6 +140,7 @@ void orc_e4m3fn_to_f32_n(const uint8_t *x, float *y, int64_t n);
 void orc_quant_rows(int fmt, const float *x, int64_t n, int D, uint8_t *codes, void *scales);
 void orc_h64_rotate_n(const float *x, float *y, int64_t ngroups);
 void orc_quant_int4_rows(const float *x, int64_t n, int D, int8_t *codes, uint16_t *scales);
+void orc_quant_rk4v4_rows(const float *x, int64_t n, int D, uint8_t *idx, uint16_t *scales);
 
 #ifdef __cplusplus
 }

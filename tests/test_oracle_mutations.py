@@ -13,7 +13,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "kvq_oracle.c")
-PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_attention.py", "tests/test_oracle_rk8v4.py"]
+PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_attention.py", "tests/test_oracle_rk8v4.py",
+        "tests/test_oracle_rk4v4.py"]
 
 # (name, original text, planted mistake)
 MUTATIONS = [
@@ -47,6 +48,13 @@ MUTATIONS = [
     ("int4_divisor_8", "uint16_t h = orc_f32_to_f16_rne(a / 7.0f);", "uint16_t h = orc_f32_to_f16_rne(a / 8.0f);"),
     ("v4_nibble_order", "return word * 8 + 16 * (k % 2) + 4 * (k / 2);", "return word * 8 + 4 * k;"),
     ("v4_scale_group_64", "orc_scale_elem(p->format, 1, slot, d / 32, D)", "orc_scale_elem(p->format, 1, slot, d / 64, D)"),
+    ("lloyd_threshold_not_midpoint", "for (int i = 1; i < 16; ++i) t[i] = 0.5 * (L[i - 1] + L[i]);",
+     "for (int i = 1; i < 16; ++i) t[i] = 0.4 * L[i - 1] + 0.6 * L[i];"),
+    ("rk4_codes_truncated", "codes[i] = (int8_t)rint(127.0 * L[i] / L[15]);", "codes[i] = (int8_t)(127.0 * L[i] / L[15]);"),
+    ("rk4_ties_upward", "if (0.5f * (float)(c[m] + c[m + 1]) < u) ++k;", "if (0.5f * (float)(c[m] + c[m + 1]) <= u) ++k;"),
+    ("rk4_scale_divisor", "uint16_t h = orc_f32_to_f16_rne(a / 127.0f);\n    float sc = orc_f16_to_f32(h);",
+     "uint16_t h = orc_f32_to_f16_rne(a / 96.0f);\n    float sc = orc_f16_to_f32(h);"),
+    ("k4_nibble_order", "return byte * 8 + 4 * ((d % 8) / 4);", "return byte * 8 + 4 * (d % 2);"),
 ]
 
 

@@ -34,6 +34,16 @@
  *                     not rotated: a signed 4-bit code (-7..7, two's complement)
  *                     per element with one fp16 scale per 32 dims:
  *                     scale = fp16_rne(absmax / 7), code = clamp(rint(x / scale), -7, 7).
+ *   KVQ_RK4V4         rk8v4's values; keys rotated as in rk8v4, then each rotated
+ *                     dimension is a 4-bit index into the 16-level Lloyd-Max
+ *                     quantizer of a unit Gaussian (NInfer-3090 README, "Lloyd-Max
+ *                     4-bit keys (rk4v4)"; 17,920 B/token on the 27B).  Level i
+ *                     carries the fixed INT8 code rint(127 * L_i / L_15): -127 -96
+ *                     -75 -58 -44 -31 -18 -6 6 18 31 44 58 75 96 127 (index 0..15),
+ *                     so a key dequantizes as code(index) * scale with the
+ *                     KVQ_INT8_G64 group scale fp16_rne(absmax / 127) of the rotated
+ *                     group; index = the level whose code is nearest to y / scale
+ *                     (fp32), ties to the lower level.
  *   A group (or row) whose absmax is 0 stores scale 0 and all-zero codes.
  *
  * Conventions for every call:
@@ -76,7 +86,7 @@ enum {
   KVQ_ERR_LAUNCH = -5       /* the HIP runtime refused a launch (no device, bad stream, ...) */
 };
 
-typedef enum { KVQ_INT8_G64 = 0, KVQ_FP8_E4M3_ROW = 1, KVQ_RK8V4 = 2 } kvq_format_t;
+typedef enum { KVQ_INT8_G64 = 0, KVQ_FP8_E4M3_ROW = 1, KVQ_RK8V4 = 2, KVQ_RK4V4 = 3 } kvq_format_t;
 typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype_t;
 
 /*
@@ -87,9 +97,10 @@ typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype_t;
  *                      starts at byte p * 64 * head_dim.  int8 (INT8_G64) or
  *                      E4M3FN bytes (FP8_E4M3_ROW).  RK8V4: k_codes as INT8_G64;
  *                      v_codes 64 * head_dim / 2 bytes per page (4-bit codes).
+ *                      RK4V4: k_codes and v_codes 64 * head_dim / 2 bytes per page.
  *   k_scales, v_scales INT8_G64: fp16, 64 * head_dim/64 per page, page p at
  *                      element p * head_dim;  FP8_E4M3_ROW: fp32, 64 per page,
- *                      page p at element p * 64.  RK8V4: k_scales as INT8_G64;
+ *                      page p at element p * 64.  RK8V4, RK4V4: k_scales as INT8_G64;
  *                      v_scales fp16, 64 * head_dim/32 per page (element p * 2 * head_dim).
  *
  * Inside a page (s = token slot 0..63, d = dim, D = head_dim, G64 = D/64,
@@ -107,6 +118,10 @@ typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype_t;
  *           + (s/32) * 4, with q = 4 * ((s/16) % 2) + s % 4 (a word holds 8 slots of
  *           one dim; the two 16-dim tiles of a 32-dim pair sit side by side)
  *   RK8V4 V scale of (s, 32-dim group g)  element (run(s) * (D/32) + g) * 16 + pos(s)
+ *   RK4V4 V codes and scales, K scales     as RK8V4
+ *   RK4V4 K index of (s, d)  4 bits at bit 8*(d%4) + 4*((d%8)/4) of the little-endian
+ *           32-bit word at byte u * 16 + ((d/64)%2) * 8 + ((d%16)/8) * 4, with
+ *           u = ((s/16) * (D/128) + d/128) * 64 + ((d%64)/16) * 16 + s%16
  * These orders make every 64-lane load of the attention kernel one contiguous
  * 1 KiB segment that lands directly in matrix-core operand registers.
  */

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 INT8_G64 = 0
 FP8_E4M3_ROW = 1
 RK8V4 = 2
+RK4V4 = 3
 F32 = 0
 BF16 = 1
 PAGE = 64
@@ -108,9 +109,9 @@ class Cache:
         self.format, self.num_blocks, self.num_kv_heads, self.head_dim = fmt, num_blocks, num_kv_heads, head_dim
         n = num_blocks * num_kv_heads * PAGE
         if k_codes is None:
-            k_codes = torch.empty(n * head_dim, dtype=torch.uint8, device=device)
-            v_codes = torch.empty(n * head_dim // (2 if fmt == RK8V4 else 1), dtype=torch.uint8, device=device)
-            if fmt == RK8V4:  # INT8 group-64 keys; 4-bit values with one fp16 scale per 32 dims
+            k_codes = torch.empty(n * head_dim // (2 if fmt == RK4V4 else 1), dtype=torch.uint8, device=device)
+            v_codes = torch.empty(n * head_dim // (2 if fmt in (RK8V4, RK4V4) else 1), dtype=torch.uint8, device=device)
+            if fmt in (RK8V4, RK4V4):  # fp16 group-64 key scales; 4-bit values with one fp16 scale per 32 dims
                 k_scales = torch.empty(n * (head_dim // 64), dtype=torch.float16, device=device)
                 v_scales = torch.empty(n * (head_dim // 32), dtype=torch.float16, device=device)
             elif fmt == INT8_G64:

@@ -121,14 +121,14 @@ __global__ __launch_bounds__(kPage * D / 16) void append_page_kernel(AppendArgs 
 #pragma unroll
     for (int e = 0; e < 16; ++e) x[e] = 0.0f;
   }
-  if constexpr (FMT == 2) {
-    if (which == 0) h64_rotate_threads(x, c16);  // rk8v4 keys: rotate each 64-dim group
+  if constexpr (FMT == 2 || FMT == 3) {
+    if (which == 0) h64_rotate_threads(x, c16);  // rk8v4 / rk4v4 keys: rotate each 64-dim group
   }
   uint32_t c[16];
   float amax = 0.0f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
-  if (FMT == 2 && which == 1) {  // rk8v4 values: 4-bit codes, one fp16 scale per 32 dims (2 threads)
+  if ((FMT == 2 || FMT == 3) && which == 1) {  // rk8v4 values: 4-bit codes, one fp16 scale per 32 dims (2 threads)
     amax = fmaxf(amax, __shfl_xor(amax, 1));
     const _Float16 s16 = static_cast<_Float16>(amax / 7.0f);
     const float sc = static_cast<float>(s16);
@@ -140,16 +140,20 @@ __global__ __launch_bounds__(kPage * D / 16) void append_page_kernel(AppendArgs 
     }
     if (mine && (c16 & 1) == 0)
       static_cast<_Float16 *>(a.v_scales)[page * (kPage * D / 32) + (run * (D / 32) + c16 / 2) * 16 + spos] = s16;
-  } else if constexpr (FMT == 0 || FMT == 2) {  // INT8, one fp16 scale per 64 dims: 4 neighbouring threads
+  } else if constexpr (FMT != 1) {  // INT8 (rk4v4: its scale), one fp16 scale per 64 dims: 4 neighbouring threads
     amax = fmaxf(amax, __shfl_xor(amax, 1));
     amax = fmaxf(amax, __shfl_xor(amax, 2));
     const _Float16 s16 = static_cast<_Float16>(amax / 127.0f);
     const float sc = static_cast<float>(s16);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      float r = 0.0f;
-      if (sc != 0.0f) r = fminf(fmaxf(rintf(x[e] / sc), -127.0f), 127.0f);
-      c[e] = static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu;
+      if constexpr (FMT == 3) {  // rk4v4 key: the level index
+        c[e] = rk4_index(sc != 0.0f ? x[e] / sc : 0.0f);
+      } else {
+        float r = 0.0f;
+        if (sc != 0.0f) r = fminf(fmaxf(rintf(x[e] / sc), -127.0f), 127.0f);
+        c[e] = static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu;
+      }
     }
     if (mine && (c16 & 3) == 0) {
       const int g = c16 / 4;
@@ -168,6 +172,22 @@ __global__ __launch_bounds__(kPage * D / 16) void append_page_kernel(AppendArgs 
 #pragma unroll
   for (int k = 0; k < 4; ++k) w[k] = c[4 * k] | (c[4 * k + 1] << 8) | (c[4 * k + 2] << 16) | (c[4 * k + 3] << 24);
 
+  if constexpr (FMT == 3) {
+    if (which == 0) {  // rk4v4 K: the 16 level indices of this slot are its own 8 bytes
+      if (mine) {
+        uint32_t kw[2];
+#pragma unroll
+        for (int hk = 0; hk < 2; ++hk) {
+          kw[hk] = 0;
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) kw[hk] |= (c[8 * hk + bb] << (8 * bb)) | (c[8 * hk + bb + 4] << (8 * bb + 4));
+        }
+        *reinterpret_cast<uint2 *>(a.k_codes + page * kPage * (D / 2) + k4_word_byte<D>(sl, 16 * c16)) =
+            make_uint2(kw[0], kw[1]);
+      }
+      return;
+    }
+  }
   if (which == 0) {  // K: the 16 dims of this slot are one 16-byte tile row
     if (mine) {
       const size_t off = (static_cast<size_t>(sl / 16) * NC + c16) * 256 + (sl % 16) * 16;
@@ -179,7 +199,7 @@ __global__ __launch_bounds__(kPage * D / 16) void append_page_kernel(AppendArgs 
   // thread) is dim d = (k/64)*16 + k%16, run r = (k/16)%4, whose byte 4j+i holds slot 16j+4r+i
   *reinterpret_cast<uint4 *>(vstage + sl * D + 16 * c16) = make_uint4(w[0], w[1], w[2], w[3]);
   __syncthreads();
-  if constexpr (FMT == 2) {
+  if constexpr (FMT == 2 || FMT == 3) {
     // rk8v4: 8-byte chunk k (one per thread) holds dim d = 16*dt + (k/2)%16 with
     // dt = 2*(k/128) + k%2, run r = (k/32)%4; its word w holds the slots 16*(2w + q/4) +
     // 4r + q%4 (q = 0..7), code q at bit 16*(q%2) + 4*(q/2)
@@ -262,6 +282,10 @@ hipError_t launch_append(int format, int head_dim, int src_dtype, const AppendAr
   KVQ_APPEND_CASE(2, 128, 1)
   KVQ_APPEND_CASE(2, 256, 0)
   KVQ_APPEND_CASE(2, 256, 1)
+  KVQ_APPEND_CASE(3, 128, 0)
+  KVQ_APPEND_CASE(3, 128, 1)
+  KVQ_APPEND_CASE(3, 256, 0)
+  KVQ_APPEND_CASE(3, 256, 1)
 #undef KVQ_APPEND_CASE
   return hipErrorInvalidValue;
 }

@@ -82,6 +82,25 @@ __device__ inline f16x8 v4_to_f16(uint32_t w) {
   return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// rk4v4 keys: one 32-bit word holds the 4-bit level indices of 8 dims of one key, byte b
+// = dim b (low nibble) and dim b + 4 (high nibble).  Each index becomes its level's INT8
+// code, biased by 128 (a 16-entry byte table read with two byte permutes and a per-byte
+// select on bit 3), and the biased bytes become exact f16 as in i8pair.
+__device__ inline uint32_t rk4_lut(uint32_t sel) {
+  // biased codes c + 128 of the levels -127 -96 -75 -58 -44 -31 -18 -6 6 18 31 44 58 75 96 127
+  constexpr uint32_t T0 = 0x46352001u, T1 = 0x7A6E6154u, T2 = 0xAC9F9286u, T3 = 0xFFE0CBBAu;
+  const uint32_t s7 = sel & 0x07070707u;
+  const uint32_t lo = __builtin_amdgcn_perm(T1, T0, s7), hi = __builtin_amdgcn_perm(T3, T2, s7);
+  const uint32_t m = __builtin_amdgcn_perm(0u, 0u, ((sel >> 3) & 0x01010101u) | 0x0C0C0C0Cu);  // 0x00 / 0xFF
+  return (hi & m) | (lo & ~m);
+}
+__device__ inline f16x8 k4_to_f16(uint32_t w) {
+  const uint32_t a = rk4_lut(w & 0x0F0F0F0Fu), b = rk4_lut((w >> 4) & 0x0F0F0F0Fu);
+  const f16x2 p0 = i8pair(a, 0x04010400u), p1 = i8pair(a, 0x04030402u);
+  const f16x2 p2 = i8pair(b, 0x04010400u), p3 = i8pair(b, 0x04030402u);
+  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 // x ~= hi + lo with hi = f16(x) rounded toward zero and lo = f16(x - hi): the
 // pair carries ~21 significant bits.
 __device__ inline void split_f16(float x0, float x1, f16x2 &hi, f16x2 &lo) {
@@ -151,9 +170,10 @@ template <int D, int FMT>
 struct PageRegs {
   static constexpr int G64 = D / 64, DPW = D / 64;  // dim tiles per wave = D/16/4
   static constexpr int KSN = (FMT == 1) ? 1 : (D / 128);
-  static constexpr int VN = (FMT == 2) ? DPW / 2 : DPW;
+  static constexpr int KN = (FMT == 3) ? G64 / 2 : G64;  // rk4v4: 16 bytes per pair of 64-dim groups
+  static constexpr int VN = (FMT >= 2) ? DPW / 2 : DPW;
   static constexpr int VSN = (FMT == 0) ? 2 : (FMT == 1 ? 4 : DPW);
-  uint4 k[G64];
+  uint4 k[KN];
   uint4 v[VN];
   uint4 ks[KSN];
   uint4 vs[VSN];
@@ -178,8 +198,14 @@ __device__ inline void load_k_part(PageRegs<D, FMT> &r, const AttnArgs &a, int p
   constexpr int G64 = D / 64, NCH = D / 16;
   const size_t pg = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pg_any));  // wave-uniform page
   const uint4 *kp = reinterpret_cast<const uint4 *>(a.k_codes + pg * kPage * D);
+  if constexpr (FMT == 3) {  // 4-bit keys: (key tile, group pair) units of 1 KiB, 16 bytes per lane
+    const uint4 *kp4 = reinterpret_cast<const uint4 *>(a.k_codes + pg * kPage * (D / 2));
 #pragma unroll
-  for (int cg = 0; cg < G64; ++cg) r.k[cg] = ld_stream(kp + (wave * NCH + 4 * cg) * 16 + lane);
+    for (int p = 0; p < G64 / 2; ++p) r.k[p] = ld_stream(kp4 + (wave * (G64 / 2) + p) * 64 + lane);
+  } else {
+#pragma unroll
+    for (int cg = 0; cg < G64; ++cg) r.k[cg] = ld_stream(kp + (wave * NCH + 4 * cg) * 16 + lane);
+  }
   if constexpr (FMT != 1) {
     const uint4 *ksp = reinterpret_cast<const uint4 *>(static_cast<const _Float16 *>(a.k_scales) + pg * D);
 #pragma unroll
@@ -194,7 +220,7 @@ template <int D, int FMT>
 __device__ inline void load_v_part(PageRegs<D, FMT> &r, const AttnArgs &a, int pg_any, int wave, int lane, int q4) {
   constexpr int G64 = D / 64, DPW = D / 64;
   const size_t pg = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pg_any));
-  if constexpr (FMT == 2) {  // 4-bit codes: tile pair p of the wave is one KiB, 16 bytes per lane
+  if constexpr (FMT >= 2) {  // 4-bit codes: tile pair p of the wave is one KiB, 16 bytes per lane
     const uint4 *vp = reinterpret_cast<const uint4 *>(a.v_codes + pg * kPage * (D / 2));
 #pragma unroll
     for (int p = 0; p < DPW / 2; ++p) r.v[p] = ld_stream(vp + (wave * (DPW / 2) + p) * 64 + lane);
@@ -253,7 +279,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   constexpr int G64 = D / 64, NCH = D / 16, DPW = D / 64;
   constexpr int QP = QLO ? 2 : 1;
   constexpr int KF = (FMT == 2) ? 0 : FMT;  // key code format: rk8v4 keys are INT8 group-64
-  static_assert(FMT != 2 || QLO != 0, "rotated queries need the lo part");
+  static_assert(FMT < 2 || QLO != 0, "rotated queries need the lo part");
   using SM = Smem<D, NT, NTEAM, QP>;
   constexpr int ROWS = SM::ROWS, PST = SM::PST;
   __shared__ uint4 qs[SM::QS];
@@ -358,8 +384,8 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 
   // ---- queries -> LDS in B-operand order: entry (nt, cg, hk, hl, lane) holds dims
   // 64cg + 16(lane/16) + 8hk + 0..7 of row 16nt + lane%16, as f16 hi (hl=0) or lo (hl=1).
-  if constexpr (FMT == 2) {
-    // rk8v4: the keys are stored rotated by H64/8 per 64-dim group, so each 64-dim group
+  if constexpr (FMT >= 2) {
+    // rk8v4, rk4v4: the keys are stored rotated by H64/8 per 64-dim group, so each 64-dim group
     // of a query row is rotated by the same matrix (butterflies in fp32, one thread per
     // (row, group)) before it is split into f16 hi + lo
     for (int task = tid; task < ROWS * G64; task += 256 * NTEAM) {
@@ -394,7 +420,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
       }
     }
   }
-  for (int e = tid; e < ((FMT == 2) ? 0 : NT * G64 * 2 * 64); e += 256 * NTEAM) {
+  for (int e = tid; e < ((FMT >= 2) ? 0 : NT * G64 * 2 * 64); e += 256 * NTEAM) {
     const int ln = e & 63, hk = (e >> 6) & 1, cg = (e >> 7) % G64, nt = (e >> 7) / G64;
     const int r = row0 + 16 * nt + (ln & 15);
     const int d0 = 64 * cg + 16 * (ln >> 4) + 8 * hk;
@@ -485,7 +511,13 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
       }
 #pragma unroll
       for (int hk = 0; hk < 2; ++hk) {
-        const f16x8 ka = hk ? codes_to_f16<KF>(pr.k[cg].z, pr.k[cg].w) : codes_to_f16<KF>(pr.k[cg].x, pr.k[cg].y);
+        f16x8 ka;
+        if constexpr (FMT == 3) {
+          const uint4 &kw = pr.k[cg / 2];
+          ka = k4_to_f16((cg & 1) ? (hk ? kw.w : kw.z) : (hk ? kw.y : kw.x));
+        } else {
+          ka = hk ? codes_to_f16<KF>(pr.k[cg].z, pr.k[cg].w) : codes_to_f16<KF>(pr.k[cg].x, pr.k[cg].y);
+        }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           acc[nt] = mfma16(ka, qc[hk][nt][0], acc[nt]);
@@ -495,7 +527,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
       if constexpr (QPF == 2) {
         if (cg + 2 < G64) read_q(qc, cg + 2);
       }
-      if constexpr (KF == 0) {  // fold each key's fp16 group scale, restart the group sum
+      if constexpr (KF != 1) {  // fold each key's fp16 group scale, restart the group sum
         const uint4 w = pr.ks[cg >> 1];
         float sk[4];
         f16x2_to_f32((cg & 1) ? w.z : w.x, sk[0], sk[1]);
@@ -536,7 +568,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     if constexpr (MASKED) {
       // slots at or past L may hold anything (never written): zero their V codes
       const int kbase = p * kPage + 4 * q4;  // key of (kt, i) is kbase + 16kt + i
-      if constexpr (FMT == 2) {
+      if constexpr (FMT >= 2) {
         // word ks holds keys kt = 2ks + q/4, i = q%4 (q = 0..7) at bit 16*(q%2) + 4*(q/2)
         uint32_t mw[2];
 #pragma unroll
@@ -616,7 +648,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     };
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      if constexpr (FMT == 2) {
+      if constexpr (FMT >= 2) {
         // one 32-dim scale group per pair of dim tiles, with its own B operands (built
         // one row tile at a time to keep few of them live)
 #pragma unroll
@@ -961,7 +993,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 template <int D, int NT, int FMT, int QDT>
 hipError_t split_one(const AttnArgs &a, hipStream_t s) {
   // fp32 queries need the hi+lo pair; bf16 queries are one exact f16, unless rotated (rk8v4)
-  constexpr int QLO = QDT == 0 ? 1 : (FMT == 2 ? 2 : 0);
+  constexpr int QLO = QDT == 0 ? 1 : (FMT >= 2 ? 2 : 0);
   const dim3 grid(a.n_splits, a.num_kv_heads, a.num_seqs);
   if (a.k_new != nullptr)
     hipLaunchKernelGGL((attn_split_kernel<D, NT, FMT, QLO, kTeams, 1>), grid, dim3(256 * kTeams), 0, s, a);
@@ -972,7 +1004,7 @@ hipError_t split_one(const AttnArgs &a, hipStream_t s) {
 
 template <int D, int FMT, int QDT>
 hipError_t prefill_one(const AttnArgs &a, hipStream_t s) {
-  constexpr int QLO = QDT == 0 ? 1 : (FMT == 2 ? 2 : 0);
+  constexpr int QLO = QDT == 0 ? 1 : (FMT >= 2 ? 2 : 0);
   const dim3 grid(a.n_splits, a.num_kv_heads * a.row_blocks, a.num_seqs);
   hipLaunchKernelGGL((attn_split_kernel<D, kPrefillNT, FMT, QLO, kPrefillTeams, 2>), grid, dim3(256 * kPrefillTeams),
                      0, s, a);
@@ -993,7 +1025,7 @@ hipError_t launch_attn_split(int format, int head_dim, int q_dtype, const AttnAr
   if (head_dim == DD && nt == NTT && format == F && q_dtype == Q) return split_one<DD, NTT, F, Q>(a, s);
 #define KVQ_SPLIT_DQ(DD, NTT) \
   KVQ_SPLIT_CASE(DD, NTT, 0, 0) KVQ_SPLIT_CASE(DD, NTT, 0, 1) KVQ_SPLIT_CASE(DD, NTT, 1, 0) KVQ_SPLIT_CASE(DD, NTT, 1, 1) \
-  KVQ_SPLIT_CASE(DD, NTT, 2, 0) KVQ_SPLIT_CASE(DD, NTT, 2, 1)
+  KVQ_SPLIT_CASE(DD, NTT, 2, 0) KVQ_SPLIT_CASE(DD, NTT, 2, 1) KVQ_SPLIT_CASE(DD, NTT, 3, 0) KVQ_SPLIT_CASE(DD, NTT, 3, 1)
   KVQ_SPLIT_DQ(128, 1)
   KVQ_SPLIT_DQ(128, 2)
   KVQ_SPLIT_DQ(256, 1)
@@ -1009,6 +1041,7 @@ hipError_t launch_attn_prefill(int format, int head_dim, int q_dtype, const Attn
   KVQ_PF_CASE(128, 0, 0) KVQ_PF_CASE(128, 0, 1) KVQ_PF_CASE(128, 1, 0) KVQ_PF_CASE(128, 1, 1)
   KVQ_PF_CASE(256, 0, 0) KVQ_PF_CASE(256, 0, 1) KVQ_PF_CASE(256, 1, 0) KVQ_PF_CASE(256, 1, 1)
   KVQ_PF_CASE(128, 2, 0) KVQ_PF_CASE(128, 2, 1) KVQ_PF_CASE(256, 2, 0) KVQ_PF_CASE(256, 2, 1)
+  KVQ_PF_CASE(128, 3, 0) KVQ_PF_CASE(128, 3, 1) KVQ_PF_CASE(256, 3, 0) KVQ_PF_CASE(256, 3, 1)
 #undef KVQ_PF_CASE
   return hipErrorInvalidValue;
 }

@@ -15,7 +15,7 @@ bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 int check_cache(const kvq_cache_t *c) {
   if (!c) return KVQ_ERR_INVALID_ARG;
-  if (c->format != KVQ_INT8_G64 && c->format != KVQ_FP8_E4M3_ROW && c->format != KVQ_RK8V4) return KVQ_ERR_INVALID_ARG;
+  if (c->format < KVQ_INT8_G64 || c->format > KVQ_RK4V4) return KVQ_ERR_INVALID_ARG;
   if (c->num_blocks < 1 || c->num_kv_heads < 1 || c->block_size < 1) return KVQ_ERR_INVALID_ARG;
   if (c->block_size != kvq::kPage) return KVQ_ERR_UNSUPPORTED;
   if (c->head_dim != 128 && c->head_dim != 256) return KVQ_ERR_UNSUPPORTED;

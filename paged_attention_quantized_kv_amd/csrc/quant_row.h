@@ -80,6 +80,28 @@ __device__ inline void v4_place(int s, int d, size_t &word, int &shift) {
   shift = 16 * (k % 2) + 4 * (k / 2);
 }
 
+// rk4v4 keys (NInfer-3090 README, "Lloyd-Max 4-bit keys (rk4v4)"): the INT8 codes of
+// the 16 Lloyd-Max levels of a unit Gaussian, rint(127 * L_i / L_15), ascending; a
+// rotated coordinate u = y / scale (the INT8 group scale) takes the level whose code is
+// nearest, ties to the lower one: its index is the count of midpoints below u.
+__device__ inline uint32_t rk4_index(float u) {
+  constexpr float kMid[15] = {-111.5f, -85.5f, -66.5f, -51.0f, -37.5f, -24.5f, -12.0f, 0.0f,
+                              12.0f,   24.5f,  37.5f,  51.0f,  66.5f,  85.5f,  111.5f};
+  uint32_t k = 0;
+#pragma unroll
+  for (int m = 0; m < 15; ++m) k += (kMid[m] < u) ? 1u : 0u;
+  return k;
+}
+
+// rk4v4 keys: byte offset of the 32-bit word holding dims 8*(d/8) .. +7 of slot s in a
+// page of 64*D/2 bytes (see kvq.h); byte b of the word holds dim b (low nibble) and
+// dim b + 4 (high nibble) of those 8.
+template <int D>
+__device__ inline size_t k4_word_byte(int s, int d) {
+  const size_t unit = static_cast<size_t>((s / 16) * (D / 128) + d / 128) * 64 + ((d % 64) / 16) * 16 + (s % 16);
+  return unit * 16 + ((d / 64) % 2) * 8 + ((d % 16) / 8) * 4;
+}
+
 // Row t of sequence b, KV head h, K (which=0) or V (which=1) of the
 // [B][n_new][Hkv][D] source: this lane's D/64 consecutive elements, widened.
 template <int D, int SRC>
@@ -104,15 +126,43 @@ __device__ inline void store_row(const AppendArgs &a, const float (&xin)[D / 64]
   float x[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) x[e] = xin[e];
-  if constexpr (FMT == 2) {
+  if constexpr (FMT == 2 || FMT == 3) {
     if (which == 0) h64_rotate_lanes<E>(x, lane);
   }
 
   const size_t page = static_cast<size_t>(blk) * a.num_kv_heads + h;
   uint32_t c[E];
 
-  if constexpr (FMT == 2) {
-    if (which == 1) {  // rk8v4 values: signed 4-bit codes, one fp16 scale per 32 dims
+  if constexpr (FMT == 3) {
+    if (which == 0) {  // rk4v4 keys: level indices over the INT8 group scale of the rotated row
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(x[e]));
+#pragma unroll
+      for (int off = 1; off < LPG; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+      const _Float16 s16 = static_cast<_Float16>(amax / 127.0f);
+      const float s = static_cast<float>(s16);
+      // this lane's nibbles in the word of its 8-dim block; the 8/E lanes of a block
+      // combine them and the first one writes the word (a row owns its key bytes)
+      uint32_t wv = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int d = lane * E + e;
+        wv |= rk4_index(s != 0.0f ? x[e] / s : 0.0f) << (8 * (d % 4) + 4 * ((d % 8) / 4));
+      }
+#pragma unroll
+      for (int off = 1; off < 8 / E; off <<= 1) wv |= __shfl_xor(wv, off);
+      if ((lane % (8 / E)) == 0)
+        *reinterpret_cast<uint32_t *>(a.k_codes + page * kPage * (D / 2) + k4_word_byte<D>(slot, lane * E)) = wv;
+      if ((lane % LPG) == 0) {
+        const int g = lane / LPG;
+        static_cast<_Float16 *>(a.k_scales)[page * D + ((run * 4 + slot / 16) * E + g) * 4 + slot % 4] = s16;
+      }
+      return;
+    }
+  }
+  if constexpr (FMT == 2 || FMT == 3) {
+    if (which == 1) {  // rk8v4 (and rk4v4) values: signed 4-bit codes, one fp16 scale per 32 dims
       constexpr int LPG32 = 32 / E;
       float amax = 0.0f;
 #pragma unroll

@@ -28,7 +28,7 @@ def new_cache(K, w: S.Workload, device, poison: bool = True):
     if poison:
         cache.k_codes.fill_(POISON_CODE)
         cache.v_codes.fill_(POISON_CODE)
-        if s.fmt in (S.FMT_INT8_G64, S.FMT_RK8V4):  # fp16 scales
+        if s.fmt in (S.FMT_INT8_G64, S.FMT_RK8V4, S.FMT_RK4V4):  # fp16 scales
             cache.k_scales.view(torch.int16).fill_(POISON_F16)
             cache.v_scales.view(torch.int16).fill_(POISON_F16)
         else:
@@ -68,7 +68,7 @@ def fill_gpu(K, w: S.Workload, cache, device, chunk: int = 8192, decode_rows: bo
 def oracle_pool(O, w: S.Workload):
     s = w.shape
     pool = O.Pool(s.fmt, w.num_blocks, s.Hkv, s.D, fill=POISON_CODE)
-    if s.fmt in (S.FMT_INT8_G64, S.FMT_RK8V4):
+    if s.fmt in (S.FMT_INT8_G64, S.FMT_RK8V4, S.FMT_RK4V4):
         pool.k_scales[:] = POISON_F16
         pool.v_scales[:] = POISON_F16
     else:

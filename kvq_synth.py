@@ -18,6 +18,7 @@ tokens; shapes after NInfer-4090 README "What this fork changes", d256-h24-kv4):
   mtp128k_rk8v4  mtp128k's data in the rk8v4 format (rotated INT8 keys,
               4-bit group-32 values)
   mtp128k_rk4v4  the same in the rk4v4 format (4-bit Lloyd-Max keys)
+  mtp128k_bf16, full256k_bf16  the same data in the BF16 reference format
 
 Every pool starts filled with poison (code bytes 0x7F, NaN scales), so a read of
 a slot that was never appended shows up as NaN in the output.  Block-table
@@ -36,12 +37,13 @@ FMT_INT8_G64 = 0
 FMT_FP8_ROW = 1
 FMT_RK8V4 = 2
 FMT_RK4V4 = 3
+FMT_BF16 = 4
 SRC_F32 = 0
 SRC_BF16 = 1
 
 CONFIG_NAMES = ["tiny", "qwen32k", "mtp128k", "c8", "full256k_int8", "full256k_fp8"]
 _SEED_INDEX = {"tiny": 0, "qwen32k": 1, "mtp128k": 2, "c8": 3, "full256k_int8": 4, "full256k_fp8": 4,
-               "mtp128k_rk8v4": 2, "mtp128k_rk4v4": 2}
+               "mtp128k_rk8v4": 2, "mtp128k_rk4v4": 2, "mtp128k_bf16": 2, "full256k_bf16": 4}
 
 
 @dataclasses.dataclass
@@ -74,6 +76,10 @@ def shape(name: str, **over) -> Shape:
         s = Shape(name, 1, 1, 24, 4, 256, [262144], SRC_BF16, FMT_INT8_G64, True, chunk=4096)
     elif name == "mtp128k_rk8v4":
         s = Shape(name, 1, 4, 24, 4, 256, [131072], SRC_BF16, FMT_RK8V4, True)
+    elif name == "mtp128k_bf16":
+        s = Shape(name, 1, 4, 24, 4, 256, [131072], SRC_BF16, FMT_BF16, True)
+    elif name == "full256k_bf16":
+        s = Shape(name, 1, 1, 24, 4, 256, [262144], SRC_BF16, FMT_BF16, True)
     elif name == "mtp128k_rk4v4":
         s = Shape(name, 1, 4, 24, 4, 256, [131072], SRC_BF16, FMT_RK4V4, True)
     elif name == "full256k_fp8":
@@ -129,6 +135,8 @@ class Workload:
         s = self.shape
         if s.fmt == FMT_RK8V4:  # INT8 keys with fp16 group-64 scales, 4-bit values with fp16 group-32 scales
             per_tok_head = (s.D + 2 * (s.D // 64)) + (s.D // 2 + 2 * (s.D // 32))
+        elif s.fmt == FMT_BF16:  # two bytes per element, no scales
+            per_tok_head = 2 * 2 * s.D
         elif s.fmt == FMT_RK4V4:  # 4-bit keys with fp16 group-64 scales, rk8v4 values
             per_tok_head = (s.D // 2 + 2 * (s.D // 64)) + (s.D // 2 + 2 * (s.D // 32))
         else:

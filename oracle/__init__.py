@@ -26,6 +26,7 @@ FMT_INT8_G64 = 0
 FMT_FP8_ROW = 1
 FMT_RK8V4 = 2
 FMT_RK4V4 = 3
+FMT_BF16 = 4
 SRC_F32 = 0
 SRC_BF16 = 1
 
@@ -58,7 +59,7 @@ def lib():
             L = C.CDLL(LIB_PATH)
         vp, i64, i32 = C.c_void_p, C.c_int64, C.c_int
         for name in ("orc_f32_to_f16_n", "orc_f16_to_f32_n", "orc_bf16_to_f32_n",
-                     "orc_f32_to_e4m3fn_n", "orc_e4m3fn_to_f32_n"):
+                     "orc_f32_to_e4m3fn_n", "orc_e4m3fn_to_f32_n", "orc_f32_to_bf16_n"):
             getattr(L, name).argtypes = [vp, vp, i64]
             getattr(L, name).restype = None
         L.orc_quant_rows.argtypes = [i32, vp, i64, i32, vp, vp]
@@ -120,6 +121,13 @@ def bf16_bits_to_f32(b) -> np.ndarray:
     b = np.ascontiguousarray(b, dtype=np.uint16)
     y = np.empty(b.shape, np.float32)
     lib().orc_bf16_to_f32_n(_ptr(b), _ptr(y), b.size)
+    return y
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty(x.shape, np.uint16)
+    lib().orc_f32_to_bf16_n(_ptr(x), _ptr(y), x.size)
     return y
 
 
@@ -227,6 +235,12 @@ class Pool:
     def __init__(self, fmt: int, num_blocks: int, num_kv_heads: int, head_dim: int, fill: int = 0):
         self.fmt, self.num_blocks, self.num_kv_heads, self.head_dim = fmt, num_blocks, num_kv_heads, head_dim
         n = num_blocks * num_kv_heads * 64
+        if fmt == FMT_BF16:  # two bytes per element, no scales (one-element placeholders)
+            self.k_codes = np.full(n * head_dim * 2, fill, np.uint8)
+            self.v_codes = np.full(n * head_dim * 2, fill, np.uint8)
+            self.k_scales = np.zeros(1, np.uint16)
+            self.v_scales = np.zeros(1, np.uint16)
+            return
         self.k_codes = np.full(n * head_dim // (2 if fmt == FMT_RK4V4 else 1), fill, np.uint8)
         self.v_codes = np.full(n * head_dim // (2 if fmt in (FMT_RK8V4, FMT_RK4V4) else 1), fill, np.uint8)
         if fmt in (FMT_RK8V4, FMT_RK4V4):

@@ -81,6 +81,16 @@ float orc_bf16_to_f32(uint16_t b) {
   return (float)(s ? -v : v);
 }
 
+/* bfloat16 from binary32: keep the top 16 bits, rounding the lower 16 to nearest, ties
+ * to even (a carry may bump the exponent, up to infinity); NaN gives a quiet NaN. */
+uint16_t orc_f32_to_bf16_rne(float f) {
+  uint32_t x = f32_bits(f);
+  if ((x & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((x >> 16) | 0x0040u);
+  uint32_t hi = x >> 16, rest = x & 0xFFFFu;
+  if (rest > 0x8000u || (rest == 0x8000u && (hi & 1u))) hi += 1u;
+  return (uint16_t)hi;
+}
+
 /* OCP FP8 E4M3FN: 1 sign, 4 exponent (bias 7), 3 fraction bits, no
  * infinities; S.1111.111 is NaN; subnormals are multiples of 2^-9; the
  * largest finite magnitude is 448 (code 0x7E). */
@@ -398,6 +408,12 @@ int orc_append(const orc_pool *p, const void *k_new, const void *v_new, int src_
           int64_t row = (((int64_t)b * n_new + t) * H + h) * D;
           for (int d = 0; d < D; ++d) x[d] = load_src(src, src_dtype, row + d);
           int64_t pg = page_index(p, block, h);
+          if (p->format == ORC_FMT_BF16) {
+            uint16_t *page16 = (uint16_t *)pool_codes + pg * 64 * D;
+            for (int d = 0; d < D; ++d)
+              page16[which ? orc_v_byte(slot, d, D) : orc_k_byte(slot, d, D)] = orc_f32_to_bf16_rne(x[d]);
+            continue;
+          }
           if ((p->format == ORC_FMT_RK8V4 || p->format == ORC_FMT_RK4V4) && which == 1) {
             uint8_t *page4 = pool_codes + pg * 64 * (D / 2);
             orc_quant_int4_g32(x, D, (int8_t *)codes, s16);
@@ -457,6 +473,10 @@ int orc_append(const orc_pool *p, const void *k_new, const void *v_new, int src_
 double orc_dequant(const orc_pool *p, int which, int block, int kvh, int slot, int d) {
   const int D = p->head_dim;
   int64_t pg = page_index(p, block, kvh);
+  if (p->format == ORC_FMT_BF16) {
+    const uint16_t *page16 = (const uint16_t *)(which ? p->v_codes : p->k_codes) + pg * 64 * D;
+    return (double)orc_bf16_to_f32(page16[which ? orc_v_byte(slot, d, D) : orc_k_byte(slot, d, D)]);
+  }
   if (p->format == ORC_FMT_RK4V4 && which == 0) {
     const uint8_t *page4 = p->k_codes + pg * 64 * (D / 2);
     int64_t bit = orc_k4_bit(slot, d, D);
@@ -631,4 +651,7 @@ void orc_quant_int4_rows(const float *x, int64_t n, int D, int8_t *codes, uint16
 /* rk4v4 key rows: level indices [n][D] (0..15) and scales [n][D/64] */
 void orc_quant_rk4v4_rows(const float *x, int64_t n, int D, uint8_t *idx, uint16_t *scales) {
   for (int64_t r = 0; r < n; ++r) orc_quant_rk4v4_k(x + r * D, D, idx + r * D, scales + r * (D / 64));
+}
+void orc_f32_to_bf16_n(const float *x, uint16_t *y, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) y[i] = orc_f32_to_bf16_rne(x[i]);
 }

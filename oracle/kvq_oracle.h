@@ -34,6 +34,9 @@
  *    rint(127 * L_i / L_15), the group scale is the INT8 one (fp16(absmax / 127)),
  *    and a coordinate takes the level whose code is nearest to x / scale (a tie
  *    goes to the lower level).
+ *  - BF16 KV (the unquantized reference format, 65,536 B/token on the 27B:
+ *    NInfer-3090 README, "Choosing a KV format"): each K and V element stored
+ *    as bfloat16, round to nearest even from the source, no scales.
  *  - Quantization happens when rows are appended, in the append op:
  *    NInfer-3090 README, intro and "RotorQuant KV (rk8v4)".
  *  - Each decode step reads the whole cache: NInfer-3090 README, "Choosing a
@@ -52,7 +55,7 @@
 extern "C" {
 #endif
 
-enum { ORC_FMT_INT8_G64 = 0, ORC_FMT_FP8_ROW = 1, ORC_FMT_RK8V4 = 2, ORC_FMT_RK4V4 = 3 };
+enum { ORC_FMT_INT8_G64 = 0, ORC_FMT_FP8_ROW = 1, ORC_FMT_RK8V4 = 2, ORC_FMT_RK4V4 = 3, ORC_FMT_BF16 = 4 };
 enum { ORC_SRC_F32 = 0, ORC_SRC_BF16 = 1 };
 
 /* Scalar conversions, written from the IEEE-754 binary16, bfloat16 and OCP
@@ -60,6 +63,7 @@ enum { ORC_SRC_F32 = 0, ORC_SRC_BF16 = 1 };
 uint16_t orc_f32_to_f16_rne(float f);
 float orc_f16_to_f32(uint16_t h);
 float orc_bf16_to_f32(uint16_t b);
+uint16_t orc_f32_to_bf16_rne(float f); /* RNE; NaN stays NaN */
 uint8_t orc_f32_to_e4m3fn(float f); /* RNE, saturate to +-448, NaN -> 0x7F */
 float orc_e4m3fn_to_f32(uint8_t c);
 
@@ -83,7 +87,8 @@ void orc_quant_rk4v4_k(const float *x, int D, uint8_t *idx, uint16_t *scales);
 /* One value row of D values -> D signed 4-bit codes (-7..7, one per int8) and D/32 fp16 scales. */
 void orc_quant_int4_g32(const float *x, int D, int8_t *codes, uint16_t *scales);
 
-/* Byte offset of (token slot s, dim d) inside one (block, kv head) page. */
+/* Byte offset of (token slot s, dim d) inside one (block, kv head) page (1-byte codes;
+ * the BF16 format stores element (s, d) at twice this offset). */
 int64_t orc_k_byte(int s, int d, int D);
 int64_t orc_v_byte(int s, int d, int D);
 /* rk8v4 values: bit offset of the 4-bit code of (slot s, dim d) inside a page of 64*D/2 bytes. */
@@ -137,6 +142,7 @@ void orc_f16_to_f32_n(const uint16_t *x, float *y, int64_t n);
 void orc_bf16_to_f32_n(const uint16_t *x, float *y, int64_t n);
 void orc_f32_to_e4m3fn_n(const float *x, uint8_t *y, int64_t n);
 void orc_e4m3fn_to_f32_n(const uint8_t *x, float *y, int64_t n);
+void orc_f32_to_bf16_n(const float *x, uint16_t *y, int64_t n);
 void orc_quant_rows(int fmt, const float *x, int64_t n, int D, uint8_t *codes, void *scales);
 void orc_h64_rotate_n(const float *x, float *y, int64_t ngroups);
 void orc_quant_int4_rows(const float *x, int64_t n, int D, int8_t *codes, uint16_t *scales);

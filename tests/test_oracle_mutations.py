@@ -14,7 +14,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "kvq_oracle.c")
 PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_attention.py", "tests/test_oracle_rk8v4.py",
-        "tests/test_oracle_rk4v4.py"]
+        "tests/test_oracle_rk4v4.py", "tests/test_oracle_bf16.py"]
 
 # (name, original text, planted mistake)
 MUTATIONS = [
@@ -55,6 +55,10 @@ MUTATIONS = [
     ("rk4_scale_divisor", "uint16_t h = orc_f32_to_f16_rne(a / 127.0f);\n    float sc = orc_f16_to_f32(h);",
      "uint16_t h = orc_f32_to_f16_rne(a / 96.0f);\n    float sc = orc_f16_to_f32(h);"),
     ("k4_nibble_order", "return byte * 8 + 4 * ((d % 8) / 4);", "return byte * 8 + 4 * (d % 2);"),
+    ("bf16_ties_away", "if (rest > 0x8000u || (rest == 0x8000u && (hi & 1u))) hi += 1u;", "if (rest >= 0x8000u) hi += 1u;"),
+    ("bf16_truncates", "if (rest > 0x8000u || (rest == 0x8000u && (hi & 1u))) hi += 1u;", "(void)rest;"),
+    ("bf16_k_in_v_order", "page16[which ? orc_v_byte(slot, d, D) : orc_k_byte(slot, d, D)] = orc_f32_to_bf16_rne(x[d]);",
+     "page16[orc_v_byte(slot, d, D)] = orc_f32_to_bf16_rne(x[d]);"),
 ]
 
 

@@ -34,7 +34,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
 HEADLINE = "mtp128k"
-DEPTHS = ["qwen32k", "mtp128k", "full256k_int8", "full256k_fp8", "mtp128k_rk8v4", "mtp128k_rk4v4"]
+DEPTHS = ["qwen32k", "mtp128k", "full256k_int8", "full256k_fp8", "mtp128k_rk8v4", "mtp128k_rk4v4", "mtp128k_bf16",
+          "full256k_bf16"]
 SETTLE_S = 0.2  # seconds of untimed back-to-back steps before the warmup steps
 FLUSH_BYTES = 1.5 * 2 ** 30  # bytes read between two reads of one pool copy (> 256 MB MALL)
 KERNEL_SOURCES = ("internal.h", "quant_row.h", "attn.hip")  # what the split kernel is built from
@@ -331,7 +332,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=HEADLINE, choices=["tiny", "qwen32k", "mtp128k", "mtp128k_rk8v4", "mtp128k_rk4v4", "c8", "full256k_int8",
+    ap.add_argument("--workload", default=HEADLINE, choices=["tiny", "qwen32k", "mtp128k", "mtp128k_rk8v4", "mtp128k_rk4v4", "mtp128k_bf16", "full256k_bf16", "c8",
+                                                             "full256k_int8",
                                                              "full256k_fp8"])
     ap.add_argument("--headline-only", action="store_true", help="skip the other depths")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -416,7 +418,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: B={shp.B} T={shp.T} Hq={shp.Hq} Hkv={shp.Hkv} D={shp.D} "
                                f"L={shp.lens[0] if shp.B == 1 else 'ragged'} page=64 "
-                               f"{ {0: 'INT8 g64', 1: 'FP8 E4M3 row', 2: 'rk8v4', 3: 'rk4v4'}[shp.fmt]} KV",
+                               f"{ {0: 'INT8 g64', 1: 'FP8 E4M3 row', 2: 'rk8v4', 3: 'rk4v4', 4: 'BF16'}[shp.fmt]} KV",
                    "global_batch": shp.B * shp.T, "seq_len": shp.lens[0] if shp.B == 1 else max(shp.lens),
                    "step": "paged_decode_step: append of the T new rows + paged decode attention (2 kernels)",
                    "parallelism": "single GPU"},

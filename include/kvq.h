@@ -44,6 +44,10 @@
  *                     KVQ_INT8_G64 group scale fp16_rne(absmax / 127) of the rotated
  *                     group; index = the level whose code is nearest to y / scale
  *                     (fp32), ties to the lower level.
+ *   KVQ_BF16_KV       the unquantized reference: each K and V element as bfloat16,
+ *                     round to nearest even from the source, no scales (65,536
+ *                     B/token on the 27B; NInfer-3090 README, "Choosing a KV
+ *                     format").  Attention reads the elements as they are.
  *   A group (or row) whose absmax is 0 stores scale 0 and all-zero codes.
  *
  * Conventions for every call:
@@ -86,7 +90,7 @@ enum {
   KVQ_ERR_LAUNCH = -5       /* the HIP runtime refused a launch (no device, bad stream, ...) */
 };
 
-typedef enum { KVQ_INT8_G64 = 0, KVQ_FP8_E4M3_ROW = 1, KVQ_RK8V4 = 2, KVQ_RK4V4 = 3 } kvq_format_t;
+typedef enum { KVQ_INT8_G64 = 0, KVQ_FP8_E4M3_ROW = 1, KVQ_RK8V4 = 2, KVQ_RK4V4 = 3, KVQ_BF16_KV = 4 } kvq_format_t;
 typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype_t;
 
 /*
@@ -98,6 +102,8 @@ typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype_t;
  *                      E4M3FN bytes (FP8_E4M3_ROW).  RK8V4: k_codes as INT8_G64;
  *                      v_codes 64 * head_dim / 2 bytes per page (4-bit codes).
  *                      RK4V4: k_codes and v_codes 64 * head_dim / 2 bytes per page.
+ *                      BF16_KV: k_codes and v_codes 64 * head_dim bf16 per page;
+ *                      k_scales and v_scales are not used (may be NULL).
  *   k_scales, v_scales INT8_G64: fp16, 64 * head_dim/64 per page, page p at
  *                      element p * head_dim;  FP8_E4M3_ROW: fp32, 64 per page,
  *                      page p at element p * 64.  RK8V4, RK4V4: k_scales as INT8_G64;
@@ -119,6 +125,7 @@ typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype_t;
  *           one dim; the two 16-dim tiles of a 32-dim pair sit side by side)
  *   RK8V4 V scale of (s, 32-dim group g)  element (run(s) * (D/32) + g) * 16 + pos(s)
  *   RK4V4 V codes and scales, K scales     as RK8V4
+ *   BF16_KV K or V element (s, d)  the INT8 K or V byte offset above, in bf16 elements
  *   RK4V4 K index of (s, d)  4 bits at bit 8*(d%4) + 4*((d%8)/4) of the little-endian
  *           32-bit word at byte u * 16 + ((d/64)%2) * 8 + ((d%16)/8) * 4, with
  *           u = ((s/16) * (D/128) + d/128) * 64 + ((d%64)/16) * 16 + s%16

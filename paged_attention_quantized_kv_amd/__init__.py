@@ -19,6 +19,7 @@ INT8_G64 = 0
 FP8_E4M3_ROW = 1
 RK8V4 = 2
 RK4V4 = 3
+BF16_KV = 4
 F32 = 0
 BF16 = 1
 PAGE = 64
@@ -108,7 +109,12 @@ class Cache:
                  k_codes=None, v_codes=None, k_scales=None, v_scales=None):
         self.format, self.num_blocks, self.num_kv_heads, self.head_dim = fmt, num_blocks, num_kv_heads, head_dim
         n = num_blocks * num_kv_heads * PAGE
-        if k_codes is None:
+        if k_codes is None and fmt == BF16_KV:  # bf16 elements, no scales (small placeholders)
+            k_codes = torch.empty(n * head_dim, dtype=torch.bfloat16, device=device)
+            v_codes = torch.empty(n * head_dim, dtype=torch.bfloat16, device=device)
+            k_scales = torch.zeros(8, dtype=torch.float16, device=device)
+            v_scales = torch.zeros(8, dtype=torch.float16, device=device)
+        elif k_codes is None:
             k_codes = torch.empty(n * head_dim // (2 if fmt == RK4V4 else 1), dtype=torch.uint8, device=device)
             v_codes = torch.empty(n * head_dim // (2 if fmt in (RK8V4, RK4V4) else 1), dtype=torch.uint8, device=device)
             if fmt in (RK8V4, RK4V4):  # fp16 group-64 key scales; 4-bit values with one fp16 scale per 32 dims

@@ -70,7 +70,7 @@ template <int FMT, int D, int SRC>
 __global__ __launch_bounds__(kPage * D / 16) void append_page_kernel(AppendArgs a) {
   constexpr int NC = D / 16;  // threads per slot
   constexpr int G64 = D / 64;
-  __shared__ __align__(16) uint8_t vstage[kPage * D];  // V codes, row-major [slot][dim]
+  __shared__ __align__(16) uint8_t vstage[kPage * D * (FMT == 4 ? 2 : 1)];  // V codes, row-major [slot][dim]
   const int tid = threadIdx.x, sl = tid / NC, c16 = tid % NC;
   const int h = blockIdx.y, which = blockIdx.z & 1, b = blockIdx.z >> 1;
   const long pos0 = a.start_pos[b];
@@ -120,6 +120,49 @@ __global__ __launch_bounds__(kPage * D / 16) void append_page_kernel(AppendArgs 
   } else {
 #pragma unroll
     for (int e = 0; e < 16; ++e) x[e] = 0.0f;
+  }
+  if constexpr (FMT == 4) {  // BF16: no quantization, the INT8 element order at two bytes each
+    uint32_t hw[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) hw[k] = f32_to_bf16_rne(x[2 * k]) | (f32_to_bf16_rne(x[2 * k + 1]) << 16);
+    if (which == 0) {  // the 16 dims of this slot: one 32-byte tile row
+      if (mine) {
+        uint4 *dst = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.k_codes) + page * kPage * D +
+                                               (static_cast<size_t>(sl / 16) * NC + c16) * 256 + (sl % 16) * 16);
+        dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        dst[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+      }
+      return;
+    }
+    uint16_t *vst = reinterpret_cast<uint16_t *>(vstage);
+    uint4 *vrow = reinterpret_cast<uint4 *>(vst + sl * D + 16 * c16);
+    vrow[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    vrow[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+    __syncthreads();
+    // run k (one per thread): dim d = (k/64)*16 + k%16, run r = (k/16)%4; element 4j+i is slot 16j+4r+i
+    const int k = tid, d = (k / 64) * 16 + (k % 16), r = (k / 16) % 4;
+    uint16_t *dst = reinterpret_cast<uint16_t *>(a.v_codes) + page * kPage * D + static_cast<size_t>(k) * 16;
+    if (full) {
+      uint32_t v[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const int s0 = 16 * j + 4 * r + i;
+          v[2 * j + i / 2] = static_cast<uint32_t>(vst[s0 * D + d]) | (static_cast<uint32_t>(vst[(s0 + 1) * D + d]) << 16);
+        }
+      reinterpret_cast<uint4 *>(dst)[0] = make_uint4(v[0], v[1], v[2], v[3]);
+      reinterpret_cast<uint4 *>(dst)[1] = make_uint4(v[4], v[5], v[6], v[7]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int sj = 16 * j + 4 * r + i;
+          if (sj >= s_lo && sj < s_hi) dst[4 * j + i] = vst[sj * D + d];
+        }
+    }
+    return;
   }
   if constexpr (FMT == 2 || FMT == 3) {
     if (which == 0) h64_rotate_threads(x, c16);  // rk8v4 / rk4v4 keys: rotate each 64-dim group
@@ -286,6 +329,10 @@ hipError_t launch_append(int format, int head_dim, int src_dtype, const AppendAr
   KVQ_APPEND_CASE(3, 128, 1)
   KVQ_APPEND_CASE(3, 256, 0)
   KVQ_APPEND_CASE(3, 256, 1)
+  KVQ_APPEND_CASE(4, 128, 0)
+  KVQ_APPEND_CASE(4, 128, 1)
+  KVQ_APPEND_CASE(4, 256, 0)
+  KVQ_APPEND_CASE(4, 256, 1)
 #undef KVQ_APPEND_CASE
   return hipErrorInvalidValue;
 }

@@ -33,10 +33,26 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 
 __device__ inline f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// the BF16 format: bf16 operands, taken straight from the pool
+__device__ inline f32x4 mfma16_bf(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+// x = hi + mid + lo exactly enough for the BF16 format's P (24 significant bits): hi and
+// mid are x and its residual cut to bf16 (exact residuals), lo the last residual rounded.
+// Returns the bf16 pairs of two values x0, x1 packed per term.
+__device__ inline void split_bf16x3(float x0, float x1, uint32_t &hi, uint32_t &mid, uint32_t &lo) {
+  const float h0 = __uint_as_float(__float_as_uint(x0) & 0xFFFF0000u), h1 = __uint_as_float(__float_as_uint(x1) & 0xFFFF0000u);
+  const float r0 = x0 - h0, r1 = x1 - h1;
+  const float m0 = __uint_as_float(__float_as_uint(r0) & 0xFFFF0000u), m1 = __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
+  hi = __builtin_amdgcn_perm(__float_as_uint(h1), __float_as_uint(h0), 0x07060302u);
+  mid = __builtin_amdgcn_perm(__float_as_uint(m1), __float_as_uint(m0), 0x07060302u);
+  lo = f32_to_bf16_rne(r0 - m0) | (f32_to_bf16_rne(r1 - m1) << 16);
 }
 
 // Two signed int8 bytes of x (selected by `sel` after the sign flip) -> two
@@ -169,10 +185,11 @@ constexpr float kLazy = 8.0f;
 template <int D, int FMT>
 struct PageRegs {
   static constexpr int G64 = D / 64, DPW = D / 64;  // dim tiles per wave = D/16/4
-  static constexpr int KSN = (FMT == 1) ? 1 : (D / 128);
-  static constexpr int KN = (FMT == 3) ? G64 / 2 : G64;  // rk4v4: 16 bytes per pair of 64-dim groups
-  static constexpr int VN = (FMT >= 2) ? DPW / 2 : DPW;
-  static constexpr int VSN = (FMT == 0) ? 2 : (FMT == 1 ? 4 : DPW);
+  // BF16 (FMT 4): 32 bytes of K per (key, 16 dims) and of V per (dim, 16 keys), no scales
+  static constexpr int KSN = (FMT == 1 || FMT == 4) ? 1 : (D / 128);
+  static constexpr int KN = (FMT == 3) ? G64 / 2 : (FMT == 4 ? 2 * G64 : G64);  // rk4v4: 16 bytes per pair of 64-dim groups
+  static constexpr int VN = (FMT == 2 || FMT == 3) ? DPW / 2 : (FMT == 4 ? 2 * DPW : DPW);
+  static constexpr int VSN = (FMT == 0) ? 2 : (FMT == 1 ? 4 : (FMT == 4 ? 1 : DPW));
   uint4 k[KN];
   uint4 v[VN];
   uint4 ks[KSN];
@@ -198,7 +215,16 @@ __device__ inline void load_k_part(PageRegs<D, FMT> &r, const AttnArgs &a, int p
   constexpr int G64 = D / 64, NCH = D / 16;
   const size_t pg = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pg_any));  // wave-uniform page
   const uint4 *kp = reinterpret_cast<const uint4 *>(a.k_codes + pg * kPage * D);
-  if constexpr (FMT == 3) {  // 4-bit keys: (key tile, group pair) units of 1 KiB, 16 bytes per lane
+  if constexpr (FMT == 4) {  // bf16 keys: the INT8 unit u of this lane holds 16 dims, here 2 x 16 bytes
+    const uint4 *kp16 = reinterpret_cast<const uint4 *>(a.k_codes + pg * kPage * D * 2);
+#pragma unroll
+    for (int cg = 0; cg < G64; ++cg) {
+      const int u = (wave * NCH + 4 * cg) * 16 + lane;
+      r.k[2 * cg] = ld_stream(kp16 + 2 * u);
+      r.k[2 * cg + 1] = ld_stream(kp16 + 2 * u + 1);
+    }
+    return;
+  } else if constexpr (FMT == 3) {  // 4-bit keys: (key tile, group pair) units of 1 KiB, 16 bytes per lane
     const uint4 *kp4 = reinterpret_cast<const uint4 *>(a.k_codes + pg * kPage * (D / 2));
 #pragma unroll
     for (int p = 0; p < G64 / 2; ++p) r.k[p] = ld_stream(kp4 + (wave * (G64 / 2) + p) * 64 + lane);
@@ -220,7 +246,17 @@ template <int D, int FMT>
 __device__ inline void load_v_part(PageRegs<D, FMT> &r, const AttnArgs &a, int pg_any, int wave, int lane, int q4) {
   constexpr int G64 = D / 64, DPW = D / 64;
   const size_t pg = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pg_any));
-  if constexpr (FMT >= 2) {  // 4-bit codes: tile pair p of the wave is one KiB, 16 bytes per lane
+  if constexpr (FMT == 4) {  // bf16 values: the INT8 unit u of this lane (16 keys of one dim), here 2 x 16 bytes
+    const uint4 *vp16 = reinterpret_cast<const uint4 *>(a.v_codes + pg * kPage * D * 2);
+#pragma unroll
+    for (int j = 0; j < DPW; ++j) {
+      const int u = (wave * DPW + j) * 64 + lane;
+      r.v[2 * j] = ld_stream(vp16 + 2 * u);
+      r.v[2 * j + 1] = ld_stream(vp16 + 2 * u + 1);
+    }
+    return;
+  }
+  if constexpr (FMT == 2 || FMT == 3) {  // 4-bit codes: tile pair p of the wave is one KiB, 16 bytes per lane
     const uint4 *vp = reinterpret_cast<const uint4 *>(a.v_codes + pg * kPage * (D / 2));
 #pragma unroll
     for (int p = 0; p < DPW / 2; ++p) r.v[p] = ld_stream(vp + (wave * (DPW / 2) + p) * 64 + lane);
@@ -279,7 +315,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   constexpr int G64 = D / 64, NCH = D / 16, DPW = D / 64;
   constexpr int QP = QLO ? 2 : 1;
   constexpr int KF = (FMT == 2) ? 0 : FMT;  // key code format: rk8v4 keys are INT8 group-64
-  static_assert(FMT < 2 || QLO != 0, "rotated queries need the lo part");
+  static_assert(FMT != 2 && FMT != 3 || QLO != 0, "rotated queries need the lo part");
   using SM = Smem<D, NT, NTEAM, QP>;
   constexpr int ROWS = SM::ROWS, PST = SM::PST;
   __shared__ uint4 qs[SM::QS];
@@ -384,7 +420,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 
   // ---- queries -> LDS in B-operand order: entry (nt, cg, hk, hl, lane) holds dims
   // 64cg + 16(lane/16) + 8hk + 0..7 of row 16nt + lane%16, as f16 hi (hl=0) or lo (hl=1).
-  if constexpr (FMT >= 2) {
+  if constexpr (FMT == 2 || FMT == 3) {
     // rk8v4, rk4v4: the keys are stored rotated by H64/8 per 64-dim group, so each 64-dim group
     // of a query row is rotated by the same matrix (butterflies in fp32, one thread per
     // (row, group)) before it is split into f16 hi + lo
@@ -420,7 +456,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
       }
     }
   }
-  for (int e = tid; e < ((FMT >= 2) ? 0 : NT * G64 * 2 * 64); e += 256 * NTEAM) {
+  for (int e = tid; e < ((FMT == 2 || FMT == 3) ? 0 : NT * G64 * 2 * 64); e += 256 * NTEAM) {
     const int ln = e & 63, hk = (e >> 6) & 1, cg = (e >> 7) % G64, nt = (e >> 7) / G64;
     const int r = row0 + 16 * nt + (ln & 15);
     const int d0 = 64 * cg + 16 * (ln >> 4) + 8 * hk;
@@ -433,7 +469,14 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
         // QLO = 1 for fp32 queries (hi + lo), 2 for rotated bf16 queries (hi + lo), 0 for
         // bf16 queries (one exact f16)
         const float x0 = load_q<QLO != 1>(a.q, qb + 2 * j), x1 = load_q<QLO != 1>(a.q, qb + 2 * j + 1);
-        if constexpr (QLO) {
+        if constexpr (FMT == 4) {
+          // BF16 pool: bf16 operands; a bf16 query is exact, an fp32 one is bf16 hi (cut)
+          // + lo (the exact residual rounded)
+          const uint32_t h0 = __float_as_uint(x0) & 0xFFFF0000u, h1 = __float_as_uint(x1) & 0xFFFF0000u;
+          const uint32_t l = f32_to_bf16_rne(x0 - __uint_as_float(h0)) | (f32_to_bf16_rne(x1 - __uint_as_float(h1)) << 16);
+          hi[j] = __builtin_bit_cast(f16x2, (h0 >> 16) | h1);
+          lo[j] = __builtin_bit_cast(f16x2, QLO ? l : 0u);
+        } else if constexpr (QLO) {
           split_f16(x0, x1, hi[j], lo[j]);
         } else {
           hi[j] = f16x2{static_cast<_Float16>(x0), static_cast<_Float16>(x1)};  // RNE; exact for bf16 in range
@@ -511,6 +554,14 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
       }
 #pragma unroll
       for (int hk = 0; hk < 2; ++hk) {
+        if constexpr (FMT == 4) {  // bf16 keys enter the matrix cores as they are
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            acc[nt] = mfma16_bf(pr.k[2 * cg + hk], __builtin_bit_cast(uint4, qc[hk][nt][0]), acc[nt]);
+            if constexpr (QLO) acc[nt] = mfma16_bf(pr.k[2 * cg + hk], __builtin_bit_cast(uint4, qc[hk][nt][QP - 1]), acc[nt]);
+          }
+          continue;
+        }
         f16x8 ka;
         if constexpr (FMT == 3) {
           const uint4 &kw = pr.k[cg / 2];
@@ -527,7 +578,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
       if constexpr (QPF == 2) {
         if (cg + 2 < G64) read_q(qc, cg + 2);
       }
-      if constexpr (KF != 1) {  // fold each key's fp16 group scale, restart the group sum
+      if constexpr (KF != 1 && KF != 4) {  // fold each key's fp16 group scale, restart the group sum
         const uint4 w = pr.ks[cg >> 1];
         float sk[4];
         f16x2_to_f32((cg & 1) ? w.z : w.x, sk[0], sk[1]);
@@ -539,6 +590,12 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
           acc[nt] = f32x4{0, 0, 0, 0};
         }
       }
+    }
+    if constexpr (FMT == 4) {  // no scales
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[nt][i] = acc[nt][i];
     }
     if constexpr (FMT == 1) {
       const float sk[4] = {__uint_as_float(pr.ks[0].x), __uint_as_float(pr.ks[0].y), __uint_as_float(pr.ks[0].z),
@@ -565,6 +622,50 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   // ---- phase 3: O^T += V^T P^T for this wave's dim tiles; each key's V scale folded into its weight
   auto accumulate = [&](auto masked_tag, PageRegs<D, FMT> &pr, int p, const float *pb) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    if constexpr (FMT == 4) {
+      // BF16 pool: V^T straight from the pool (pr.v[2j + ks]: keys 16(2ks) + 4(lane/16) + i,
+      // then 16(2ks+1) + ...), the fp32 weights as three bf16 terms
+      if constexpr (MASKED) {  // slots at or past L may hold anything: zero their values
+        const int kbase = p * kPage + 4 * q4;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          uint32_t mw[4];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int key = kbase + 16 * (2 * ks + w / 2) + 2 * (w % 2);
+            mw[w] = ((key < L) ? 0x0000FFFFu : 0u) | ((key + 1 < L) ? 0xFFFF0000u : 0u);
+          }
+#pragma unroll
+          for (int j = 0; j < DPW; ++j) {
+            pr.v[2 * j + ks].x &= mw[0];
+            pr.v[2 * j + ks].y &= mw[1];
+            pr.v[2 * j + ks].z &= mw[2];
+            pr.v[2 * j + ks].w &= mw[3];
+          }
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const float4 p0 = *reinterpret_cast<const float4 *>(pb + (16 * nt + c16) * PST + 16 * (2 * ks) + 4 * q4);
+          const float4 p1 = *reinterpret_cast<const float4 *>(pb + (16 * nt + c16) * PST + 16 * (2 * ks + 1) + 4 * q4);
+          uint32_t h[4], m[4], l[4];
+          split_bf16x3(p0.x, p0.y, h[0], m[0], l[0]);
+          split_bf16x3(p0.z, p0.w, h[1], m[1], l[1]);
+          split_bf16x3(p1.x, p1.y, h[2], m[2], l[2]);
+          split_bf16x3(p1.z, p1.w, h[3], m[3], l[3]);
+          const uint4 bh = make_uint4(h[0], h[1], h[2], h[3]), bm = make_uint4(m[0], m[1], m[2], m[3]);
+          const uint4 bl = make_uint4(l[0], l[1], l[2], l[3]);
+#pragma unroll
+          for (int j = 0; j < DPW; ++j) {
+            o[nt][j] = mfma16_bf(pr.v[2 * j + ks], bh, o[nt][j]);
+            o[nt][j] = mfma16_bf(pr.v[2 * j + ks], bm, o[nt][j]);
+            o[nt][j] = mfma16_bf(pr.v[2 * j + ks], bl, o[nt][j]);
+          }
+        }
+      return;
+    }
     if constexpr (MASKED) {
       // slots at or past L may hold anything (never written): zero their V codes
       const int kbase = p * kPage + 4 * q4;  // key of (kt, i) is kbase + 16kt + i
@@ -726,7 +827,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 #pragma unroll
         for (int i = 0; i < 4; ++i) pv[i] = exp2_hw(z[nt][i] - msafe);
         psum[nt] = (pv[0] + pv[1]) + (pv[2] + pv[3]);
-        if constexpr (FMT != 1) {
+        if constexpr (FMT != 1 && FMT != 4) {
           // INT8 and rk8v4: the weights go out as f16 hi+lo pairs (the V scales, fp16, are
           // applied by the accumulating wave with packed f16 arithmetic)
           f16x2 h01, l01, h23, l23;
@@ -993,7 +1094,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 template <int D, int NT, int FMT, int QDT>
 hipError_t split_one(const AttnArgs &a, hipStream_t s) {
   // fp32 queries need the hi+lo pair; bf16 queries are one exact f16, unless rotated (rk8v4)
-  constexpr int QLO = QDT == 0 ? 1 : (FMT >= 2 ? 2 : 0);
+  constexpr int QLO = QDT == 0 ? 1 : ((FMT == 2 || FMT == 3) ? 2 : 0);
   const dim3 grid(a.n_splits, a.num_kv_heads, a.num_seqs);
   if (a.k_new != nullptr)
     hipLaunchKernelGGL((attn_split_kernel<D, NT, FMT, QLO, kTeams, 1>), grid, dim3(256 * kTeams), 0, s, a);
@@ -1004,7 +1105,7 @@ hipError_t split_one(const AttnArgs &a, hipStream_t s) {
 
 template <int D, int FMT, int QDT>
 hipError_t prefill_one(const AttnArgs &a, hipStream_t s) {
-  constexpr int QLO = QDT == 0 ? 1 : (FMT >= 2 ? 2 : 0);
+  constexpr int QLO = QDT == 0 ? 1 : ((FMT == 2 || FMT == 3) ? 2 : 0);
   const dim3 grid(a.n_splits, a.num_kv_heads * a.row_blocks, a.num_seqs);
   hipLaunchKernelGGL((attn_split_kernel<D, kPrefillNT, FMT, QLO, kPrefillTeams, 2>), grid, dim3(256 * kPrefillTeams),
                      0, s, a);
@@ -1025,7 +1126,8 @@ hipError_t launch_attn_split(int format, int head_dim, int q_dtype, const AttnAr
   if (head_dim == DD && nt == NTT && format == F && q_dtype == Q) return split_one<DD, NTT, F, Q>(a, s);
 #define KVQ_SPLIT_DQ(DD, NTT) \
   KVQ_SPLIT_CASE(DD, NTT, 0, 0) KVQ_SPLIT_CASE(DD, NTT, 0, 1) KVQ_SPLIT_CASE(DD, NTT, 1, 0) KVQ_SPLIT_CASE(DD, NTT, 1, 1) \
-  KVQ_SPLIT_CASE(DD, NTT, 2, 0) KVQ_SPLIT_CASE(DD, NTT, 2, 1) KVQ_SPLIT_CASE(DD, NTT, 3, 0) KVQ_SPLIT_CASE(DD, NTT, 3, 1)
+  KVQ_SPLIT_CASE(DD, NTT, 2, 0) KVQ_SPLIT_CASE(DD, NTT, 2, 1) KVQ_SPLIT_CASE(DD, NTT, 3, 0) KVQ_SPLIT_CASE(DD, NTT, 3, 1) \
+  KVQ_SPLIT_CASE(DD, NTT, 4, 0) KVQ_SPLIT_CASE(DD, NTT, 4, 1)
   KVQ_SPLIT_DQ(128, 1)
   KVQ_SPLIT_DQ(128, 2)
   KVQ_SPLIT_DQ(256, 1)
@@ -1042,6 +1144,7 @@ hipError_t launch_attn_prefill(int format, int head_dim, int q_dtype, const Attn
   KVQ_PF_CASE(256, 0, 0) KVQ_PF_CASE(256, 0, 1) KVQ_PF_CASE(256, 1, 0) KVQ_PF_CASE(256, 1, 1)
   KVQ_PF_CASE(128, 2, 0) KVQ_PF_CASE(128, 2, 1) KVQ_PF_CASE(256, 2, 0) KVQ_PF_CASE(256, 2, 1)
   KVQ_PF_CASE(128, 3, 0) KVQ_PF_CASE(128, 3, 1) KVQ_PF_CASE(256, 3, 0) KVQ_PF_CASE(256, 3, 1)
+  KVQ_PF_CASE(128, 4, 0) KVQ_PF_CASE(128, 4, 1) KVQ_PF_CASE(256, 4, 0) KVQ_PF_CASE(256, 4, 1)
 #undef KVQ_PF_CASE
   return hipErrorInvalidValue;
 }

@@ -15,13 +15,14 @@ bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 int check_cache(const kvq_cache_t *c) {
   if (!c) return KVQ_ERR_INVALID_ARG;
-  if (c->format < KVQ_INT8_G64 || c->format > KVQ_RK4V4) return KVQ_ERR_INVALID_ARG;
+  if (c->format < KVQ_INT8_G64 || c->format > KVQ_BF16_KV) return KVQ_ERR_INVALID_ARG;
   if (c->num_blocks < 1 || c->num_kv_heads < 1 || c->block_size < 1) return KVQ_ERR_INVALID_ARG;
   if (c->block_size != kvq::kPage) return KVQ_ERR_UNSUPPORTED;
   if (c->head_dim != 128 && c->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
   const void *p[4] = {c->k_codes, c->v_codes, c->k_scales, c->v_scales};
-  for (const void *x : p)
-    if (!x || !aligned16(x)) return KVQ_ERR_INVALID_ARG;
+  const int n = (c->format == KVQ_BF16_KV) ? 2 : 4;  // the BF16 pool has no scales
+  for (int i = 0; i < n; ++i)
+    if (!p[i] || !aligned16(p[i])) return KVQ_ERR_INVALID_ARG;
   return KVQ_OK;
 }
 

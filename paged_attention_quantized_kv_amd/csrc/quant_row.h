@@ -80,6 +80,14 @@ __device__ inline void v4_place(int s, int d, size_t &word, int &shift) {
   shift = 16 * (k % 2) + 4 * (k / 2);
 }
 
+// bfloat16 bits of v, round to nearest even (a carry may bump the exponent, up to
+// infinity); NaN gives a quiet NaN.
+__device__ inline uint32_t f32_to_bf16_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 // rk4v4 keys (NInfer-3090 README, "Lloyd-Max 4-bit keys (rk4v4)"): the INT8 codes of
 // the 16 Lloyd-Max levels of a unit Gaussian, rint(127 * L_i / L_15), ascending; a
 // rotated coordinate u = y / scale (the INT8 group scale) takes the level whose code is
@@ -132,6 +140,29 @@ __device__ inline void store_row(const AppendArgs &a, const float (&xin)[D / 64]
 
   const size_t page = static_cast<size_t>(blk) * a.num_kv_heads + h;
   uint32_t c[E];
+
+  if constexpr (FMT == 4) {  // BF16: the element order of INT8 at two bytes per element
+    uint16_t *el = reinterpret_cast<uint16_t *>(which ? a.v_codes : a.k_codes) + page * kPage * D;
+    const int d0 = lane * E;
+    if (which == 0) {  // the E dims of this lane are adjacent in one 16-dim tile row
+      const size_t off = (static_cast<size_t>(slot / 16) * (D / 16) + d0 / 16) * 256 + (slot % 16) * 16 + d0 % 16;
+      uint32_t wv[E / 2];
+#pragma unroll
+      for (int k = 0; k < E / 2; ++k) wv[k] = f32_to_bf16_rne(x[2 * k]) | (f32_to_bf16_rne(x[2 * k + 1]) << 16);
+      if constexpr (E == 4) {
+        *reinterpret_cast<uint2 *>(el + off) = make_uint2(wv[0], wv[1]);
+      } else {
+        *reinterpret_cast<uint32_t *>(el + off) = wv[0];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int d = d0 + e;
+        el[(static_cast<size_t>(d / 16) * 4 + run) * 256 + (d % 16) * 16 + spos] = static_cast<uint16_t>(f32_to_bf16_rne(x[e]));
+      }
+    }
+    return;
+  }
 
   if constexpr (FMT == 3) {
     if (which == 0) {  // rk4v4 keys: level indices over the INT8 group scale of the rotated row

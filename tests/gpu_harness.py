@@ -25,7 +25,10 @@ def src_tensor(a: np.ndarray, src: int, device) -> torch.Tensor:
 def new_cache(K, w: S.Workload, device, poison: bool = True):
     s = w.shape
     cache = K.Cache(s.fmt, w.num_blocks, s.Hkv, s.D, device=device)
-    if poison:
+    if poison and s.fmt == S.FMT_BF16:  # every element a bf16 NaN
+        cache.k_codes.view(torch.int16).fill_(-1)
+        cache.v_codes.view(torch.int16).fill_(-1)
+    elif poison:
         cache.k_codes.fill_(POISON_CODE)
         cache.v_codes.fill_(POISON_CODE)
         if s.fmt in (S.FMT_INT8_G64, S.FMT_RK8V4, S.FMT_RK4V4):  # fp16 scales
@@ -67,7 +70,13 @@ def fill_gpu(K, w: S.Workload, cache, device, chunk: int = 8192, decode_rows: bo
 
 def oracle_pool(O, w: S.Workload):
     s = w.shape
-    pool = O.Pool(s.fmt, w.num_blocks, s.Hkv, s.D, fill=POISON_CODE)
+    pool = O.Pool(s.fmt, w.num_blocks, s.Hkv, s.D, fill=0xFF if s.fmt == S.FMT_BF16 else POISON_CODE)
+    if s.fmt == S.FMT_BF16:
+        for b in range(s.B):
+            L = int(w.seq_lens[b])
+            pool.append(w.rows("k", b, 0, L), w.rows("v", b, 0, L), s.src, w.block_table[b:b + 1],
+                        np.array([0], np.int32))
+        return pool
     if s.fmt in (S.FMT_INT8_G64, S.FMT_RK8V4, S.FMT_RK4V4):
         pool.k_scales[:] = POISON_F16
         pool.v_scales[:] = POISON_F16
@@ -85,9 +94,12 @@ def pool_equal(cache, pool) -> dict:
     """Byte-exact comparison of the device pool with the oracle's pool; returns mismatch counts."""
     res = {}
     for name in ("k_codes", "v_codes", "k_scales", "v_scales"):
-        g = getattr(cache, name).cpu().numpy().view(np.uint8)
+        if name.endswith("scales") and cache.format == S.FMT_BF16:  # the BF16 pool has no scales
+            res[name] = 0
+            continue
+        g = getattr(cache, name).contiguous().view(torch.uint8).cpu().numpy()
         o = getattr(pool, name).view(np.uint8)
-        res[name] = int(np.count_nonzero(g != o))
+        res[name] = int(np.count_nonzero(g != o)) if g.size == o.size else -1
     return res
 
 

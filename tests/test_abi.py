@@ -54,7 +54,7 @@ def _attn(K, d, q=0x5000, qdt=1, B=1, T=4, Hq=24, bt=0x7000, mb=4, sl=0x8000, L=
 def test_append_validation(K):
     E = dict(inv=-1, uns=-2, cap=-4, launch=-5)
     assert K.lib.kv_append_quant(None, None, None, 1, 1, 1, None, 1, None, None) == E["inv"]
-    assert _append(K, _desc(K, fmt=4)) == E["inv"]
+    assert _append(K, _desc(K, fmt=5)) == E["inv"]
     assert _append(K, _desc(K, fmt=-1)) == E["inv"]
     assert _append(K, _desc(K, fmt=3)) == E["launch"]  # rk4v4
     assert _append(K, _desc(K, fmt=2)) == E["launch"]  # rk8v4: valid, reaches the runtime
@@ -163,9 +163,16 @@ def test_prefill_workspace(K):
     assert K.prefill_workspace_bytes(1, 4, 24, 4, 192, 4096) == 0
 
 
-@pytest.mark.parametrize("fmt", [2, 3])
-def test_rk_formats_are_accepted_by_every_attention_call(K, fmt):
+@pytest.mark.parametrize("fmt", [2, 3, 4])
+def test_rk_and_bf16_formats_are_accepted_by_every_attention_call(K, fmt):
     d = _desc(K, fmt=fmt)
     for fn in ("paged_decode_attn", "paged_decode_attn_split", "paged_decode_attn_merge", "paged_prefill_attn"):
         assert _attn(K, d, fn=fn) == -5  # valid: reaches the runtime, which has no device here
     assert _attn(K, _desc(K, fmt=fmt, D=64)) == -2
+
+
+def test_bf16_pool_needs_no_scales(K):
+    d = K.CacheDesc(4, 16, 64, 4, 256, 0, 0x1000, 0x2000, 0, 0)
+    assert _attn(K, d) == -5  # valid: reaches the runtime, which has no device here
+    d = K.CacheDesc(0, 16, 64, 4, 256, 0, 0x1000, 0x2000, 0, 0)
+    assert _attn(K, d) == -1  # the INT8 pool does

@@ -1091,6 +1091,390 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   }
 }
 
+// ---- Prefill kernel for INT8 and FP8 pools with bf16 queries.
+//
+// A workgroup of 4 waves owns 128 query rows (t*G + g) of one KV head and one chunk of
+// its context; wave w owns rows 32w .. 32w+31 outright: their queries stay in registers
+// as the B operands of S^T = K Q^T, their softmax state and their output O^T = V^T P^T
+// (all D dims) stay in the wave, and the weights go from the score registers straight
+// into the P·V products (the V layout puts each lane's keys where the S^T tile leaves
+// them), so no wave waits on another for softmax.  The K and V codes of a page are
+// converted to f16 once per workgroup, by all 256 threads, into LDS (double-buffered:
+// page p+1 is converted while page p is multiplied, page p+2 is in flight from HBM), and
+// every wave reads its matrix-core A operands from there: one barrier per page.
+#ifndef KVQ_PREFILL_NTW
+#define KVQ_PREFILL_NTW 1
+#endif
+template <int D, int FMT>
+__global__ __launch_bounds__(64 * 8 / KVQ_PREFILL_NTW, 1) void prefill_kernel(AttnArgs a) {
+  constexpr int G64 = D / 64, KB = D / 32, DT = D / 16, NTW = KVQ_PREFILL_NTW, ROWS = 128;
+  constexpr int NW = 8 / NTW, NTH = 64 * NW;  // waves (16*NTW rows each) and threads of the workgroup
+  constexpr int CPT = 64 * DT / NTH;          // 16-byte code chunks of K (and of V) per thread per page
+  __shared__ uint4 kl[2][4 * KB * 64];  // f16 K operands: [(kt*KB + kb)*64 + lane]
+  __shared__ uint4 vl[2][DT * 2 * 64];  // f16 V^T operands: [(dt*2 + ks)*64 + lane]
+  // INT8: the page's K and V scales (D fp16 each), copied from the pool in its own layout,
+  // so the waves read them from LDS (FP8 pools, one scale per key, read theirs directly)
+  constexpr int SCU = (FMT == 0) ? D * 2 / 16 : 1;  // uint4 per scale array
+  __shared__ uint4 sl[2][2 * SCU];
+  __shared__ int32_t lds_pg[kMaxPrefillChunkPages];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q4 = lane >> 4, c16 = lane & 15;
+  const int split = blockIdx.x, kvh = blockIdx.y % a.num_kv_heads, b = blockIdx.z;
+  const int row0 = (blockIdx.y / a.num_kv_heads) * ROWS;
+  const int L = a.seq_lens[b];
+  const int R = a.rows;
+  if (L < a.T || L > a.max_seq_len || L > a.max_blocks * kPage) {  // the merge writes NaN rows
+    if (a.direct_out != 0 && split == 0) {                        // no merge: write them here
+      for (int e = tid; e < ROWS * D; e += NTH) {
+        const int r = row0 + e / D;
+        if (r < R)
+          a.out[((static_cast<size_t>(b) * a.T + r / a.group) * a.num_q_heads + kvh * a.group + r % a.group) * D +
+                e % D] = NAN;
+      }
+    }
+    return;
+  }
+  // keys the block's rows see: row r = t*G + g sees positions 0 .. L - T + t
+  const int lim = L - a.T + (min(row0 + ROWS, R) - 1) / a.group + 1;
+  const int lo_last = L - a.T + row0 / a.group;  // the last key the block's first row sees
+  const int tok0 = split * a.tokens_per_split;
+  if (tok0 >= lim) return;  // chunk past every key of these rows: the merge skips it
+  const int tok1 = min(tok0 + a.tokens_per_split, lim);
+  const int page0 = tok0 / kPage, npg = (tok1 + kPage - 1) / kPage - page0;
+
+  // ---- the chunk's block ids -> pool pages in LDS (an invalid id reads block 0 and flags the chunk)
+  bool bad = false;
+  const int32_t *bt = a.block_table + static_cast<size_t>(b) * a.max_blocks;
+  for (int i = tid; i < npg; i += NTH) {
+    const int blk = bt[page0 + i];
+    const bool ok = (blk >= 0) && (blk < a.num_blocks);
+    bad |= !ok;
+    lds_pg[i] = (ok ? blk : 0) * a.num_kv_heads + kvh;
+  }
+  const int any_bad = __syncthreads_or(bad ? 1 : 0);
+
+  // ---- page codes: HBM -> registers -> f16 operands in LDS
+  uint4 kc[CPT], vc[CPT], sc4 = make_uint4(0, 0, 0, 0);
+  auto gload = [&](int i) {
+    const size_t pg = static_cast<uint32_t>(lds_pg[i]);
+    const uint4 *kp = reinterpret_cast<const uint4 *>(a.k_codes + pg * kPage * D);
+    const uint4 *vp = reinterpret_cast<const uint4 *>(a.v_codes + pg * kPage * D);
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      kc[k] = ld_stream(kp + tid + NTH * k);
+      vc[k] = ld_stream(vp + tid + NTH * k);
+    }
+    if constexpr (FMT == 0) {
+      if (tid < 2 * SCU) {  // threads 0 .. SCU-1: K scales, SCU .. 2 SCU-1: V scales
+        const uint4 *sp = reinterpret_cast<const uint4 *>(static_cast<const _Float16 *>(tid < SCU ? a.k_scales : a.v_scales) +
+                                                          pg * D);
+        sc4 = ld_stream(sp + (tid % SCU));
+      }
+    }
+  };
+  auto convert = [&](int buf, int p) {
+    if constexpr (FMT == 0) {
+      if (tid < 2 * SCU) sl[buf][tid] = sc4;
+    }
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int c = tid + NTH * k;
+      // K chunk c: key s = (c / (16 DT)) * 16 + c % 16, dims 16 dt .. +15 with dt = (c / 16) % DT;
+      // in the S^T products it is key tile s/16, dim block dt/2, lanes 16 (2 (dt%2) + hk) + s%16
+      const int kt = c / (16 * DT), dt = (c / 16) % DT, sr = c % 16;
+      uint4 *kd = &kl[buf][(kt * KB + dt / 2) * 64 + 32 * (dt % 2) + sr];
+      kd[0] = __builtin_bit_cast(uint4, codes_to_f16<FMT>(kc[k].x, kc[k].y));
+      kd[16] = __builtin_bit_cast(uint4, codes_to_f16<FMT>(kc[k].z, kc[k].w));
+      // V chunk c: dim 16 (c/64) + c%16, the 16 keys 16 kt + 4 ((c%64)/16) + i; slots at or
+      // past L may hold anything (never written): zero their codes
+      uint4 v = vc[k];
+      const int kbase = p * kPage + 4 * ((c % 64) / 16);
+      if (kbase + 48 + 3 >= L) {
+        uint32_t mw[4];
+#pragma unroll
+        for (int kt2 = 0; kt2 < 4; ++kt2) {
+          uint32_t wv = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) wv |= (kbase + 16 * kt2 + i < L) ? (0xFFu << (8 * i)) : 0u;
+          mw[kt2] = wv;
+        }
+        v.x &= mw[0];
+        v.y &= mw[1];
+        v.z &= mw[2];
+        v.w &= mw[3];
+      }
+      vl[buf][((c / 64) * 2 + 0) * 64 + c % 64] = __builtin_bit_cast(uint4, codes_to_f16<FMT>(v.x, v.y));
+      vl[buf][((c / 64) * 2 + 1) * 64 + c % 64] = __builtin_bit_cast(uint4, codes_to_f16<FMT>(v.z, v.w));
+    }
+  };
+  if (npg > 0) gload(0);
+
+  // ---- this wave's queries (bf16, exact in f16) -> registers: B operand of dim block kb
+  f16x8 qf[NTW][KB];
+  int last[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int r = row0 + 16 * NTW * wave + 16 * nt + c16;
+    last[nt] = (r < R) ? (L - a.T + r / a.group) : -1;  // -1: padding row, sees nothing
+    const size_t qb = ((static_cast<size_t>(b) * a.T + r / a.group) * a.num_q_heads + kvh * a.group + r % a.group) * D;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (r < R) u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + qb + 32 * kb + 8 * q4);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      f16x2 h[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        h[j] = f16x2{static_cast<_Float16>(__uint_as_float(w[j] << 16)),
+                     static_cast<_Float16>(__uint_as_float(w[j] & 0xFFFF0000u))};
+      qf[nt][kb] = f16x8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+    }
+  }
+  if (npg > 0) convert(0, page0);
+  if (npg > 1) gload(1);
+  __syncthreads();
+
+  f32x4 o[NTW][DT];
+  float m[NTW], lsum[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    m[nt] = -INFINITY;
+    lsum[nt] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[nt][dt] = f32x4{0, 0, 0, 0};
+  }
+
+  for (int it = 0; it < npg; ++it) {
+    const int p = page0 + it, buf = it & 1;
+    [[maybe_unused]] const size_t pg = static_cast<uint32_t>(lds_pg[it]);
+    if (it + 1 < npg) convert(buf ^ 1, p + 1);  // the next page, loaded one iteration ago
+    if (it + 2 < npg) gload(it + 2);
+    const bool full = (p * kPage + kPage - 1) <= lo_last;  // every real row sees every key of the page
+
+    // ---- S^T = K Q^T for the 4 key tiles x this wave's 2 row tiles, scales folded per 64 dims
+    float z[4][NTW][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[kt][nt][i] = 0.0f;
+#pragma unroll
+    for (int g = 0; g < G64; ++g) {
+      f32x4 acc[4][NTW];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) acc[kt][nt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int kb = 2 * g; kb < 2 * g + 2; ++kb)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const f16x8 ka = lds_f16x8(&kl[buf][(kt * KB + kb) * 64 + lane]);
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt) acc[kt][nt] = mfma16(ka, qf[nt][kb], acc[kt][nt]);
+        }
+      if constexpr (FMT == 0) {
+        // fp16 scales of this lane's keys 16 kt + 4 q4 + i in group g: element
+        // ((q4*4 + kt) * G64 + g) * 4 + i of the page's K scales
+        const uint2 *ksp = reinterpret_cast<const uint2 *>(&sl[buf][0]);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const uint2 w = ksp[(q4 * 4 + kt) * G64 + g];
+          float sk[4];
+          f16x2_to_f32(w.x, sk[0], sk[1]);
+          f16x2_to_f32(w.y, sk[2], sk[3]);
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z[kt][nt][i] += sk[i] * acc[kt][nt][i];
+        }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z[kt][nt][i] += acc[kt][nt][i];
+      }
+    }
+    if constexpr (FMT == 1) {  // one fp32 scale per key: element q4*16 + kt*4 + i
+      const float4 *ksp = reinterpret_cast<const float4 *>(static_cast<const float *>(a.k_scales) + pg * kPage);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const float4 w = ksp[q4 * 4 + kt];
+        const float sk[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) z[kt][nt][i] *= sk[i];
+      }
+    }
+    // log2 units; the causal mask (and keys past L) on the pages that need it
+    float pm[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = z[kt][nt][i] * a.qk_scale_log2;
+          if (!full) v = (p * kPage + 16 * kt + 4 * q4 + i <= last[nt]) ? v : -INFINITY;
+          z[kt][nt][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      pm[nt] = max_xor32(max_xor16(mx));
+    }
+    // ---- online softmax, per row inside the wave: the reference maximum moves only when
+    // a page maximum passes it by more than kLazy (weights stay <= 2^kLazy)
+    bool up = false;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) up |= pm[nt] > m[nt] + kLazy;
+    if (__any(up)) {
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const bool u = pm[nt] > m[nt] + kLazy;
+        const float mnew = u ? pm[nt] : m[nt];
+        const float alpha = u ? exp2_hw(m[nt] - mnew) : 1.0f;  // 0 when m was -inf
+        m[nt] = mnew;
+        lsum[nt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[nt][dt] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const float ms = (m[nt] == -INFINITY) ? 0.0f : m[nt];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          z[kt][nt][i] = exp2_hw(z[kt][nt][i] - ms);
+          lsum[nt] += z[kt][nt][i];
+        }
+    }
+
+    // ---- O^T += V^T P^T: key half ks is key tiles 2ks, 2ks+1 (this lane's keys 4 q4 + i of each)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if constexpr (FMT == 0) {
+        f16x2 ph[NTW][4], pl[NTW][4];
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            split_f16(z[2 * ks + kk][nt][0], z[2 * ks + kk][nt][1], ph[nt][2 * kk], pl[nt][2 * kk]);
+            split_f16(z[2 * ks + kk][nt][2], z[2 * ks + kk][nt][3], ph[nt][2 * kk + 1], pl[nt][2 * kk + 1]);
+          }
+        // V scales (fp16) of this lane's keys in 64-dim group g: 8 values, element
+        // (q4*G64 + g)*16 + 8 ks .. of the page's V scales
+        const uint4 *vsp = &sl[buf][SCU];
+#pragma unroll
+        for (int g = 0; g < G64; ++g) {
+          const uint4 w = vsp[(q4 * G64 + g) * 2 + ks];
+          f16x2 sc[4] = {__builtin_bit_cast(f16x2, w.x), __builtin_bit_cast(f16x2, w.y), __builtin_bit_cast(f16x2, w.z),
+                         __builtin_bit_cast(f16x2, w.w)};
+          if (!full) {  // unwritten slots (weight 0) may hold NaN scales
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const int key = p * kPage + 16 * (2 * ks + j / 2) + 4 * q4 + 2 * (j % 2) + e;
+                if (key >= L) sc[j][e] = _Float16(0);
+              }
+          }
+          f16x8 bh[NTW], bl[NTW];
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt) {
+            f16x2 hi[4], lo[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) scale_pair(ph[nt][j], pl[nt][j], sc[j], hi[j], lo[j]);
+            bh[nt] = f16x8{hi[0][0], hi[0][1], hi[1][0], hi[1][1], hi[2][0], hi[2][1], hi[3][0], hi[3][1]};
+            bl[nt] = f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]};
+          }
+#pragma unroll
+          for (int dt = 4 * g; dt < 4 * g + 4; ++dt) {
+            const f16x8 va = lds_f16x8(&vl[buf][(dt * 2 + ks) * 64 + lane]);
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+              o[nt][dt] = mfma16(va, bh[nt], o[nt][dt]);
+              o[nt][dt] = mfma16(va, bl[nt], o[nt][dt]);
+            }
+          }
+        }
+      } else {  // FP8: one fp32 scale per key, the same for every dim
+        const float4 *vsp = reinterpret_cast<const float4 *>(static_cast<const float *>(a.v_scales) + pg * kPage);
+        f16x8 bh[NTW], bl[NTW];
+        float sv[2][4];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const float4 w = vsp[q4 * 4 + 2 * ks + kk];
+          sv[kk][0] = w.x;
+          sv[kk][1] = w.y;
+          sv[kk][2] = w.z;
+          sv[kk][3] = w.w;
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          f16x2 hi[4], lo[4];
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            float pv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float pp = z[2 * ks + kk][nt][i];
+              pv[i] = (pp != 0.0f) ? pp * sv[kk][i] : 0.0f;  // unwritten slots: NaN scales
+            }
+            split_f16(pv[0], pv[1], hi[2 * kk], lo[2 * kk]);
+            split_f16(pv[2], pv[3], hi[2 * kk + 1], lo[2 * kk + 1]);
+          }
+          bh[nt] = f16x8{hi[0][0], hi[0][1], hi[1][0], hi[1][1], hi[2][0], hi[2][1], hi[3][0], hi[3][1]};
+          bl[nt] = f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]};
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const f16x8 va = lds_f16x8(&vl[buf][(dt * 2 + ks) * 64 + lane]);
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt) {
+            o[nt][dt] = mfma16(va, bh[nt], o[nt][dt]);
+            o[nt][dt] = mfma16(va, bl[nt], o[nt][dt]);
+          }
+        }
+      }
+    }
+    __syncthreads();  // the next page's operands are in LDS; this page's buffer is free
+  }
+
+  // ---- rows: l summed over the 4 lanes of a row; normalized rows to out, or the partials
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const float lt = sum_xor32(sum_xor16(lsum[nt]));
+    const int r = row0 + 16 * NTW * wave + 16 * nt + c16;
+    if (r >= R) continue;
+    const float l = any_bad ? NAN : lt;
+    if (a.direct_out != 0) {
+      const size_t orow = ((static_cast<size_t>(b) * a.T + r / a.group) * a.num_q_heads + kvh * a.group + r % a.group) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const f32x4 v = o[nt][dt];
+        *reinterpret_cast<float4 *>(a.out + orow + 16 * dt + 4 * q4) = make_float4(v[0] / l, v[1] / l, v[2] / l, v[3] / l);
+      }
+    } else {
+      const size_t part = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits + split;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const f32x4 v = o[nt][dt];
+        *reinterpret_cast<float4 *>(a.ws_o + (part * R + r) * D + 16 * dt + 4 * q4) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+      if (q4 == 0) {
+        a.ws_ml[(part * R + r) * 2 + 0] = m[nt];
+        a.ws_ml[(part * R + r) * 2 + 1] = l;
+      }
+    }
+  }
+}
+
 template <int D, int NT, int FMT, int QDT>
 hipError_t split_one(const AttnArgs &a, hipStream_t s) {
   // fp32 queries need the hi+lo pair; bf16 queries are one exact f16, unless rotated (rk8v4)
@@ -1105,6 +1489,11 @@ hipError_t split_one(const AttnArgs &a, hipStream_t s) {
 
 template <int D, int FMT, int QDT>
 hipError_t prefill_one(const AttnArgs &a, hipStream_t s) {
+  if constexpr ((FMT == 0 || FMT == 1) && QDT == 1) {  // the prefill kernel: 128-row blocks
+    const dim3 grid(a.n_splits, a.num_kv_heads * a.row_blocks, a.num_seqs);
+    hipLaunchKernelGGL((prefill_kernel<D, FMT>), grid, dim3(64 * 8 / KVQ_PREFILL_NTW), 0, s, a);
+    return hipGetLastError();
+  }
   constexpr int QLO = QDT == 0 ? 1 : ((FMT == 2 || FMT == 3) ? 2 : 0);
   const dim3 grid(a.n_splits, a.num_kv_heads * a.row_blocks, a.num_seqs);
   hipLaunchKernelGGL((attn_split_kernel<D, kPrefillNT, FMT, QLO, kPrefillTeams, 2>), grid, dim3(256 * kPrefillTeams),

@@ -72,5 +72,8 @@ hipError_t launch_append(int format, int head_dim, int src_dtype, const AppendAr
 hipError_t launch_attn_split(int format, int head_dim, int q_dtype, const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_merge(int head_dim, const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_prefill(int format, int head_dim, int q_dtype, const AttnArgs &a, hipStream_t s);
+// query rows per prefill row block: the prefill kernel (INT8 and FP8 pools, bf16 queries)
+// takes 128, the split kernel's prefill instance kPrefillRows
+inline int prefill_block_rows(int format, int q_dtype) { return (format <= 1 && q_dtype == 1) ? 128 : kPrefillRows; }
 
 }  // namespace kvq

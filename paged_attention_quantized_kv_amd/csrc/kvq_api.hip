@@ -6,6 +6,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "internal.h"
 
 namespace {
@@ -76,7 +78,7 @@ struct PrefillShape {
 };
 
 int prefill_shape(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                  int32_t max_seq_len, PrefillShape *s) {
+                  int32_t max_seq_len, int block_rows, PrefillShape *s) {
   if (num_seqs < 1 || T < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_seq_len < 1) return KVQ_ERR_INVALID_ARG;
   if (head_dim != 128 && head_dim != 256) return KVQ_ERR_UNSUPPORTED;
   if (num_q_heads % num_kv_heads != 0) return KVQ_ERR_UNSUPPORTED;
@@ -84,7 +86,7 @@ int prefill_shape(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_
   if (max_seq_len < T) return KVQ_ERR_INVALID_ARG;
   const int32_t group = num_q_heads / num_kv_heads;
   const long rows = static_cast<long>(T) * group;
-  const long row_blocks = (rows + kvq::kPrefillRows - 1) / kvq::kPrefillRows;
+  const long row_blocks = (rows + block_rows - 1) / block_rows;
   if (rows > 0x7FFFFFFFL || row_blocks * num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
   if (static_cast<long>(num_seqs) * T * num_q_heads * (head_dim / 64) > 0x7FFFFFFFL) return KVQ_ERR_UNSUPPORTED;
   const long pages = (static_cast<long>(max_seq_len) + kvq::kPage - 1) / kvq::kPage;
@@ -266,9 +268,15 @@ int paged_decode_step(const kvq_cache_t *cache, const void *k_new, const void *v
 
 size_t paged_prefill_attn_workspace_bytes(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
                                           int32_t head_dim, int32_t max_seq_len) {
-  PrefillShape s;
-  if (prefill_shape(num_seqs, T, num_q_heads, num_kv_heads, head_dim, max_seq_len, &s) != KVQ_OK) return 0;
-  return s.ml_bytes + s.o_bytes;
+  // the larger of the two row-block sizes' needs (the kernel depends on the format and
+  // the query dtype, which this query does not take)
+  size_t n = 0;
+  for (int rows : {128, kvq::kPrefillRows}) {
+    PrefillShape s;
+    if (prefill_shape(num_seqs, T, num_q_heads, num_kv_heads, head_dim, max_seq_len, rows, &s) != KVQ_OK) return 0;
+    n = std::max(n, s.ml_bytes + s.o_bytes);
+  }
+  return n;
 }
 
 int paged_prefill_attn(const kvq_cache_t *cache, const void *q, int32_t q_dtype, int32_t num_seqs, int32_t T,
@@ -283,7 +291,8 @@ int paged_prefill_attn(const kvq_cache_t *cache, const void *q, int32_t q_dtype,
   if (max_blocks_per_seq < 1) return KVQ_ERR_INVALID_ARG;
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVQ_ERR_INVALID_ARG;
   PrefillShape s;
-  rc = prefill_shape(num_seqs, T, num_q_heads, cache->num_kv_heads, cache->head_dim, max_seq_len, &s);
+  rc = prefill_shape(num_seqs, T, num_q_heads, cache->num_kv_heads, cache->head_dim, max_seq_len,
+                     kvq::prefill_block_rows(cache->format, q_dtype), &s);
   if (rc) return rc;
   if (static_cast<long>(max_seq_len) > static_cast<long>(max_blocks_per_seq) * kvq::kPage) return KVQ_ERR_CAPACITY;
   if (workspace_bytes < s.ml_bytes + s.o_bytes) return KVQ_ERR_WORKSPACE;

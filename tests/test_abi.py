@@ -143,8 +143,9 @@ def test_prefill_validation(K):
     assert _attn(K, d, wsb=16, T=100, Hq=8, L=256, fn=fn) == -3
     assert _attn(K, _desc(K, D=64), fn=fn) == -2
     assert _attn(K, d, B=1025, fn=fn) == -2
-    # 64-row blocks x KV heads beyond the grid's y limit
-    assert _attn(K, d, T=200000, Hq=24, L=200000, mb=3125, fn=fn) == -2
+    # row blocks (128 rows for INT8 with bf16 queries) x KV heads beyond the grid's y limit
+    assert _attn(K, d, T=400000, Hq=24, L=400000, mb=6250, fn=fn) == -2
+    assert _attn(K, d, T=200000, Hq=24, L=200000, mb=3125, qdt=0, fn=fn) == -2  # fp32 queries: 64-row blocks
     # any T, and T x group beyond the decode limit: valid, reaches the runtime (no device here)
     assert _attn(K, d, T=9, fn=fn) == -5
     assert _attn(K, d, T=4096, Hq=24, L=4096, mb=64, fn=fn) == -5

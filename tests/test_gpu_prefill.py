@@ -60,13 +60,13 @@ def test_prefill_small(K, name):
 
 @pytest.mark.parametrize("fmt", [S.FMT_INT8_G64, S.FMT_FP8_ROW])
 def test_prefill_direct_rows(K, fmt):
-    """4096 query rows per KV head: 64 row blocks x 2 KV heads x 2 sequences fill the
-    chip with one chunk each, so the split kernel writes the rows itself."""
-    shp = S.tiny_shape(B=2, T=512, Hq=16, Hkv=2, D=128, lens=(700, 1500), src=S.SRC_BF16, fmt=fmt,
+    """8192 query rows per KV head: 64 row blocks of 128 x 2 KV heads x 2 sequences fill
+    the chip with one chunk each, so the kernel writes the rows itself."""
+    shp = S.tiny_shape(B=2, T=1024, Hq=16, Hkv=2, D=128, lens=(1100, 1500), src=S.SRC_BF16, fmt=fmt,
                        outliers=True, name="pf_direct")
     w = S.make(shp, seed=S.seed_of("tiny") + 600 + fmt)
     assert _direct(K, w.shape, w.max_seq_len)
-    check(K, w, rows=_prefill_rows(w, (0, 1, 31, 32, 33, 255, 480, 511), 5), chunk=300, prefill=True)
+    check(K, w, rows=_prefill_rows(w, (0, 1, 15, 16, 17, 255, 480, 1023), 5), chunk=300, prefill=True)
 
 
 @pytest.mark.parametrize("name", ["full256k_int8", "full256k_fp8"])
@@ -88,7 +88,9 @@ def test_prefill_t_le_8_matches_decode(K):
     bt = H.fill_gpu(K, w, cache, DEV)
     dec = H.run_attn(K, w, cache, bt, DEV)
     pre = H.run_attn(K, w, cache, bt, DEV, prefill=True)
-    assert float((dec - pre).abs().max()) <= 1e-5
+    # the two kernels sum in different orders (chunks, wave ownership): agreement well inside the
+    # 2e-3 bar each holds against the oracle
+    assert float((dec - pre).abs().max()) <= 1e-4
 
 
 def test_prefill_repeat_is_bit_identical(K):
@@ -102,7 +104,7 @@ def test_prefill_repeat_is_bit_identical(K):
 
 @pytest.mark.parametrize("direct", [False, True])
 def test_prefill_bad_tables_give_nan_rows_without_touching_others(K, direct):
-    T = 512 if direct else 40
+    T = 1024 if direct else 40
     w = S.make(S.tiny_shape(B=3, T=T, Hq=16, Hkv=2, D=128, lens=(T + 200, T + 300, T + 100), src=S.SRC_BF16),
                seed=23)
     s = w.shape

@@ -31,6 +31,12 @@ PREFILL = {
     "pf_int8_f32_long": S.tiny_shape(B=1, T=70, Hq=16, Hkv=2, D=128, lens=(5000,), src=S.SRC_F32),
     "pf_fp8_scratch_bf16": S.tiny_shape(B=2, T=130, Hq=24, Hkv=4, D=256, lens=(130, 333), src=S.SRC_BF16,
                                         fmt=S.FMT_FP8_ROW, outliers=True),
+    # bf16 queries over INT8 / FP8 pools take the prefill kernel (128-row blocks): a D=128 FP8 case,
+    # rows that end mid-tile (T*G = 3*50 = 150), and a page-aligned context end
+    "pf_fp8_d128_g3": S.tiny_shape(B=1, T=50, Hq=6, Hkv=2, D=128, lens=(700,), src=S.SRC_BF16, fmt=S.FMT_FP8_ROW,
+                                   outliers=True),
+    "pf_int8_b3_ragged": S.tiny_shape(B=3, T=33, Hq=8, Hkv=1, D=256, lens=(33, 64, 1025), src=S.SRC_BF16,
+                                      outliers=True),
 }
 
 

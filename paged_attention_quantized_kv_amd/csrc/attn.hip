@@ -15,14 +15,20 @@
 // dimension of 16x16x32 f16 matrix-core products, so every KV byte is read once:
 //   S^T[key][row] = K[key][dim] * Q^T[dim][row]   (A = K codes, B = Q)
 //   O^T[dim][row] = V^T[dim][key] * P^T[key][row] (A = V codes, B = softmax weights)
-// Per page the team exchanges row maxima and softmax weights through LDS (two
-// barriers); the next page's codes and scales are already in flight in a
-// second register buffer.  K/V codes are converted to f16 exactly (int8 via
-// byte permutes and one packed subtract, FP8 via the hardware converter);
-// softmax weights enter as f16 hi+lo pairs, fp32 queries as hi+lo, bf16
-// queries as one f16 (exact in f16's normal range), so the rounding is fp32
-// summation.  The page layout (kvq.h) makes each 64-lane 16-byte load one
-// contiguous KiB that lands in the operand registers.
+// Per page the team exchanges row maxima and softmax weights through LDS with one
+// barrier (the weights are written optimistically against a lazily moved reference
+// maximum; a rare second barrier settles a page whose maximum passed it); the next
+// page's codes and scales are already in flight in a second register buffer.  K/V codes
+// are converted to f16 exactly (int8 via byte permutes and one packed subtract, FP8 via
+// the hardware converter, 4-bit codes via masks or a byte-permute table); softmax
+// weights enter as f16 hi+lo pairs, fp32 queries as hi+lo, bf16 queries as one f16
+// (exact in f16's normal range), so the rounding is fp32 summation.  The BF16 pool
+// enters bf16 matrix-core products as it is.  The page layout (kvq.h) makes each
+// 64-lane 16-byte load one contiguous KiB that lands in the operand registers.
+//
+// Prefill (T query rows per sequence, any T) runs either the split kernel's APP = 2
+// instance (64-row blocks) or, for INT8 and FP8 pools with bf16 queries, prefill_kernel
+// (128-row blocks whose waves own their rows; see there).
 #include <type_traits>
 
 #include "quant_row.h"

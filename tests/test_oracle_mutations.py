@@ -5,6 +5,7 @@ dropped term, a wrong sign, index or operand order), builds it with gcc, and run
 oracle pin suite against it: the suite must fail.  The unmodified copy must pass.
 CPU only; the oracle itself is never modified.
 """
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -78,14 +79,28 @@ def _pins_pass(so):
     return r.returncode == 0, r.stdout[-2000:]
 
 
-def test_unmodified_copy_passes(tmp_path):
-    ok, out = _pins_pass(_build(tmp_path, open(SRC).read(), "clean"))
+@pytest.fixture(scope="module")
+def outcomes(tmp_path_factory):
+    """Every copy (the clean one and each planted mistake) built and run through the pins,
+    several at a time (each run is its own process): name -> (pins passed, output tail)."""
+    text = open(SRC).read()
+    cases = {"clean": text}
+    for name, orig, bad in MUTATIONS:
+        assert text.count(orig) == 1, f"mutation site of {name} not found exactly once"
+        cases[name] = text.replace(orig, bad)
+    tmp = tmp_path_factory.mktemp("mutations")
+    workers = max(1, min(8, (os.cpu_count() or 2) - 1))
+    with concurrent.futures.ThreadPoolExecutor(workers) as pool:
+        futs = {name: pool.submit(lambda n=name, t=src: _pins_pass(_build(tmp, t, n))) for name, src in cases.items()}
+        return {name: f.result() for name, f in futs.items()}
+
+
+def test_unmodified_copy_passes(outcomes):
+    ok, out = outcomes["clean"]
     assert ok, out
 
 
-@pytest.mark.parametrize("name,orig,bad", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_planted_mistake_is_caught(tmp_path, name, orig, bad):
-    text = open(SRC).read()
-    assert text.count(orig) == 1, f"mutation site of {name} not found exactly once"
-    ok, out = _pins_pass(_build(tmp_path, text.replace(orig, bad), name))
+@pytest.mark.parametrize("name", [m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(outcomes, name):
+    ok, _ = outcomes[name]
     assert not ok, f"the pins did not catch {name}"

@@ -290,3 +290,26 @@ def test_check_tables_counts_bad_lengths_and_block_ids(K):
                          w.max_seq_len)
     torch.cuda.synchronize()
     assert res.tolist() == [1, 2]
+
+
+def test_cohort_member_matches_its_own_single_sequence_run(K):
+    """Sequence b of a ragged cohort sharing one pool (pages interleaved by the shuffled
+    table) gives, to within summation order, what it gives run alone."""
+    w = S.make(S.tiny_shape(B=4, T=4, Hq=24, Hkv=4, D=256, lens=(900, 3000, 64, 1777), src=S.SRC_BF16,
+                            outliers=True), seed=61)
+    s = w.shape
+    cache = H.new_cache(K, w, DEV)
+    bt = H.fill_gpu(K, w, cache, DEV)
+    cohort = H.run_attn(K, w, cache, bt, DEV)
+    q = H.src_tensor(w.q, s.src, DEV)
+    for b in range(s.B):
+        L = int(w.seq_lens[b])
+        sl = torch.tensor([L], dtype=torch.int32, device=DEV)
+        qb = q[b:b + 1].contiguous()
+        out = torch.empty(qb.shape, dtype=torch.float32, device=DEV)
+        ws = K.alloc_workspace(cache, 1, s.T, s.Hq, L, device=DEV)
+        K.paged_decode_attn(cache, qb, bt[b:b + 1].contiguous(), sl, L, w.softmax_scale, out, ws)
+        torch.cuda.synchronize()
+        err = float((out[0] - cohort[b]).abs().max())
+        say(f"[cohort] seq {b} L={L}: max-abs difference {err:.2e}")
+        assert err <= 1e-4

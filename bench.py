@@ -35,7 +35,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
 HEADLINE = "mtp128k"
 DEPTHS = ["qwen32k", "mtp128k", "full256k_int8", "full256k_fp8", "mtp128k_rk8v4", "mtp128k_rk4v4", "mtp128k_bf16",
-          "full256k_bf16"]
+          "full256k_bf16", "full256k_rk8v4", "full256k_rk4v4"]
 SETTLE_S = 0.2  # seconds of untimed back-to-back steps before the warmup steps
 FLUSH_BYTES = 1.5 * 2 ** 30  # bytes read between two reads of one pool copy (> 256 MB MALL)
 KERNEL_SOURCES = ("internal.h", "quant_row.h", "attn.hip")  # what the split kernel is built from
@@ -332,7 +332,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=HEADLINE, choices=["tiny", "qwen32k", "mtp128k", "mtp128k_rk8v4", "mtp128k_rk4v4", "mtp128k_bf16", "full256k_bf16", "c8",
+    ap.add_argument("--workload", default=HEADLINE, choices=["tiny", "qwen32k", "mtp128k", "mtp128k_rk8v4", "mtp128k_rk4v4", "mtp128k_bf16", "full256k_bf16",
+                                                             "full256k_rk8v4", "full256k_rk4v4", "c8",
                                                              "full256k_int8",
                                                              "full256k_fp8"])
     ap.add_argument("--headline-only", action="store_true", help="skip the other depths")

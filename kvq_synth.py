@@ -19,6 +19,7 @@ tokens; shapes after NInfer-4090 README "What this fork changes", d256-h24-kv4):
               4-bit group-32 values)
   mtp128k_rk4v4  the same in the rk4v4 format (4-bit Lloyd-Max keys)
   mtp128k_bf16, full256k_bf16  the same data in the BF16 reference format
+  full256k_rk8v4, full256k_rk4v4  full256k's data (T=1) in the rotated formats
 
 Every pool starts filled with poison (code bytes 0x7F, NaN scales), so a read of
 a slot that was never appended shows up as NaN in the output.  Block-table
@@ -43,7 +44,8 @@ SRC_BF16 = 1
 
 CONFIG_NAMES = ["tiny", "qwen32k", "mtp128k", "c8", "full256k_int8", "full256k_fp8"]
 _SEED_INDEX = {"tiny": 0, "qwen32k": 1, "mtp128k": 2, "c8": 3, "full256k_int8": 4, "full256k_fp8": 4,
-               "mtp128k_rk8v4": 2, "mtp128k_rk4v4": 2, "mtp128k_bf16": 2, "full256k_bf16": 4}
+               "mtp128k_rk8v4": 2, "mtp128k_rk4v4": 2, "mtp128k_bf16": 2, "full256k_bf16": 4,
+               "full256k_rk8v4": 4, "full256k_rk4v4": 4}
 
 
 @dataclasses.dataclass
@@ -80,6 +82,10 @@ def shape(name: str, **over) -> Shape:
         s = Shape(name, 1, 4, 24, 4, 256, [131072], SRC_BF16, FMT_BF16, True)
     elif name == "full256k_bf16":
         s = Shape(name, 1, 1, 24, 4, 256, [262144], SRC_BF16, FMT_BF16, True)
+    elif name == "full256k_rk8v4":
+        s = Shape(name, 1, 1, 24, 4, 256, [262144], SRC_BF16, FMT_RK8V4, True)
+    elif name == "full256k_rk4v4":
+        s = Shape(name, 1, 1, 24, 4, 256, [262144], SRC_BF16, FMT_RK4V4, True)
     elif name == "mtp128k_rk4v4":
         s = Shape(name, 1, 4, 24, 4, 256, [131072], SRC_BF16, FMT_RK4V4, True)
     elif name == "full256k_fp8":

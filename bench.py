@@ -14,7 +14,7 @@ Inputs are seeded synthetic data (kvq_synth) already resident in HBM.  Steps
 rotate over several copies of the page pool so the 256 MB Infinity Cache never
 holds the pool a step reads: every timed byte comes from HBM.
 
-Prints ONE JSON line.  --gpus N > 1 exits: this build runs on one GPU.
+Prints ONE JSON line.  --gpus N > 1 exits: the library runs on one GPU (multi-GPU sharding is a design only).
 """
 from __future__ import annotations
 
@@ -343,7 +343,7 @@ def main():
                     help="before timing, copy a buffer of this many MiB once (a known-size kernel for counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
               "(the multi-GPU sharding is a design only)", file=sys.stderr)
         sys.exit(2)
 

@@ -313,3 +313,31 @@ def test_cohort_member_matches_its_own_single_sequence_run(K):
         err = float((out[0] - cohort[b]).abs().max())
         say(f"[cohort] seq {b} L={L}: max-abs difference {err:.2e}")
         assert err <= 1e-4
+
+
+def _lens(seed, B, lo, hi):
+    return tuple(int(x) for x in np.random.default_rng(seed).integers(lo, hi + 1, size=B))
+
+
+MANY = {
+    "b64_t4_int8": S.tiny_shape(B=64, T=4, Hq=24, Hkv=4, D=256, lens=_lens(73, 64, 4, 3000), src=S.SRC_BF16,
+                                outliers=True, name="b64_t4_int8"),
+    "b300_t1_int8": S.tiny_shape(B=300, T=1, Hq=24, Hkv=4, D=256, lens=_lens(71, 300, 1, 400), src=S.SRC_BF16,
+                                 outliers=True, name="b300_t1_int8"),
+    "b1024_t2_fp8": S.tiny_shape(B=1024, T=2, Hq=8, Hkv=2, D=128, lens=_lens(72, 1024, 2, 150), src=S.SRC_F32,
+                                 fmt=S.FMT_FP8_ROW, name="b1024_t2_fp8"),
+}
+
+
+@pytest.mark.parametrize("name", list(MANY))
+def test_many_sequences(K, name):
+    """Cohorts up to the 1024-sequence limit with ragged contexts (lengths down to T):
+    B * Hkv reaches or passes the 256 workgroups a launch aims for, so each (sequence,
+    KV head) is one chunk; both the two-call path and the fused step."""
+    shp = MANY[name]
+    n_splits, _ = K.num_splits(shp.B, shp.T, shp.Hq, shp.Hkv, shp.D, max(shp.lens))
+    assert n_splits == 1
+    w = S.make(shp, seed=S.seed_of("tiny") + 500 + list(MANY).index(name))
+    rows = _sample_rows(w, 2)  # two heads of the first and last row of every sequence
+    check(K, w, rows=rows)
+    _fused_check(K, w, rows=rows)

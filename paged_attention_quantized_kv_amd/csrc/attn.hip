@@ -422,7 +422,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   // the first pages load while the queries are staged (and, for the fused step, the new
   // rows read) -- unless one of them holds new rows, which must be written first
   const bool early = (APP != 1) || (page0 + NTEAM - 1 < (L - a.T) / kPage);
-  if (early && n_it > 0) load_page<D, FMT>(rA, a, page_of(0), wave, lane, q4);
+  if (early && n_it > 0) load_k_part<D, FMT>(rA, a, page_of(0), wave, lane, q4);
 
   // ---- queries -> LDS in B-operand order: entry (nt, cg, hk, hl, lane) holds dims
   // 64cg + 16(lane/16) + 8hk + 0..7 of row 16nt + lane%16, as f16 hi (hl=0) or lo (hl=1).
@@ -511,6 +511,8 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
       if ((tid >> 6) < n_rows) __builtin_amdgcn_s_waitcnt(0);
     }
   }
+  // the first page's V half goes out after the staging, so its K half arrives first
+  if (early && n_it > 0) load_v_part<D, FMT>(rA, a, page_of(0), wave, lane, q4);
   __syncthreads();
   if (!early && n_it > 0) load_page<D, FMT>(rA, a, page_of(0), wave, lane, q4);
 

@@ -999,104 +999,68 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   }
 }
 
-// Merge kernel: one workgroup of 256 threads per 64-dim slice of an output row
-// (b, t, h).  Every load is issued up front: thread (sl, c4) holds 4 dims of up to
-// MPER chunks of chunk slice sl, and the chunk maxima and sums are read beside them;
-// block reductions give the log-sum-exp weights; the chunk slices are summed in a
-// fixed order (deterministic).
-__device__ inline float block_max(float v, float *red) {
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
-__device__ inline float block_sum(float v, float *red) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
-}
-
+// Merge kernel: one wave per 64-dim slice of an output row (b, t, h).  Lane l holds
+// float4 column l % 16 of the slice for the chunks s = l / 16 + 4k, with each chunk's
+// maximum and sum; every load is issued at once, beside the sequence length.  All
+// n_splits chunk slots lie in the workspace; slots past the chunks that hold the row's
+// keys carry stale values and are dropped by selection.  The log-sum-exp weights and
+// the sums over the four chunk groups use cross-lane swaps only (no LDS, no barrier),
+// in a fixed order (deterministic).
 template <int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  constexpr int NQ = D / 64;       // 64-dim slices of a row, one workgroup each
-  constexpr int CS = 16;           // float4 columns of a slice
-  constexpr int NSL = 256 / CS;    // chunk slices
-  constexpr int MPER = 8;          // chunks per thread kept in registers
-  constexpr int MAXS = kMergeMaxSplits;
-  __shared__ float w_s[MAXS];
-  __shared__ float red[4];
-  __shared__ float4 acc_s[NSL][CS];
-  const int row = blockIdx.x / NQ, qs = blockIdx.x % NQ, tid = threadIdx.x;
+__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
+  constexpr int NQ = D / 64;  // 64-dim slices of a row, one wave each
+  constexpr int MPER = 16;    // chunks per lane held in registers (all of them up to 64 chunks)
+  const int row = blockIdx.x / NQ, qs = blockIdx.x % NQ, lane = threadIdx.x;
   const int h = row % a.num_q_heads, t = (row / a.num_q_heads) % a.T, b = row / (a.num_q_heads * a.T);
   float *dst = a.out + static_cast<size_t>(row) * D + 64 * qs;
+  const int kvh = h / a.group, r = t * a.group + h % a.group;
+  const size_t part0 = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits;
+  const int c4 = lane & 15, sg = lane >> 4, col = qs * 16 + c4;
+  const float2 *ml2 = reinterpret_cast<const float2 *>(a.ws_ml);
+  auto o_at = [&](int s) { return reinterpret_cast<const float4 *>(a.ws_o + ((part0 + s) * a.rows + r) * D)[col]; };
+
+  float4 x[MPER];
+  float2 ml[MPER];
+#pragma unroll
+  for (int k = 0; k < MPER; ++k) {
+    const int s = min(sg + 4 * k, a.n_splits - 1);
+    x[k] = o_at(s);
+    ml[k] = ml2[(part0 + s) * a.rows + r];
+  }
   const int L = a.seq_lens[b];
   if (L < a.T || L > a.max_seq_len || L > a.max_blocks * kPage) {
-    if (tid < 64) dst[tid] = NAN;
+    dst[lane] = NAN;
     return;
   }
-  const int kvh = h / a.group, r = t * a.group + h % a.group;
   // chunks holding keys this row sees (later chunks were skipped or hold none of them)
   const int ns = (L - a.T + t + a.tokens_per_split) / a.tokens_per_split;
-  const size_t part0 = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits;
-  const int c4 = tid % CS, sl = tid / CS, col = qs * CS + c4;
-
-  // ---- issue the first MPER partial-output loads of this thread and the chunk statistics
-  float4 x[MPER];
+  float mloc = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < MPER; ++k) {
-    const int s = min(sl + k * NSL, ns - 1);
-    x[k] = reinterpret_cast<const float4 *>(a.ws_o + ((part0 + s) * a.rows + r) * D)[col];
-  }
-  float mx = -INFINITY;
-  for (int s = tid; s < ns; s += 256) mx = fmaxf(mx, a.ws_ml[((part0 + s) * a.rows + r) * 2]);
-  const float M = block_max(mx, red);
+  for (int k = 0; k < MPER; ++k)
+    if (sg + 4 * k < ns) mloc = fmaxf(mloc, ml[k].x);
+  for (int s = sg + 4 * MPER; s < ns; s += 4) mloc = fmaxf(mloc, ml2[(part0 + s) * a.rows + r].x);
+  const float M = max_xor32(max_xor16(mloc));
   const float Ms = (M == -INFINITY) ? 0.0f : M;
-  float lt = 0.0f;
-  for (int s = tid; s < ns; s += 256) {
-    const size_t pr = (part0 + s) * a.rows + r;
-    const float w = exp2f(a.ws_ml[pr * 2] - Ms);
-    if (s < MAXS) w_s[s] = w;
-    lt += w * a.ws_ml[pr * 2 + 1];
-  }
-  const float Lt = block_sum(lt, red);  // its barriers also publish w_s
-  auto weight = [&](int s) -> float {
-    return (s < MAXS) ? w_s[s] : exp2f(a.ws_ml[((part0 + s) * a.rows + r) * 2] - Ms);
-  };
   float4 acc = make_float4(0, 0, 0, 0);
-#pragma unroll
-  for (int k = 0; k < MPER; ++k) {
-    const int s = sl + k * NSL;
-    const float w = (s < ns) ? weight(s) : 0.0f;
-    acc.x += w * x[k].x;
-    acc.y += w * x[k].y;
-    acc.z += w * x[k].z;
-    acc.w += w * x[k].w;
-  }
-  for (int s = sl + MPER * NSL; s < ns; s += NSL) {  // long contexts with many chunks
-    const float w = weight(s);
-    const float4 y = reinterpret_cast<const float4 *>(a.ws_o + ((part0 + s) * a.rows + r) * D)[col];
+  float lt = 0.0f;
+  auto add = [&](float2 st, float4 y) {
+    const float w = exp2f(st.x - Ms);
+    lt += w * st.y;
     acc.x += w * y.x;
     acc.y += w * y.y;
     acc.z += w * y.z;
     acc.w += w * y.w;
-  }
-  acc_s[sl][c4] = acc;
-  __syncthreads();
-  if (tid < CS) {
-    float4 v = acc_s[0][tid];
+  };
 #pragma unroll
-    for (int k = 1; k < NSL; ++k) {
-      const float4 y = acc_s[k][tid];
-      v.x += y.x;
-      v.y += y.y;
-      v.z += y.z;
-      v.w += y.w;
-    }
-    reinterpret_cast<float4 *>(dst)[tid] = make_float4(v.x / Lt, v.y / Lt, v.z / Lt, v.w / Lt);
-  }
+  for (int k = 0; k < MPER; ++k)
+    if (sg + 4 * k < ns) add(ml[k], x[k]);
+  for (int s = sg + 4 * MPER; s < ns; s += 4) add(ml2[(part0 + s) * a.rows + r], o_at(s));  // long contexts
+  lt = sum_xor32(sum_xor16(lt));
+  acc.x = sum_xor32(sum_xor16(acc.x));
+  acc.y = sum_xor32(sum_xor16(acc.y));
+  acc.z = sum_xor32(sum_xor16(acc.z));
+  acc.w = sum_xor32(sum_xor16(acc.w));
+  if (sg == 0) reinterpret_cast<float4 *>(dst)[c4] = make_float4(acc.x / lt, acc.y / lt, acc.z / lt, acc.w / lt);
 }
 
 // ---- Prefill kernel for INT8 and FP8 pools with bf16 queries.
@@ -1511,7 +1475,7 @@ hipError_t prefill_one(const AttnArgs &a, hipStream_t s) {
 
 template <int D>
 hipError_t merge_one(const AttnArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(a.num_seqs * a.T * a.num_q_heads * (D / 64)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(a.num_seqs * a.T * a.num_q_heads * (D / 64)), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -28,7 +28,6 @@ constexpr int kMaxPrefillChunkPages = 4096;  // the same for prefill (262,144 to
 constexpr int kPrefillNT = KVQ_PREFILL_NT;        // 16-row tiles of a prefill row block
 constexpr int kPrefillTeams = KVQ_PREFILL_TEAMS;  // 4-wave teams of a prefill workgroup
 constexpr int kPrefillRows = 16 * kPrefillNT;   // query rows (t*G + g) of a prefill row block
-constexpr int kMergeMaxSplits = 1024; // chunk weights the merge keeps in LDS
 constexpr int kBulkAppendRows = 64;   // appends of at least this many rows per sequence go page by page
 
 // Launch arguments of kv_append_quant, validated on the host.

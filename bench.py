@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
 HEADLINE = "mtp128k"
-DEPTHS = ["qwen32k", "mtp128k", "full256k_int8", "full256k_fp8", "mtp128k_rk8v4", "mtp128k_rk4v4", "mtp128k_bf16",
+DEPTHS = ["qwen32k", "mtp128k", "c8", "full256k_int8", "full256k_fp8", "mtp128k_rk8v4", "mtp128k_rk4v4", "mtp128k_bf16",
           "full256k_bf16", "full256k_rk8v4", "full256k_rk4v4"]
 SETTLE_S = 0.2  # seconds of untimed back-to-back steps before the warmup steps
 FLUSH_BYTES = 1.5 * 2 ** 30  # bytes read between two reads of one pool copy (> 256 MB MALL)

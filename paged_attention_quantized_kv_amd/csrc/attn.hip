@@ -1065,13 +1065,14 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
 
 // ---- Prefill kernel for INT8 and FP8 pools with bf16 queries.
 //
-// A workgroup of 4 waves owns 128 query rows (t*G + g) of one KV head and one chunk of
-// its context; wave w owns rows 32w .. 32w+31 outright: their queries stay in registers
+// A workgroup of 8 waves owns 128 query rows (t*G + g) of one KV head and one chunk of
+// its context; wave w owns rows 16w .. 16w+15 outright (KVQ_PREFILL_NTW = 2 builds 4
+// waves of 32 rows instead, one wave per SIMD): their queries stay in registers
 // as the B operands of S^T = K Q^T, their softmax state and their output O^T = V^T P^T
 // (all D dims) stay in the wave, and the weights go from the score registers straight
 // into the P·V products (the V layout puts each lane's keys where the S^T tile leaves
 // them), so no wave waits on another for softmax.  The K and V codes of a page are
-// converted to f16 once per workgroup, by all 256 threads, into LDS (double-buffered:
+// converted to f16 once per workgroup, by all its threads, into LDS (double-buffered:
 // page p+1 is converted while page p is multiplied, page p+2 is in flight from HBM), and
 // every wave reads its matrix-core A operands from there: one barrier per page.
 #ifndef KVQ_PREFILL_NTW

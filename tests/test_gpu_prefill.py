@@ -130,3 +130,27 @@ def test_prefill_bad_tables_give_nan_rows_without_touching_others(K, direct):
     say(f"[prefill bad tables] direct={direct}")
     assert torch.equal(out[0], good[0])
     assert torch.isnan(out[1]).all() and torch.isnan(out[2]).all()
+
+
+def _ragged(seed, B, lo, hi):
+    return tuple(int(x) for x in np.random.default_rng(seed).integers(lo, hi + 1, size=B))
+
+
+MANY_PF = {
+    # 40 sequences x 2 row blocks x 4 KV heads: one chunk per row block, rows written directly
+    "pf_b40_direct": dict(B=40, T=40, Hq=24, Hkv=4, D=256, lens=(40,) + _ragged(81, 39, 40, 900)),
+    # 8 sequences x 2 row blocks x 1 KV head: chunked contexts and a merge
+    "pf_b8_merged": dict(B=8, T=20, Hq=8, Hkv=1, D=128, lens=(20,) + _ragged(82, 7, 20, 3000)),
+}
+
+
+@pytest.mark.parametrize("fmt", [S.FMT_INT8_G64, S.FMT_FP8_ROW, S.FMT_RK8V4])
+@pytest.mark.parametrize("name", list(MANY_PF))
+def test_prefill_many_sequences(K, name, fmt):
+    """Prefill batches of many sequences with ragged contexts (lengths down to T, so some
+    sequences prefill from an empty cache): chunks are sized from the longest context and
+    the short sequences' later chunks are skipped; both launch modes, sampled rows."""
+    shp = S.tiny_shape(src=S.SRC_BF16, fmt=fmt, outliers=True, name=name, **MANY_PF[name])
+    w = S.make(shp, seed=S.seed_of("tiny") + 700 + 10 * list(MANY_PF).index(name) + fmt)
+    assert _direct(K, w.shape, w.max_seq_len) == name.endswith("direct")
+    check(K, w, rows=_prefill_rows(w, (0, 1, shp.T - 1), 2), chunk=128, prefill=True)

@@ -341,3 +341,19 @@ def test_many_sequences(K, name):
     rows = _sample_rows(w, 2)  # two heads of the first and last row of every sequence
     check(K, w, rows=rows)
     _fused_check(K, w, rows=rows)
+
+
+@pytest.mark.parametrize("shp", [
+    S.tiny_shape(B=1, T=2, Hq=8, Hkv=1, D=128, lens=(20000,), src=S.SRC_F32, name="splits157_f32"),
+    S.tiny_shape(B=2, T=1, Hq=4, Hkv=1, D=128, lens=(40000, 9000), src=S.SRC_BF16, fmt=S.FMT_FP8_ROW,
+                 outliers=True, name="splits105_fp8"),
+], ids=lambda s: s.name)
+def test_merge_of_more_than_64_chunks(K, shp):
+    """One KV head and long contexts: more than 64 chunks per row, past the chunks the
+    merge holds in registers (its loop over the rest), with a short second sequence
+    whose rows stop early among them; both paths."""
+    n_splits, _ = K.num_splits(shp.B, shp.T, shp.Hq, shp.Hkv, shp.D, max(shp.lens))
+    assert n_splits > 64
+    w = S.make(shp, seed=S.seed_of("tiny") + 800 + shp.B)
+    check(K, w)
+    _fused_check(K, w)

@@ -1,6 +1,12 @@
-"""Build libkvq.so (the HIP C-ABI library) in-tree with hipcc for gfx950."""
+"""Build libkvq.so (the HIP C-ABI library) in-tree with hipcc for gfx950.
+
+Every source is compiled to an object of its own, in parallel (the attention
+kernels are split by KV format over attn_f<FMT>.hip), then linked into one
+shared library.
+"""
 from __future__ import annotations
 
+import concurrent.futures as cf
 import os
 import subprocess
 import sys
@@ -8,29 +14,45 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kvq_api.hip", "append.hip", "attn.hip", "check.hip")]
-HEADERS = [os.path.join(HERE, "csrc", "internal.h"), os.path.join(ROOT, "include", "kvq.h")]
+OBJ_DIR = os.path.join(HERE, "_build")
+SOURCES = [os.path.join(HERE, "csrc", f) for f in
+           ("kvq_api.hip", "append.hip", "attn.hip", "attn_f0.hip", "attn_f1.hip", "attn_f2.hip", "attn_f3.hip",
+            "attn_f4.hip", "check.hip")]
+HEADERS = [os.path.join(HERE, "csrc", f) for f in ("internal.h", "quant_row.h", "attn_kernels.h")] + \
+          [os.path.join(ROOT, "include", "kvq.h")]
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # IEEE fp32 division: quantization codes are decided by x / scale
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     # no packed-fp32 instructions in any kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
+NOISE = "is not a recognized feature for this target"
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    cmd = [hipcc] + HIPCC_FLAGS + SOURCES + ["-o", LIB + ".tmp"]
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + err)
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+    err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if NOISE not in l)
+    return r.returncode, err
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    objs = [os.path.join(OBJ_DIR, os.path.basename(s)[:-4] + ".o") for s in SOURCES]
+    jobs = jobs or min(len(SOURCES), max(1, min(16, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        res = list(ex.map(lambda so: _run([hipcc] + HIPCC_FLAGS + ["-c", so[0], "-o", so[1]]), zip(SOURCES, objs)))
+    for (rc, err), src in zip(res, SOURCES):
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n" + err)
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+    rc, err = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", LIB + ".tmp"])
+    if rc != 0:
+        raise RuntimeError("hipcc link failed:\n" + err)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -1,1514 +1,41 @@
-// attn.hip -- paged decode attention over the quantized page pool.
-//
-// The result is out = softmax(q k^T * scale) v over the dequantized cache,
-// which every decode step reads in full (NInfer-3090 README, "Choosing a KV
-// format"); the context of each (sequence, KV head) is cut into
-// chunks (split-K over the context) whose partial results are merged with
-// log-sum-exp weights.
-//
-// Split kernel: a workgroup owns one chunk of one (sequence, KV head) and runs
-// NTEAM teams of 4 waves; team t takes the chunk's pages t, t+NTEAM, ...  The
-// 4 waves of a team share each page: wave w computes the scores of key tile w
-// (16 keys) and accumulates the output for dim quarter w, so a wave holds a
-// quarter of the page and a quarter of the output.  All T*G query rows of the
-// KV head (T new tokens x G query heads of the group) ride along as the N
-// dimension of 16x16x32 f16 matrix-core products, so every KV byte is read once:
-//   S^T[key][row] = K[key][dim] * Q^T[dim][row]   (A = K codes, B = Q)
-//   O^T[dim][row] = V^T[dim][key] * P^T[key][row] (A = V codes, B = softmax weights)
-// Per page the team exchanges row maxima and softmax weights through LDS with one
-// barrier (the weights are written optimistically against a lazily moved reference
-// maximum; a rare second barrier settles a page whose maximum passed it); the next
-// page's codes and scales are already in flight in a second register buffer.  K/V codes
-// are converted to f16 exactly (int8 via byte permutes and one packed subtract, FP8 via
-// the hardware converter, 4-bit codes via masks or a byte-permute table); softmax
-// weights enter as f16 hi+lo pairs, fp32 queries as hi+lo, bf16 queries as one f16
-// (exact in f16's normal range), so the rounding is fp32 summation.  The BF16 pool
-// enters bf16 matrix-core products as it is.  The page layout (kvq.h) makes each
-// 64-lane 16-byte load one contiguous KiB that lands in the operand registers.
-//
-// Prefill (T query rows per sequence, any T) runs either the split kernel's APP = 2
-// instance (64-row blocks) or, for INT8 and FP8 pools with bf16 queries, prefill_kernel
-// (128-row blocks whose waves own their rows; see there).
-#include <type_traits>
-
-#include "quant_row.h"
+// attn.hip -- dispatch of the attention launches by KV format, and the merge launch.
+// The kernels live in attn_kernels.h; each format's instances are compiled in attn_f<FMT>.hip.
+#include "attn_kernels.h"
 
 namespace kvq {
-namespace {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-
-__device__ inline f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-// the BF16 format: bf16 operands, taken straight from the pool
-__device__ inline f32x4 mfma16_bf(uint4 a, uint4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-// x = hi + mid + lo exactly enough for the BF16 format's P (24 significant bits): hi and
-// mid are x and its residual cut to bf16 (exact residuals), lo the last residual rounded.
-// Returns the bf16 pairs of two values x0, x1 packed per term.
-__device__ inline void split_bf16x3(float x0, float x1, uint32_t &hi, uint32_t &mid, uint32_t &lo) {
-  const float h0 = __uint_as_float(__float_as_uint(x0) & 0xFFFF0000u), h1 = __uint_as_float(__float_as_uint(x1) & 0xFFFF0000u);
-  const float r0 = x0 - h0, r1 = x1 - h1;
-  const float m0 = __uint_as_float(__float_as_uint(r0) & 0xFFFF0000u), m1 = __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
-  hi = __builtin_amdgcn_perm(__float_as_uint(h1), __float_as_uint(h0), 0x07060302u);
-  mid = __builtin_amdgcn_perm(__float_as_uint(m1), __float_as_uint(m0), 0x07060302u);
-  lo = f32_to_bf16_rne(r0 - m0) | (f32_to_bf16_rne(r1 - m1) << 16);
-}
-
-// Two signed int8 bytes of x (selected by `sel` after the sign flip) -> two
-// exact f16 values.  Flipping the sign bit maps c to u = c + 128; the f16 with
-// high byte 0x64 and low byte u is 1024 + u, so subtracting 1152 leaves c.
-__device__ inline f16x2 i8pair(uint32_t xflip, uint32_t sel) {
-  const uint32_t p = __builtin_amdgcn_perm(0x64646464u, xflip, sel);
-  const f16x2 h = __builtin_bit_cast(f16x2, p);
-  const _Float16 bias = static_cast<_Float16>(1152.0f);
-  return h - f16x2{bias, bias};
-}
-
-// 8 code bytes (two dwords) -> 8 exact f16 values, in byte order.
-template <int FMT>
-__device__ inline f16x8 codes_to_f16(uint32_t w0, uint32_t w1) {
-  if constexpr (FMT == 0) {
-    const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
-    const f16x2 a = i8pair(x0, 0x04010400u), b = i8pair(x0, 0x04030402u);
-    const f16x2 c = i8pair(x1, 0x04010400u), d = i8pair(x1, 0x04030402u);
-    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-  } else {
-    // OCP E4M3FN -> f16 is exact (3 fraction bits, exponents 2^-9 .. 2^8)
-    const f16x2 a = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false));
-    const f16x2 b = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true));
-    const f16x2 c = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false));
-    const f16x2 d = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true));
-    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-  }
-}
-
-// rk8v4 values: one 32-bit word holds the 4-bit codes (two's complement) of 8 keys,
-// key q at bit 16*(q%2) + 4*(q/2), so masking with 0x000F000F after a shift of 4p
-// gives keys 2p, 2p+1 in the two halves.  Flipping bit 3 of every nibble maps c to
-// n = c + 8; the f16 with bits 0x6400 | n is 1024 + n, so subtracting 1032 leaves c.
-__device__ inline f16x8 v4_to_f16(uint32_t w) {
-  const uint32_t x = w ^ 0x88888888u;
-  const _Float16 bias = static_cast<_Float16>(1032.0f);
-  const f16x2 b2{bias, bias};
-  const f16x2 a = __builtin_bit_cast(f16x2, (x & 0x000F000Fu) | 0x64006400u) - b2;
-  const f16x2 b = __builtin_bit_cast(f16x2, ((x >> 4) & 0x000F000Fu) | 0x64006400u) - b2;
-  const f16x2 c = __builtin_bit_cast(f16x2, ((x >> 8) & 0x000F000Fu) | 0x64006400u) - b2;
-  const f16x2 d = __builtin_bit_cast(f16x2, ((x >> 12) & 0x000F000Fu) | 0x64006400u) - b2;
-  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-// rk4v4 keys: one 32-bit word holds the 4-bit level indices of 8 dims of one key, byte b
-// = dim b (low nibble) and dim b + 4 (high nibble).  Each index becomes its level's INT8
-// code, biased by 128 (a 16-entry byte table read with two byte permutes and a per-byte
-// select on bit 3), and the biased bytes become exact f16 as in i8pair.
-__device__ inline uint32_t rk4_lut(uint32_t sel) {
-  // biased codes c + 128 of the levels -127 -96 -75 -58 -44 -31 -18 -6 6 18 31 44 58 75 96 127
-  constexpr uint32_t T0 = 0x46352001u, T1 = 0x7A6E6154u, T2 = 0xAC9F9286u, T3 = 0xFFE0CBBAu;
-  const uint32_t s7 = sel & 0x07070707u;
-  const uint32_t lo = __builtin_amdgcn_perm(T1, T0, s7), hi = __builtin_amdgcn_perm(T3, T2, s7);
-  const uint32_t m = __builtin_amdgcn_perm(0u, 0u, ((sel >> 3) & 0x01010101u) | 0x0C0C0C0Cu);  // 0x00 / 0xFF
-  return (hi & m) | (lo & ~m);
-}
-__device__ inline f16x8 k4_to_f16(uint32_t w) {
-  const uint32_t a = rk4_lut(w & 0x0F0F0F0Fu), b = rk4_lut((w >> 4) & 0x0F0F0F0Fu);
-  const f16x2 p0 = i8pair(a, 0x04010400u), p1 = i8pair(a, 0x04030402u);
-  const f16x2 p2 = i8pair(b, 0x04010400u), p3 = i8pair(b, 0x04030402u);
-  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
-// x ~= hi + lo with hi = f16(x) rounded toward zero and lo = f16(x - hi): the
-// pair carries ~21 significant bits.
-__device__ inline void split_f16(float x0, float x1, f16x2 &hi, f16x2 &lo) {
-  hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(x0, x1));
-  lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(x0 - static_cast<float>(hi[0]),
-                                                            x1 - static_cast<float>(hi[1])));
-}
-
-// The products p * s as an f16 hi+lo pair when p itself arrives as an f16 hi+lo pair
-// (ph, pl) and s is fp16: hi = f16(ph*s); the residual ph*s - hi is exact in f16, and
-// lo = f16(pl*s + residual).  Three packed f16 operations per pair of keys.
-__device__ inline void scale_pair(f16x2 ph, f16x2 pl, f16x2 s, f16x2 &hi, f16x2 &lo) {
-  hi = ph * s;
-  const f16x2 r = __builtin_elementwise_fma(ph, s, -hi);
-  lo = __builtin_elementwise_fma(pl, s, r);
-}
-
-// The same split of the products p * s (s in fp16): hi = f16(p*s) toward zero, lo =
-// f16(p*s - hi) with the residual taken from the unrounded product; each product and
-// residual is one mixed-precision fma.
-__device__ inline void split_scaled(float p0, float p1, f16x2 s, f16x2 &hi, f16x2 &lo) {
-  const float s0 = static_cast<float>(s[0]), s1 = static_cast<float>(s[1]);
-  hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf(p0, s0, 0.0f), __builtin_fmaf(p1, s1, 0.0f)));
-  lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf(p0, s0, -static_cast<float>(hi[0])),
-                                                            __builtin_fmaf(p1, s1, -static_cast<float>(hi[1]))));
-}
-
-// Element i of the query tensor, widened to fp32 (bf16 widening is exact).
-template <bool BF16>
-__device__ inline float load_q(const void *q, size_t i) {
-  if constexpr (BF16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(q)[i]) << 16);
-  return static_cast<const float *>(q)[i];
-}
-
-__device__ inline f16x8 lds_f16x8(const uint4 *p) { return __builtin_bit_cast(f16x8, *p); }
-
-// Butterfly steps across the 16-lane rows of a wave without LDS: lane l gets
-// op(x[l], x[l ^ 16]) and op(x[l], x[l ^ 32]) via the gfx950 row/half swaps.
-__device__ inline float max_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ inline float max_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ inline float sum_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ inline float sum_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// 2^x with the hardware exponential: exact at 0 and -inf; results below the
-// normal range (weights under 2^-126 of the running maximum) may flush to zero.
-__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Rescaling threshold of the online softmax, log2 units (see the softmax phase).
-constexpr float kLazy = 8.0f;
-
-// One wave's share of one page: its K tile (16 keys x all dims) and its V dim
-// tiles (all 64 keys), with their scales.  rk8v4 (FMT 2): K as INT8; V as 4-bit codes,
-// one 16-byte load per pair of dim tiles, and the fp16 scales of two 32-dim groups.
-template <int D, int FMT>
-struct PageRegs {
-  static constexpr int G64 = D / 64, DPW = D / 64;  // dim tiles per wave = D/16/4
-  // BF16 (FMT 4): 32 bytes of K per (key, 16 dims) and of V per (dim, 16 keys), no scales
-  static constexpr int KSN = (FMT == 1 || FMT == 4) ? 1 : (D / 128);
-  static constexpr int KN = (FMT == 3) ? G64 / 2 : (FMT == 4 ? 2 * G64 : G64);  // rk4v4: 16 bytes per pair of 64-dim groups
-  static constexpr int VN = (FMT == 2 || FMT == 3) ? DPW / 2 : (FMT == 4 ? 2 * DPW : DPW);
-  static constexpr int VSN = (FMT == 0) ? 2 : (FMT == 1 ? 4 : (FMT == 4 ? 1 : DPW));
-  uint4 k[KN];
-  uint4 v[VN];
-  uint4 ks[KSN];
-  uint4 vs[VSN];
-};
-
-// The pages are streamed once per call: load them with the non-temporal hint.
-__device__ inline uint4 ld_stream(const uint4 *p) {
-#if KVQ_NT_LOADS
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-  return make_uint4(t.x, t.y, t.z, t.w);
-#else
-  return *p;
-#endif
-}
-
-// The K half of one wave's share of a page (its key tile and the tile's scales) and
-// the V half (its dim tiles and all 64 keys' scales), issued separately so the loads of
-// the next page spread over the current one.
-template <int D, int FMT>
-__device__ inline void load_k_part(PageRegs<D, FMT> &r, const AttnArgs &a, int pg_any, int wave, int lane, int q4) {
-  constexpr int G64 = D / 64, NCH = D / 16;
-  const size_t pg = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pg_any));  // wave-uniform page
-  const uint4 *kp = reinterpret_cast<const uint4 *>(a.k_codes + pg * kPage * D);
-  if constexpr (FMT == 4) {  // bf16 keys: the INT8 unit u of this lane holds 16 dims, here 2 x 16 bytes
-    const uint4 *kp16 = reinterpret_cast<const uint4 *>(a.k_codes + pg * kPage * D * 2);
-#pragma unroll
-    for (int cg = 0; cg < G64; ++cg) {
-      const int u = (wave * NCH + 4 * cg) * 16 + lane;
-      r.k[2 * cg] = ld_stream(kp16 + 2 * u);
-      r.k[2 * cg + 1] = ld_stream(kp16 + 2 * u + 1);
-    }
-    return;
-  } else if constexpr (FMT == 3) {  // 4-bit keys: (key tile, group pair) units of 1 KiB, 16 bytes per lane
-    const uint4 *kp4 = reinterpret_cast<const uint4 *>(a.k_codes + pg * kPage * (D / 2));
-#pragma unroll
-    for (int p = 0; p < G64 / 2; ++p) r.k[p] = ld_stream(kp4 + (wave * (G64 / 2) + p) * 64 + lane);
-  } else {
-#pragma unroll
-    for (int cg = 0; cg < G64; ++cg) r.k[cg] = ld_stream(kp + (wave * NCH + 4 * cg) * 16 + lane);
-  }
-  if constexpr (FMT != 1) {
-    const uint4 *ksp = reinterpret_cast<const uint4 *>(static_cast<const _Float16 *>(a.k_scales) + pg * D);
-#pragma unroll
-    for (int j = 0; j < PageRegs<D, FMT>::KSN; ++j) r.ks[j] = ksp[(q4 * 4 + wave) * PageRegs<D, FMT>::KSN + j];
-  } else {
-    const uint4 *ksp = reinterpret_cast<const uint4 *>(static_cast<const float *>(a.k_scales) + pg * kPage);
-    r.ks[0] = ksp[q4 * 4 + wave];
-  }
-}
-
-template <int D, int FMT>
-__device__ inline void load_v_part(PageRegs<D, FMT> &r, const AttnArgs &a, int pg_any, int wave, int lane, int q4) {
-  constexpr int G64 = D / 64, DPW = D / 64;
-  const size_t pg = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pg_any));
-  if constexpr (FMT == 4) {  // bf16 values: the INT8 unit u of this lane (16 keys of one dim), here 2 x 16 bytes
-    const uint4 *vp16 = reinterpret_cast<const uint4 *>(a.v_codes + pg * kPage * D * 2);
-#pragma unroll
-    for (int j = 0; j < DPW; ++j) {
-      const int u = (wave * DPW + j) * 64 + lane;
-      r.v[2 * j] = ld_stream(vp16 + 2 * u);
-      r.v[2 * j + 1] = ld_stream(vp16 + 2 * u + 1);
-    }
-    return;
-  }
-  if constexpr (FMT == 2 || FMT == 3) {  // 4-bit codes: tile pair p of the wave is one KiB, 16 bytes per lane
-    const uint4 *vp = reinterpret_cast<const uint4 *>(a.v_codes + pg * kPage * (D / 2));
-#pragma unroll
-    for (int p = 0; p < DPW / 2; ++p) r.v[p] = ld_stream(vp + (wave * (DPW / 2) + p) * 64 + lane);
-    const uint4 *vsp = reinterpret_cast<const uint4 *>(static_cast<const _Float16 *>(a.v_scales) + pg * (kPage * D / 32));
-#pragma unroll
-    for (int p = 0; p < DPW / 2; ++p)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) r.vs[2 * p + j] = vsp[(q4 * (D / 32) + wave * (DPW / 2) + p) * 2 + j];
-    return;
-  }
-  const uint4 *vp = reinterpret_cast<const uint4 *>(a.v_codes + pg * kPage * D);
-#pragma unroll
-  for (int j = 0; j < DPW; ++j) r.v[j] = ld_stream(vp + (wave * DPW + j) * 64 + lane);
-  if constexpr (FMT == 0) {
-    const uint4 *vsp = reinterpret_cast<const uint4 *>(static_cast<const _Float16 *>(a.v_scales) + pg * D);
-    const int g = (wave * DPW) / 4;  // the 64-dim group of this wave's dims
-#pragma unroll
-    for (int j = 0; j < 2; ++j) r.vs[j] = vsp[(q4 * G64 + g) * 2 + j];
-  } else {
-    const uint4 *vsp = reinterpret_cast<const uint4 *>(static_cast<const float *>(a.v_scales) + pg * kPage);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r.vs[j] = vsp[q4 * 4 + j];
-  }
-}
-
-template <int D, int FMT>
-__device__ inline void load_page(PageRegs<D, FMT> &r, const AttnArgs &a, int pg_any, int wave, int lane, int q4) {
-  load_k_part<D, FMT>(r, a, pg_any, wave, lane, q4);
-  load_v_part<D, FMT>(r, a, pg_any, wave, lane, q4);
-}
-
-__device__ inline void f16x2_to_f32(uint32_t w, float &x, float &y) {
-  const f16x2 h = __builtin_bit_cast(f16x2, w);
-  x = static_cast<float>(h[0]);
-  y = static_cast<float>(h[1]);
-}
-
-template <int D, int NT, int NTEAM, int QP>
-struct Smem {
-  static constexpr int ROWS = 16 * NT, PST = 64 + 4, G64 = D / 64;
-  static constexpr int QS = NT * G64 * 2 * QP * 64;            // Q operand entries (uint4)
-  static constexpr int PB = NTEAM * 2 * ROWS * PST;             // softmax-weight exchange (floats)
-  static constexpr int FIN = (NTEAM > 1 ? NTEAM - 1 : 1) * ROWS * (D + 4);  // team merge (floats), aliases pb
-  static constexpr int PBF = PB > FIN ? PB : FIN;
-};
-
-// APP: 1 = also quantize and append the T new rows of each sequence (the fused
-// decode step; the source dtype is the query dtype), 0 = the cache is complete,
-// 2 = prefill: the query rows come in blocks of 16*NT rows (grid y = row block * Hkv
-// + KV head), chunks hold up to kMaxPrefillChunkPages pages, and with one chunk per
-// row block the normalized rows go straight to out.
-// QLO: 0 = bf16 queries entering as one f16 each; 1 = fp32 queries as f16 hi + lo;
-// 2 = bf16 queries rotated for rk8v4 keys (FMT 2), which no longer fit one f16: hi + lo.
-template <int D, int NT, int FMT, int QLO, int NTEAM, int APP>
-__global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) {
-  constexpr int G64 = D / 64, NCH = D / 16, DPW = D / 64;
-  constexpr int QP = QLO ? 2 : 1;
-  constexpr int KF = (FMT == 2) ? 0 : FMT;  // key code format: rk8v4 keys are INT8 group-64
-  static_assert(FMT != 2 && FMT != 3 || QLO != 0, "rotated queries need the lo part");
-  using SM = Smem<D, NT, NTEAM, QP>;
-  constexpr int ROWS = SM::ROWS, PST = SM::PST;
-  __shared__ uint4 qs[SM::QS];
-  __shared__ float4 pbuf4[SM::PBF / 4];
-  __shared__ float4 lds_mx[NTEAM][2][ROWS];  // per row: the 4 waves' page maxima
-  __shared__ int32_t lds_over[2][4 * NTEAM];  // per wave: a page maximum passed the reference by > kLazy
-  __shared__ float lds_l[NTEAM][4][ROWS];
-  __shared__ float lds_m[NTEAM][ROWS];
-  constexpr int MAXPG = (APP == 2) ? kMaxPrefillChunkPages : kMaxChunkPages;
-  __shared__ int32_t lds_pg[MAXPG];  // pool page (block * Hkv + kvh) of each page of the chunk
-  float *pbuf = reinterpret_cast<float *>(pbuf4);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = (tid >> 6) & 3, team = tid >> 8;
-  const int q4 = lane >> 4, c16 = lane & 15;
-  const int split = blockIdx.x, kvh = blockIdx.y % a.num_kv_heads, b = blockIdx.z;
-  const int row0 = (blockIdx.y / a.num_kv_heads) * ROWS;  // first query row (t*G + g) of this block
-  const int L = a.seq_lens[b];
-  if (L < a.T || L > a.max_seq_len || L > a.max_blocks * kPage) {  // the merge writes NaN rows
-    if constexpr (APP == 2) {
-      if (a.direct_out != 0 && split == 0) {  // no merge: write them here
-        for (int e = threadIdx.x; e < ROWS * D; e += blockDim.x) {
-          const int r = row0 + e / D;
-          if (r < a.rows)
-            a.out[((static_cast<size_t>(b) * a.T + r / a.group) * a.num_q_heads + kvh * a.group + r % a.group) * D +
-                  e % D] = NAN;
-        }
-      }
-    }
-    return;
-  }
-  const int R = a.rows;  // query rows of the KV head; this block holds rows row0 .. row0 + ROWS - 1
-  // keys this block's rows can see: row r = t*G + g sees positions 0 .. L - T + t
-  const int lim = (APP == 2) ? L - a.T + (min(row0 + ROWS, R) - 1) / a.group + 1 : L;
-  const int lo_last = L - a.T + row0 / a.group;  // the last key the block's first row sees
-  const int tok0 = split * a.tokens_per_split;
-  if (tok0 >= lim) return;  // chunk past every key of these rows: the merge skips it
-  const int tok1 = min(tok0 + a.tokens_per_split, lim);
-  const int page0 = tok0 / kPage, page1 = (tok1 + kPage - 1) / kPage;
-
-  // ---- the chunk's block ids -> pool pages in LDS (an invalid id reads block 0 and flags the chunk)
-  bool bad = false;
-  const int32_t *bt = a.block_table + static_cast<size_t>(b) * a.max_blocks;
-  for (int i = tid; i < page1 - page0; i += 256 * NTEAM) {
-    const int blk = bt[page0 + i];
-    const bool ok = (blk >= 0) && (blk < a.num_blocks);
-    bad |= !ok;
-    lds_pg[i] = (ok ? blk : 0) * a.num_kv_heads + kvh;
-  }
-  bad = __syncthreads_or(bad ? 1 : 0) != 0;
-
-  const int n_it = (page1 - page0 + NTEAM - 1) / NTEAM;
-  // pool page of iteration it for this team (clamped: iterations past the team's last
-  // page reload that page and skip the math)
-  auto page_of = [&](int it) -> int { return lds_pg[min(it * NTEAM + team, page1 - page0 - 1)]; };
-  PageRegs<D, FMT> rA, rB;
-
-  // ---- fused decode step: the new rows at positions L-T .. L-1 that fall in this chunk
-  // (K and V of each, one wave per row).  When their first page is not loaded before
-  // iteration 3, the source rows are read now, quantized and stored during page 0, and
-  // the writing waves wait for their stores at the end of page 0, before the barrier
-  // that precedes every load of iteration 3 on; otherwise they are written here.
-  constexpr int NW = 4 * NTEAM, RPW = (16 + NW - 1) / NW;  // T <= 8: at most 16 rows
-  [[maybe_unused]] AppendArgs aa;
-  [[maybe_unused]] float xr[RPW][G64];
-  [[maybe_unused]] int blk_r[RPW];
-  int t_lo = 0, n_rows = 0;
-  bool defer = false;
-  if constexpr (APP == 1) {
-    aa.k_new = a.k_new;
-    aa.v_new = a.v_new;
-    aa.k_codes = const_cast<uint8_t *>(a.k_codes);
-    aa.v_codes = const_cast<uint8_t *>(a.v_codes);
-    aa.k_scales = const_cast<void *>(a.k_scales);
-    aa.v_scales = const_cast<void *>(a.v_scales);
-    aa.block_table = a.block_table;
-    aa.start_pos = nullptr;
-    aa.num_seqs = a.num_seqs;
-    aa.n_new = a.T;
-    aa.num_kv_heads = a.num_kv_heads;
-    aa.max_blocks = a.max_blocks;
-    aa.num_blocks = a.num_blocks;
-    t_lo = max(0, tok0 - (L - a.T));
-    n_rows = 2 * max(0, min(a.T, tok1 - (L - a.T)) - t_lo);
-    defer = (max((L - a.T) / kPage, page0) - page0) / NTEAM >= 3;
-    if (defer) {
-#pragma unroll
-      for (int k = 0; k < RPW; ++k) {
-        const int r = (tid >> 6) + k * NW;
-        blk_r[k] = -1;
-        if (r < n_rows) {
-          const int t = t_lo + (r >> 1);
-          blk_r[k] = bt[(L - a.T + t) / kPage];
-          load_row<D, QLO == 1 ? 0 : 1>(aa, b, t, kvh, r & 1, lane, xr[k]);
-        }
-      }
-    }
-  }
-  // the first pages load while the queries are staged (and, for the fused step, the new
-  // rows read) -- unless one of them holds new rows, which must be written first
-  const bool early = (APP != 1) || (page0 + NTEAM - 1 < (L - a.T) / kPage);
-  if (early && n_it > 0) load_k_part<D, FMT>(rA, a, page_of(0), wave, lane, q4);
-
-  // ---- queries -> LDS in B-operand order: entry (nt, cg, hk, hl, lane) holds dims
-  // 64cg + 16(lane/16) + 8hk + 0..7 of row 16nt + lane%16, as f16 hi (hl=0) or lo (hl=1).
-  if constexpr (FMT == 2 || FMT == 3) {
-    // rk8v4, rk4v4: the keys are stored rotated by H64/8 per 64-dim group, so each 64-dim group
-    // of a query row is rotated by the same matrix (butterflies in fp32, one thread per
-    // (row, group)) before it is split into f16 hi + lo
-    for (int task = tid; task < ROWS * G64; task += 256 * NTEAM) {
-      const int rl = task / G64, cg = task % G64, r = row0 + rl;
-      float v[64];
-      if (r < R) {
-        const int t = r / a.group, hq = kvh * a.group + r % a.group;
-        const size_t qb = ((static_cast<size_t>(b) * a.T + t) * a.num_q_heads + hq) * D + 64 * cg;
-#pragma unroll
-        for (int i = 0; i < 64; ++i) v[i] = load_q<QLO != 1>(a.q, qb + i);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 64; ++i) v[i] = 0.0f;
-      }
-#pragma unroll
-      for (int hh = 1; hh < 64; hh <<= 1)
-#pragma unroll
-        for (int i = 0; i < 64; ++i)
-          if ((i & hh) == 0) {
-            const float u = v[i], w = v[i + hh];
-            v[i] = u + w;
-            v[i + hh] = u - w;
-          }
-#pragma unroll
-      for (int jh = 0; jh < 8; ++jh) {  // dims 8jh .. 8jh+7 of the group: lane 16(jh/2) + rl%16, hk = jh%2
-        f16x2 hi[4], lo[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) split_f16(v[8 * jh + 2 * j] * 0.125f, v[8 * jh + 2 * j + 1] * 0.125f, hi[j], lo[j]);
-        const int idx = (((rl / 16) * G64 + cg) * 2 + (jh & 1)) * QP * 64 + 16 * (jh >> 1) + (rl % 16);
-        qs[idx] = __builtin_bit_cast(uint4, f16x8{hi[0][0], hi[0][1], hi[1][0], hi[1][1], hi[2][0], hi[2][1], hi[3][0], hi[3][1]});
-        qs[idx + 64] = __builtin_bit_cast(uint4, f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]});
-      }
-    }
-  }
-  for (int e = tid; e < ((FMT == 2 || FMT == 3) ? 0 : NT * G64 * 2 * 64); e += 256 * NTEAM) {
-    const int ln = e & 63, hk = (e >> 6) & 1, cg = (e >> 7) % G64, nt = (e >> 7) / G64;
-    const int r = row0 + 16 * nt + (ln & 15);
-    const int d0 = 64 * cg + 16 * (ln >> 4) + 8 * hk;
-    f16x2 hi[4], lo[4];
-    if (r < R) {
-      const int t = r / a.group, hq = kvh * a.group + r % a.group;
-      const size_t qb = ((static_cast<size_t>(b) * a.T + t) * a.num_q_heads + hq) * D + d0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // QLO = 1 for fp32 queries (hi + lo), 2 for rotated bf16 queries (hi + lo), 0 for
-        // bf16 queries (one exact f16)
-        const float x0 = load_q<QLO != 1>(a.q, qb + 2 * j), x1 = load_q<QLO != 1>(a.q, qb + 2 * j + 1);
-        if constexpr (FMT == 4) {
-          // BF16 pool: bf16 operands; a bf16 query is exact, an fp32 one is bf16 hi (cut)
-          // + lo (the exact residual rounded)
-          const uint32_t h0 = __float_as_uint(x0) & 0xFFFF0000u, h1 = __float_as_uint(x1) & 0xFFFF0000u;
-          const uint32_t l = f32_to_bf16_rne(x0 - __uint_as_float(h0)) | (f32_to_bf16_rne(x1 - __uint_as_float(h1)) << 16);
-          hi[j] = __builtin_bit_cast(f16x2, (h0 >> 16) | h1);
-          lo[j] = __builtin_bit_cast(f16x2, QLO ? l : 0u);
-        } else if constexpr (QLO) {
-          split_f16(x0, x1, hi[j], lo[j]);
-        } else {
-          hi[j] = f16x2{static_cast<_Float16>(x0), static_cast<_Float16>(x1)};  // RNE; exact for bf16 in range
-          lo[j] = f16x2{0, 0};
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) hi[j] = lo[j] = f16x2{0, 0};
-    }
-    const int idx = ((nt * G64 + cg) * 2 + hk) * QP * 64 + ln;
-    qs[idx] = __builtin_bit_cast(uint4, f16x8{hi[0][0], hi[0][1], hi[1][0], hi[1][1], hi[2][0], hi[2][1], hi[3][0], hi[3][1]});
-    if constexpr (QLO)
-      qs[idx + 64] = __builtin_bit_cast(uint4, f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]});
-  }
-  if constexpr (APP == 1) {
-    if (!defer) {
-      for (int r = (tid >> 6); r < n_rows; r += NW) {
-        const int t = t_lo + (r >> 1);
-        const long pos = static_cast<long>(L) - a.T + t;
-        const int blk = bt[pos / kPage];
-        if (blk >= 0 && blk < a.num_blocks) quant_row<FMT, D, QLO == 1 ? 0 : 1>(aa, b, t, kvh, r & 1, pos, blk, lane);
-      }
-      // a wave that wrote rows waits until its stores have reached L2, so every wave of this
-      // workgroup loads the new rows after the barrier below (no other workgroup reads them)
-      if ((tid >> 6) < n_rows) __builtin_amdgcn_s_waitcnt(0);
-    }
-  }
-  // the first page's V half goes out after the staging, so its K half arrives first
-  if (early && n_it > 0) load_v_part<D, FMT>(rA, a, page_of(0), wave, lane, q4);
-  __syncthreads();
-  if (!early && n_it > 0) load_page<D, FMT>(rA, a, page_of(0), wave, lane, q4);
-
-  // ---- per-lane state; this lane's query row is 16nt + c16
-  float m[NT], lsum[NT];
-  int last[NT];
-  f32x4 o[NT][DPW];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m[nt] = -INFINITY;
-    lsum[nt] = 0.0f;
-    const int r = row0 + 16 * nt + c16;
-    last[nt] = (r < R) ? (L - a.T + r / a.group) : -1;  // -1: padding row, sees nothing
-#pragma unroll
-    for (int j = 0; j < DPW; ++j) o[nt][j] = f32x4{0, 0, 0, 0};
-  }
-  // ---- phase 1: scores of this wave's 16 keys (S^T = K Q^T), in log2 units, and their row maxima
-  auto scores = [&](auto masked_tag, PageRegs<D, FMT> &pr, int p, float (&z)[NT][4], float (&mloc)[NT]) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const int key0 = p * kPage + 16 * wave + 4 * q4;  // key of i is key0 + i
-    f32x4 acc[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      acc[nt] = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) z[nt][i] = 0.0f;
-    }
-    // the query fragments of 64-dim group cg, read from LDS two groups ahead of their use
-    // (bf16 queries; fp32 queries, with twice the fragments, read them at their use)
-    constexpr int QPF = (QLO || NT > 2) ? 1 : 2;  // groups of fragments in flight
-    f16x8 qf[QPF][2][NT][QP];
-    auto read_q = [&](f16x8 (&dst)[2][NT][QP], int cg) {
-#pragma unroll
-      for (int hk = 0; hk < 2; ++hk)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int hl = 0; hl < QP; ++hl) dst[hk][nt][hl] = lds_f16x8(&qs[(((nt * G64 + cg) * 2 + hk) * QP + hl) * 64 + lane]);
-    };
-#pragma unroll
-    for (int c = 0; c < QPF && c < G64; ++c) read_q(qf[c], c);
-#pragma unroll
-    for (int cg = 0; cg < G64; ++cg) {
-      f16x8 (&qc)[2][NT][QP] = qf[cg % QPF];
-      if constexpr (QPF == 1) {
-        if (cg > 0) read_q(qc, cg);
-      }
-#pragma unroll
-      for (int hk = 0; hk < 2; ++hk) {
-        if constexpr (FMT == 4) {  // bf16 keys enter the matrix cores as they are
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            acc[nt] = mfma16_bf(pr.k[2 * cg + hk], __builtin_bit_cast(uint4, qc[hk][nt][0]), acc[nt]);
-            if constexpr (QLO) acc[nt] = mfma16_bf(pr.k[2 * cg + hk], __builtin_bit_cast(uint4, qc[hk][nt][QP - 1]), acc[nt]);
-          }
-          continue;
-        }
-        f16x8 ka;
-        if constexpr (FMT == 3) {
-          const uint4 &kw = pr.k[cg / 2];
-          ka = k4_to_f16((cg & 1) ? (hk ? kw.w : kw.z) : (hk ? kw.y : kw.x));
-        } else {
-          ka = hk ? codes_to_f16<KF>(pr.k[cg].z, pr.k[cg].w) : codes_to_f16<KF>(pr.k[cg].x, pr.k[cg].y);
-        }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          acc[nt] = mfma16(ka, qc[hk][nt][0], acc[nt]);
-          if constexpr (QLO) acc[nt] = mfma16(ka, qc[hk][nt][QP - 1], acc[nt]);
-        }
-      }
-      if constexpr (QPF == 2) {
-        if (cg + 2 < G64) read_q(qc, cg + 2);
-      }
-      if constexpr (KF != 1 && KF != 4) {  // fold each key's fp16 group scale, restart the group sum
-        const uint4 w = pr.ks[cg >> 1];
-        float sk[4];
-        f16x2_to_f32((cg & 1) ? w.z : w.x, sk[0], sk[1]);
-        f16x2_to_f32((cg & 1) ? w.w : w.y, sk[2], sk[3]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) z[nt][i] += sk[i] * acc[nt][i];
-          acc[nt] = f32x4{0, 0, 0, 0};
-        }
-      }
-    }
-    if constexpr (FMT == 4) {  // no scales
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) z[nt][i] = acc[nt][i];
-    }
-    if constexpr (FMT == 1) {
-      const float sk[4] = {__uint_as_float(pr.ks[0].x), __uint_as_float(pr.ks[0].y), __uint_as_float(pr.ks[0].z),
-                           __uint_as_float(pr.ks[0].w)};
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) z[nt][i] = sk[i] * acc[nt][i];
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = z[nt][i] * a.qk_scale_log2;
-        if constexpr (MASKED) v = (key0 + i <= last[nt]) ? v : -INFINITY;
-        z[nt][i] = v;
-        mx = fmaxf(mx, v);
-      }
-      mloc[nt] = max_xor32(max_xor16(mx));
-    }
-  };
-
-  // ---- phase 3: O^T += V^T P^T for this wave's dim tiles; each key's V scale folded into its weight
-  auto accumulate = [&](auto masked_tag, PageRegs<D, FMT> &pr, int p, const float *pb) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    if constexpr (FMT == 4) {
-      // BF16 pool: V^T straight from the pool (pr.v[2j + ks]: keys 16(2ks) + 4(lane/16) + i,
-      // then 16(2ks+1) + ...), the fp32 weights as three bf16 terms
-      if constexpr (MASKED) {  // slots at or past L may hold anything: zero their values
-        const int kbase = p * kPage + 4 * q4;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          uint32_t mw[4];
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const int key = kbase + 16 * (2 * ks + w / 2) + 2 * (w % 2);
-            mw[w] = ((key < L) ? 0x0000FFFFu : 0u) | ((key + 1 < L) ? 0xFFFF0000u : 0u);
-          }
-#pragma unroll
-          for (int j = 0; j < DPW; ++j) {
-            pr.v[2 * j + ks].x &= mw[0];
-            pr.v[2 * j + ks].y &= mw[1];
-            pr.v[2 * j + ks].z &= mw[2];
-            pr.v[2 * j + ks].w &= mw[3];
-          }
-        }
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const float4 p0 = *reinterpret_cast<const float4 *>(pb + (16 * nt + c16) * PST + 16 * (2 * ks) + 4 * q4);
-          const float4 p1 = *reinterpret_cast<const float4 *>(pb + (16 * nt + c16) * PST + 16 * (2 * ks + 1) + 4 * q4);
-          uint32_t h[4], m[4], l[4];
-          split_bf16x3(p0.x, p0.y, h[0], m[0], l[0]);
-          split_bf16x3(p0.z, p0.w, h[1], m[1], l[1]);
-          split_bf16x3(p1.x, p1.y, h[2], m[2], l[2]);
-          split_bf16x3(p1.z, p1.w, h[3], m[3], l[3]);
-          const uint4 bh = make_uint4(h[0], h[1], h[2], h[3]), bm = make_uint4(m[0], m[1], m[2], m[3]);
-          const uint4 bl = make_uint4(l[0], l[1], l[2], l[3]);
-#pragma unroll
-          for (int j = 0; j < DPW; ++j) {
-            o[nt][j] = mfma16_bf(pr.v[2 * j + ks], bh, o[nt][j]);
-            o[nt][j] = mfma16_bf(pr.v[2 * j + ks], bm, o[nt][j]);
-            o[nt][j] = mfma16_bf(pr.v[2 * j + ks], bl, o[nt][j]);
-          }
-        }
-      return;
-    }
-    if constexpr (MASKED) {
-      // slots at or past L may hold anything (never written): zero their V codes
-      const int kbase = p * kPage + 4 * q4;  // key of (kt, i) is kbase + 16kt + i
-      if constexpr (FMT >= 2) {
-        // word ks holds keys kt = 2ks + q/4, i = q%4 (q = 0..7) at bit 16*(q%2) + 4*(q/2)
-        uint32_t mw[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          uint32_t wv = 0;
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            wv |= (kbase + 16 * (2 * ks + q / 4) + q % 4 < L) ? (0xFu << (16 * (q % 2) + 4 * (q / 2))) : 0u;
-          mw[ks] = wv;
-        }
-#pragma unroll
-        for (int j = 0; j < PageRegs<D, FMT>::VN; ++j) {
-          pr.v[j].x &= mw[0];
-          pr.v[j].y &= mw[1];
-          pr.v[j].z &= mw[0];
-          pr.v[j].w &= mw[1];
-        }
-      } else {
-        uint32_t mw[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          uint32_t wv = 0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) wv |= (kbase + 16 * kt + i < L) ? (0xFFu << (8 * i)) : 0u;
-          mw[kt] = wv;
-        }
-#pragma unroll
-        for (int j = 0; j < DPW; ++j) {
-          pr.v[j].x &= mw[0];
-          pr.v[j].y &= mw[1];
-          pr.v[j].z &= mw[2];
-          pr.v[j].w &= mw[3];
-        }
-      }
-    }
-    // the B operands (P^T, each key's weight times its V scale, as f16 hi + lo) of key
-    // half ks; w: the fp16 V scales of keys 16(2ks) .. 16(2ks+1)+15 of this lane group
-    auto build_b1 = [&](int ks, const uint4 &w, int nt, f16x8 &bh, f16x8 &bl) {
-      {
-        f16x2 hi[4], lo[4];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int kt = 2 * ks + kk;
-          if constexpr (FMT != 1) {
-            const uint4 pw = *reinterpret_cast<const uint4 *>(pb + (16 * nt + c16) * PST + 16 * kt + 4 * q4);
-            const f16x2 h01 = __builtin_bit_cast(f16x2, pw.x), h23 = __builtin_bit_cast(f16x2, pw.y);
-            const f16x2 l01 = __builtin_bit_cast(f16x2, pw.z), l23 = __builtin_bit_cast(f16x2, pw.w);
-            f16x2 s01 = __builtin_bit_cast(f16x2, kk ? w.z : w.x), s23 = __builtin_bit_cast(f16x2, kk ? w.w : w.y);
-            if constexpr (MASKED) {  // unwritten slots (weight 0) may hold NaN scales
-              s01 = f16x2{h01[0] != _Float16(0) ? s01[0] : _Float16(0), h01[1] != _Float16(0) ? s01[1] : _Float16(0)};
-              s23 = f16x2{h23[0] != _Float16(0) ? s23[0] : _Float16(0), h23[1] != _Float16(0) ? s23[1] : _Float16(0)};
-            }
-            scale_pair(h01, l01, s01, hi[2 * kk], lo[2 * kk]);
-            scale_pair(h23, l23, s23, hi[2 * kk + 1], lo[2 * kk + 1]);
-          } else {
-            const float4 pw = *reinterpret_cast<const float4 *>(pb + (16 * nt + c16) * PST + 16 * kt + 4 * q4);
-            const float pp[4] = {pw.x, pw.y, pw.z, pw.w};
-            const uint4 sw = pr.vs[kt];
-            const float sv[4] = {__uint_as_float(sw.x), __uint_as_float(sw.y), __uint_as_float(sw.z), __uint_as_float(sw.w)};
-            float pv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              pv[i] = pp[i] * sv[i];
-              if constexpr (MASKED) pv[i] = (pp[i] != 0.0f) ? pv[i] : 0.0f;  // unwritten slots: NaN scales
-            }
-            split_f16(pv[0], pv[1], hi[2 * kk], lo[2 * kk]);
-            split_f16(pv[2], pv[3], hi[2 * kk + 1], lo[2 * kk + 1]);
-          }
-        }
-        bh = f16x8{hi[0][0], hi[0][1], hi[1][0], hi[1][1], hi[2][0], hi[2][1], hi[3][0], hi[3][1]};
-        bl = f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]};
-      }
-    };
-    auto build_b = [&](int ks, const uint4 &w, f16x8 (&bh)[NT], f16x8 (&bl)[NT]) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) build_b1(ks, w, nt, bh[nt], bl[nt]);
-    };
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if constexpr (FMT >= 2) {
-        // one 32-dim scale group per pair of dim tiles, with its own B operands (built
-        // one row tile at a time to keep few of them live)
-#pragma unroll
-        for (int gp = 0; gp < DPW / 2; ++gp) {
-          const uint4 &vw = pr.v[gp];
-          const f16x8 va0 = v4_to_f16(ks ? vw.y : vw.x), va1 = v4_to_f16(ks ? vw.w : vw.z);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            f16x8 bh, bl;
-            build_b1(ks, pr.vs[2 * gp + ks], nt, bh, bl);
-            o[nt][2 * gp] = mfma16(va0, bh, o[nt][2 * gp]);
-            o[nt][2 * gp] = mfma16(va0, bl, o[nt][2 * gp]);
-            o[nt][2 * gp + 1] = mfma16(va1, bh, o[nt][2 * gp + 1]);
-            o[nt][2 * gp + 1] = mfma16(va1, bl, o[nt][2 * gp + 1]);
-          }
-        }
-      } else {
-        f16x8 bh[NT], bl[NT];
-        build_b(ks, pr.vs[FMT == 0 ? ks : 0], bh, bl);
-#pragma unroll
-        for (int j = 0; j < DPW; ++j) {
-          const f16x8 va = ks ? codes_to_f16<FMT>(pr.v[j].z, pr.v[j].w) : codes_to_f16<FMT>(pr.v[j].x, pr.v[j].y);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            o[nt][j] = mfma16(va, bh[nt], o[nt][j]);
-            o[nt][j] = mfma16(va, bl[nt], o[nt][j]);
-          }
-        }
-      }
-    }
-  };
-
-  // one page: pr holds it; the next page's K half is already in flight in nx, and its
-  // V half is issued once the page maxima are exchanged
-  auto step = [&](PageRegs<D, FMT> &pr, PageRegs<D, FMT> &nx, int pg_next, int it, auto more_tag) {
-    constexpr bool MORE = decltype(more_tag)::value;  // a next page exists: load its V half here
-    const int p = page0 + it * NTEAM + team;
-    const bool valid = p < page1;                              // uniform per team
-    const bool full = (p * kPage + kPage - 1) <= lo_last;      // every real row sees every key of the page
-    const int buf = it & 1;
-    float z[NT][4];
-    float mloc[NT];
-    if (valid && full) {
-      scores(std::false_type{}, pr, p, z, mloc);
-    } else if (valid) {
-      scores(std::true_type{}, pr, p, z, mloc);
-    } else {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        mloc[nt] = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) z[nt][i] = -INFINITY;
-      }
-    }
-    if (q4 == 0) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) reinterpret_cast<float *>(&lds_mx[team][buf][16 * nt + c16])[wave] = mloc[nt];
-    }
-    if constexpr (MORE) load_v_part<D, FMT>(nx, a, pg_next, wave, lane, q4);
-
-    // ---- phase 2: softmax weights against the team's reference maxima m (one per row,
-    // identical in the 4 waves).  m moves only when a page maximum passes it by more than
-    // kLazy (log2 units), so weights stay <= 2^kLazy.  Each wave first assumes that no
-    // maximum of the page passes m by that much and writes its weights with the current
-    // m; if any wave of the workgroup saw such a maximum, all waves move m to the page
-    // maxima exchanged beside the weights, rescale o and l, and rewrite their weights.
-    float *pb = pbuf + (team * 2 + buf) * ROWS * PST;
-    float psum[NT];
-    auto write_weights = [&]() {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int r = 16 * nt + c16;
-        const float msafe = (m[nt] == -INFINITY) ? 0.0f : m[nt];
-        float pv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pv[i] = exp2_hw(z[nt][i] - msafe);
-        psum[nt] = (pv[0] + pv[1]) + (pv[2] + pv[3]);
-        if constexpr (FMT != 1 && FMT != 4) {
-          // INT8 and rk8v4: the weights go out as f16 hi+lo pairs (the V scales, fp16, are
-          // applied by the accumulating wave with packed f16 arithmetic)
-          f16x2 h01, l01, h23, l23;
-          split_f16(pv[0], pv[1], h01, l01);
-          split_f16(pv[2], pv[3], h23, l23);
-          *reinterpret_cast<uint4 *>(pb + r * PST + 16 * wave + 4 * q4) =
-              make_uint4(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23),
-                         __builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23));
-        } else {
-          *reinterpret_cast<float4 *>(pb + r * PST + 16 * wave + 4 * q4) = make_float4(pv[0], pv[1], pv[2], pv[3]);
-        }
-      }
-    };
-    bool over = false;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) over |= mloc[nt] > m[nt] + kLazy;  // m = -inf: any visible key
-    const bool wave_over = __any(over);
-    if (!wave_over) write_weights();  // a wave that is over rewrites below anyway
-    if (lane == 0) lds_over[buf][(tid >> 6)] = wave_over ? 1 : 0;
-    __syncthreads();
-    int any_over = 0;
-#pragma unroll
-    for (int w = 0; w < 4 * NTEAM; ++w) any_over |= lds_over[buf][w];
-    if (any_over) {  // uniform over the workgroup
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const float4 mw4 = lds_mx[team][buf][16 * nt + c16];
-        const float pmax = fmaxf(fmaxf(mw4.x, mw4.y), fmaxf(mw4.z, mw4.w));
-        const bool up = pmax > m[nt] + kLazy;
-        const float mnew = up ? pmax : m[nt];
-        const float alpha = up ? exp2_hw(m[nt] - mnew) : 1.0f;  // 0 when m was -inf
-        m[nt] = mnew;
-        lsum[nt] *= alpha;
-#pragma unroll
-        for (int j = 0; j < DPW; ++j) o[nt][j] *= alpha;
-      }
-      write_weights();
-      __syncthreads();
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) lsum[nt] += psum[nt];
-
-    if constexpr (APP == 1) {
-      if (defer && it == 0) {  // the deferred rows of the fused step (see above)
-#pragma unroll
-        for (int k = 0; k < RPW; ++k) {
-          const int r = (tid >> 6) + k * NW;
-          if (r < n_rows && blk_r[k] >= 0 && blk_r[k] < a.num_blocks)
-            store_row<FMT, D>(aa, xr[k], kvh, r & 1, static_cast<long>(L) - a.T + t_lo + (r >> 1), blk_r[k], lane);
-        }
-      }
-    }
-    if (valid && full) {
-      accumulate(std::false_type{}, pr, p, pb);
-    } else if (valid) {
-      accumulate(std::true_type{}, pr, p, pb);
-    }
-    if constexpr (APP == 1) {
-      if (defer && it == 0 && (tid >> 6) < n_rows) __builtin_amdgcn_s_waitcnt(0);
-    }
-  };
-
-  // pages in pairs while a next page exists for both; the last page (or two) peeled off
-  // so that no load is issued past the team's pages
-  int it = 0;
-  for (; it + 2 < n_it; it += 2) {
-    const int pgB = page_of(it + 1);
-    load_k_part<D, FMT>(rB, a, pgB, wave, lane, q4);
-    step(rA, rB, pgB, it, std::true_type{});
-    const int pgA = page_of(it + 2);
-    load_k_part<D, FMT>(rA, a, pgA, wave, lane, q4);
-    step(rB, rA, pgA, it + 1, std::true_type{});
-  }
-  if (it + 1 < n_it) {
-    const int pgB = page_of(it + 1);
-    load_k_part<D, FMT>(rB, a, pgB, wave, lane, q4);
-    step(rA, rB, pgB, it, std::true_type{});
-    step(rB, rA, 0, it + 1, std::false_type{});
-  } else if (it < n_it) {
-    step(rA, rB, 0, it, std::false_type{});
-  }
-
-  // ---- per-wave row sums, then the team's and the workgroup's totals
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    lsum[nt] = sum_xor32(sum_xor16(lsum[nt]));
-  }
-  if (q4 == 0) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      lds_l[team][wave][16 * nt + c16] = lsum[nt];
-      if (wave == 0) lds_m[team][16 * nt + c16] = m[nt];
-    }
-  }
-  const int any_bad = __syncthreads_or(bad ? 1 : 0);
-  float Mrow[NT], Lrow[NT], fown[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = 16 * nt + c16;
-    float M = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < NTEAM; ++t) M = fmaxf(M, lds_m[t][r]);
-    const float Ms = (M == -INFINITY) ? 0.0f : M;
-    float Lt = 0.0f;
-#pragma unroll
-    for (int t = 0; t < NTEAM; ++t) {
-      const float lt = (lds_l[t][0][r] + lds_l[t][1][r]) + (lds_l[t][2][r] + lds_l[t][3][r]);
-      Lt += lt * exp2f(lds_m[t][r] - Ms);
-    }
-    Mrow[nt] = M;
-    Lrow[nt] = any_bad ? NAN : Lt;
-    fown[nt] = exp2f(m[nt] - Ms);
-  }
-  // teams 1.. hand their scaled outputs to team 0 through LDS (fixed order: deterministic)
-  float *fin = pbuf;
-  if constexpr (NTEAM > 1) {
-    if (team > 0) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int j = 0; j < DPW; ++j) {
-          const f32x4 v = o[nt][j] * fown[nt];
-          *reinterpret_cast<float4 *>(fin + ((team - 1) * ROWS + 16 * nt + c16) * (D + 4) + 16 * (wave * DPW + j) +
-                                      4 * q4) = make_float4(v[0], v[1], v[2], v[3]);
-        }
-    }
-    __syncthreads();
-  }
-  if (team == 0) {
-    const size_t part = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits + split;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int rl = 16 * nt + c16, r = row0 + rl;
-      if (r < R) {
-        // prefill with one chunk: the normalized row goes to out[b][t][h] (t*G + g = r)
-        const bool direct = (APP == 2) && (a.direct_out != 0);
-        const size_t orow = ((static_cast<size_t>(b) * a.T + r / a.group) * a.num_q_heads + kvh * a.group +
-                             r % a.group) * D;
-#pragma unroll
-        for (int j = 0; j < DPW; ++j) {
-          f32x4 v = o[nt][j] * fown[nt];
-          const int d = 16 * (wave * DPW + j) + 4 * q4;
-#pragma unroll
-          for (int t = 1; t < NTEAM; ++t) {
-            const float4 x = *reinterpret_cast<const float4 *>(fin + ((t - 1) * ROWS + rl) * (D + 4) + d);
-            v += f32x4{x.x, x.y, x.z, x.w};
-          }
-          if (direct) {
-            const float l = Lrow[nt];
-            *reinterpret_cast<float4 *>(a.out + orow + d) = make_float4(v[0] / l, v[1] / l, v[2] / l, v[3] / l);
-          } else {
-            *reinterpret_cast<float4 *>(a.ws_o + (part * R + r) * D + d) = make_float4(v[0], v[1], v[2], v[3]);
-          }
-        }
-        if (!direct && wave == 0 && q4 == 0) {
-          a.ws_ml[(part * R + r) * 2 + 0] = Mrow[nt];
-          a.ws_ml[(part * R + r) * 2 + 1] = Lrow[nt];
-        }
-      }
-    }
-  }
-}
-
-// Merge kernel: one wave per 64-dim slice of an output row (b, t, h).  Lane l holds
-// float4 column l % 16 of the slice for the chunks s = l / 16 + 4k, with each chunk's
-// maximum and sum; every load is issued at once, beside the sequence length.  All
-// n_splits chunk slots lie in the workspace; slots past the chunks that hold the row's
-// keys carry stale values and are dropped by selection.  The log-sum-exp weights and
-// the sums over the four chunk groups use cross-lane swaps only (no LDS, no barrier),
-// in a fixed order (deterministic).
-template <int D>
-__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
-  constexpr int NQ = D / 64;  // 64-dim slices of a row, one wave each
-  constexpr int MPER = 16;    // chunks per lane held in registers (all of them up to 64 chunks)
-  const int row = blockIdx.x / NQ, qs = blockIdx.x % NQ, lane = threadIdx.x;
-  const int h = row % a.num_q_heads, t = (row / a.num_q_heads) % a.T, b = row / (a.num_q_heads * a.T);
-  float *dst = a.out + static_cast<size_t>(row) * D + 64 * qs;
-  const int kvh = h / a.group, r = t * a.group + h % a.group;
-  const size_t part0 = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits;
-  const int c4 = lane & 15, sg = lane >> 4, col = qs * 16 + c4;
-  const float2 *ml2 = reinterpret_cast<const float2 *>(a.ws_ml);
-  auto o_at = [&](int s) { return reinterpret_cast<const float4 *>(a.ws_o + ((part0 + s) * a.rows + r) * D)[col]; };
-
-  float4 x[MPER];
-  float2 ml[MPER];
-#pragma unroll
-  for (int k = 0; k < MPER; ++k) {
-    const int s = min(sg + 4 * k, a.n_splits - 1);
-    x[k] = o_at(s);
-    ml[k] = ml2[(part0 + s) * a.rows + r];
-  }
-  const int L = a.seq_lens[b];
-  if (L < a.T || L > a.max_seq_len || L > a.max_blocks * kPage) {
-    dst[lane] = NAN;
-    return;
-  }
-  // chunks holding keys this row sees (later chunks were skipped or hold none of them)
-  const int ns = (L - a.T + t + a.tokens_per_split) / a.tokens_per_split;
-  float mloc = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < MPER; ++k)
-    if (sg + 4 * k < ns) mloc = fmaxf(mloc, ml[k].x);
-  for (int s = sg + 4 * MPER; s < ns; s += 4) mloc = fmaxf(mloc, ml2[(part0 + s) * a.rows + r].x);
-  const float M = max_xor32(max_xor16(mloc));
-  const float Ms = (M == -INFINITY) ? 0.0f : M;
-  float4 acc = make_float4(0, 0, 0, 0);
-  float lt = 0.0f;
-  auto add = [&](float2 st, float4 y) {
-    const float w = exp2f(st.x - Ms);
-    lt += w * st.y;
-    acc.x += w * y.x;
-    acc.y += w * y.y;
-    acc.z += w * y.z;
-    acc.w += w * y.w;
-  };
-#pragma unroll
-  for (int k = 0; k < MPER; ++k)
-    if (sg + 4 * k < ns) add(ml[k], x[k]);
-  for (int s = sg + 4 * MPER; s < ns; s += 4) add(ml2[(part0 + s) * a.rows + r], o_at(s));  // long contexts
-  lt = sum_xor32(sum_xor16(lt));
-  acc.x = sum_xor32(sum_xor16(acc.x));
-  acc.y = sum_xor32(sum_xor16(acc.y));
-  acc.z = sum_xor32(sum_xor16(acc.z));
-  acc.w = sum_xor32(sum_xor16(acc.w));
-  if (sg == 0) reinterpret_cast<float4 *>(dst)[c4] = make_float4(acc.x / lt, acc.y / lt, acc.z / lt, acc.w / lt);
-}
-
-// ---- Prefill kernel for INT8 and FP8 pools with bf16 queries.
-//
-// A workgroup of 8 waves owns 128 query rows (t*G + g) of one KV head and one chunk of
-// its context; wave w owns rows 16w .. 16w+15 outright (KVQ_PREFILL_NTW = 2 builds 4
-// waves of 32 rows instead, one wave per SIMD): their queries stay in registers
-// as the B operands of S^T = K Q^T, their softmax state and their output O^T = V^T P^T
-// (all D dims) stay in the wave, and the weights go from the score registers straight
-// into the P·V products (the V layout puts each lane's keys where the S^T tile leaves
-// them), so no wave waits on another for softmax.  The K and V codes of a page are
-// converted to f16 once per workgroup, by all its threads, into LDS (double-buffered:
-// page p+1 is converted while page p is multiplied, page p+2 is in flight from HBM), and
-// every wave reads its matrix-core A operands from there: one barrier per page.
-#ifndef KVQ_PREFILL_NTW
-#define KVQ_PREFILL_NTW 1
-#endif
-template <int D, int FMT>
-__global__ __launch_bounds__(64 * 8 / KVQ_PREFILL_NTW, 1) void prefill_kernel(AttnArgs a) {
-  constexpr int G64 = D / 64, KB = D / 32, DT = D / 16, NTW = KVQ_PREFILL_NTW, ROWS = 128;
-  constexpr int NW = 8 / NTW, NTH = 64 * NW;  // waves (16*NTW rows each) and threads of the workgroup
-  constexpr int CPT = 64 * DT / NTH;          // 16-byte code chunks of K (and of V) per thread per page
-  __shared__ uint4 kl[2][4 * KB * 64];  // f16 K operands: [(kt*KB + kb)*64 + lane]
-  __shared__ uint4 vl[2][DT * 2 * 64];  // f16 V^T operands: [(dt*2 + ks)*64 + lane]
-  // INT8: the page's K and V scales (D fp16 each), copied from the pool in its own layout,
-  // so the waves read them from LDS (FP8 pools, one scale per key, read theirs directly)
-  constexpr int SCU = (FMT == 0) ? D * 2 / 16 : 1;  // uint4 per scale array
-  __shared__ uint4 sl[2][2 * SCU];
-  __shared__ int32_t lds_pg[kMaxPrefillChunkPages];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q4 = lane >> 4, c16 = lane & 15;
-  const int split = blockIdx.x, kvh = blockIdx.y % a.num_kv_heads, b = blockIdx.z;
-  const int row0 = (blockIdx.y / a.num_kv_heads) * ROWS;
-  const int L = a.seq_lens[b];
-  const int R = a.rows;
-  if (L < a.T || L > a.max_seq_len || L > a.max_blocks * kPage) {  // the merge writes NaN rows
-    if (a.direct_out != 0 && split == 0) {                        // no merge: write them here
-      for (int e = tid; e < ROWS * D; e += NTH) {
-        const int r = row0 + e / D;
-        if (r < R)
-          a.out[((static_cast<size_t>(b) * a.T + r / a.group) * a.num_q_heads + kvh * a.group + r % a.group) * D +
-                e % D] = NAN;
-      }
-    }
-    return;
-  }
-  // keys the block's rows see: row r = t*G + g sees positions 0 .. L - T + t
-  const int lim = L - a.T + (min(row0 + ROWS, R) - 1) / a.group + 1;
-  const int lo_last = L - a.T + row0 / a.group;  // the last key the block's first row sees
-  const int tok0 = split * a.tokens_per_split;
-  if (tok0 >= lim) return;  // chunk past every key of these rows: the merge skips it
-  const int tok1 = min(tok0 + a.tokens_per_split, lim);
-  const int page0 = tok0 / kPage, npg = (tok1 + kPage - 1) / kPage - page0;
-
-  // ---- the chunk's block ids -> pool pages in LDS (an invalid id reads block 0 and flags the chunk)
-  bool bad = false;
-  const int32_t *bt = a.block_table + static_cast<size_t>(b) * a.max_blocks;
-  for (int i = tid; i < npg; i += NTH) {
-    const int blk = bt[page0 + i];
-    const bool ok = (blk >= 0) && (blk < a.num_blocks);
-    bad |= !ok;
-    lds_pg[i] = (ok ? blk : 0) * a.num_kv_heads + kvh;
-  }
-  const int any_bad = __syncthreads_or(bad ? 1 : 0);
-
-  // ---- page codes: HBM -> registers -> f16 operands in LDS
-  uint4 kc[CPT], vc[CPT], sc4 = make_uint4(0, 0, 0, 0);
-  auto gload = [&](int i) {
-    const size_t pg = static_cast<uint32_t>(lds_pg[i]);
-    const uint4 *kp = reinterpret_cast<const uint4 *>(a.k_codes + pg * kPage * D);
-    const uint4 *vp = reinterpret_cast<const uint4 *>(a.v_codes + pg * kPage * D);
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      kc[k] = ld_stream(kp + tid + NTH * k);
-      vc[k] = ld_stream(vp + tid + NTH * k);
-    }
-    if constexpr (FMT == 0) {
-      if (tid < 2 * SCU) {  // threads 0 .. SCU-1: K scales, SCU .. 2 SCU-1: V scales
-        const uint4 *sp = reinterpret_cast<const uint4 *>(static_cast<const _Float16 *>(tid < SCU ? a.k_scales : a.v_scales) +
-                                                          pg * D);
-        sc4 = ld_stream(sp + (tid % SCU));
-      }
-    }
-  };
-  auto convert = [&](int buf, int p) {
-    if constexpr (FMT == 0) {
-      if (tid < 2 * SCU) sl[buf][tid] = sc4;
-    }
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const int c = tid + NTH * k;
-      // K chunk c: key s = (c / (16 DT)) * 16 + c % 16, dims 16 dt .. +15 with dt = (c / 16) % DT;
-      // in the S^T products it is key tile s/16, dim block dt/2, lanes 16 (2 (dt%2) + hk) + s%16
-      const int kt = c / (16 * DT), dt = (c / 16) % DT, sr = c % 16;
-      uint4 *kd = &kl[buf][(kt * KB + dt / 2) * 64 + 32 * (dt % 2) + sr];
-      kd[0] = __builtin_bit_cast(uint4, codes_to_f16<FMT>(kc[k].x, kc[k].y));
-      kd[16] = __builtin_bit_cast(uint4, codes_to_f16<FMT>(kc[k].z, kc[k].w));
-      // V chunk c: dim 16 (c/64) + c%16, the 16 keys 16 kt + 4 ((c%64)/16) + i; slots at or
-      // past L may hold anything (never written): zero their codes
-      uint4 v = vc[k];
-      const int kbase = p * kPage + 4 * ((c % 64) / 16);
-      if (kbase + 48 + 3 >= L) {
-        uint32_t mw[4];
-#pragma unroll
-        for (int kt2 = 0; kt2 < 4; ++kt2) {
-          uint32_t wv = 0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) wv |= (kbase + 16 * kt2 + i < L) ? (0xFFu << (8 * i)) : 0u;
-          mw[kt2] = wv;
-        }
-        v.x &= mw[0];
-        v.y &= mw[1];
-        v.z &= mw[2];
-        v.w &= mw[3];
-      }
-      vl[buf][((c / 64) * 2 + 0) * 64 + c % 64] = __builtin_bit_cast(uint4, codes_to_f16<FMT>(v.x, v.y));
-      vl[buf][((c / 64) * 2 + 1) * 64 + c % 64] = __builtin_bit_cast(uint4, codes_to_f16<FMT>(v.z, v.w));
-    }
-  };
-  if (npg > 0) gload(0);
-
-  // ---- this wave's queries (bf16, exact in f16) -> registers: B operand of dim block kb
-  f16x8 qf[NTW][KB];
-  int last[NTW];
-#pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-    const int r = row0 + 16 * NTW * wave + 16 * nt + c16;
-    last[nt] = (r < R) ? (L - a.T + r / a.group) : -1;  // -1: padding row, sees nothing
-    const size_t qb = ((static_cast<size_t>(b) * a.T + r / a.group) * a.num_q_heads + kvh * a.group + r % a.group) * D;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (r < R) u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + qb + 32 * kb + 8 * q4);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-      f16x2 h[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        h[j] = f16x2{static_cast<_Float16>(__uint_as_float(w[j] << 16)),
-                     static_cast<_Float16>(__uint_as_float(w[j] & 0xFFFF0000u))};
-      qf[nt][kb] = f16x8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
-    }
-  }
-  if (npg > 0) convert(0, page0);
-  if (npg > 1) gload(1);
-  __syncthreads();
-
-  f32x4 o[NTW][DT];
-  float m[NTW], lsum[NTW];
-#pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-    m[nt] = -INFINITY;
-    lsum[nt] = 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[nt][dt] = f32x4{0, 0, 0, 0};
-  }
-
-  for (int it = 0; it < npg; ++it) {
-    const int p = page0 + it, buf = it & 1;
-    [[maybe_unused]] const size_t pg = static_cast<uint32_t>(lds_pg[it]);
-    if (it + 1 < npg) convert(buf ^ 1, p + 1);  // the next page, loaded one iteration ago
-    if (it + 2 < npg) gload(it + 2);
-    const bool full = (p * kPage + kPage - 1) <= lo_last;  // every real row sees every key of the page
-
-    // ---- S^T = K Q^T for the 4 key tiles x this wave's 2 row tiles, scales folded per 64 dims
-    float z[4][NTW][4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) z[kt][nt][i] = 0.0f;
-#pragma unroll
-    for (int g = 0; g < G64; ++g) {
-      f32x4 acc[4][NTW];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) acc[kt][nt] = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int kb = 2 * g; kb < 2 * g + 2; ++kb)
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const f16x8 ka = lds_f16x8(&kl[buf][(kt * KB + kb) * 64 + lane]);
-#pragma unroll
-          for (int nt = 0; nt < NTW; ++nt) acc[kt][nt] = mfma16(ka, qf[nt][kb], acc[kt][nt]);
-        }
-      if constexpr (FMT == 0) {
-        // fp16 scales of this lane's keys 16 kt + 4 q4 + i in group g: element
-        // ((q4*4 + kt) * G64 + g) * 4 + i of the page's K scales
-        const uint2 *ksp = reinterpret_cast<const uint2 *>(&sl[buf][0]);
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const uint2 w = ksp[(q4 * 4 + kt) * G64 + g];
-          float sk[4];
-          f16x2_to_f32(w.x, sk[0], sk[1]);
-          f16x2_to_f32(w.y, sk[2], sk[3]);
-#pragma unroll
-          for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) z[kt][nt][i] += sk[i] * acc[kt][nt][i];
-        }
-      } else {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) z[kt][nt][i] += acc[kt][nt][i];
-      }
-    }
-    if constexpr (FMT == 1) {  // one fp32 scale per key: element q4*16 + kt*4 + i
-      const float4 *ksp = reinterpret_cast<const float4 *>(static_cast<const float *>(a.k_scales) + pg * kPage);
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const float4 w = ksp[q4 * 4 + kt];
-        const float sk[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) z[kt][nt][i] *= sk[i];
-      }
-    }
-    // log2 units; the causal mask (and keys past L) on the pages that need it
-    float pm[NTW];
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = z[kt][nt][i] * a.qk_scale_log2;
-          if (!full) v = (p * kPage + 16 * kt + 4 * q4 + i <= last[nt]) ? v : -INFINITY;
-          z[kt][nt][i] = v;
-          mx = fmaxf(mx, v);
-        }
-      pm[nt] = max_xor32(max_xor16(mx));
-    }
-    // ---- online softmax, per row inside the wave: the reference maximum moves only when
-    // a page maximum passes it by more than kLazy (weights stay <= 2^kLazy)
-    bool up = false;
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) up |= pm[nt] > m[nt] + kLazy;
-    if (__any(up)) {
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        const bool u = pm[nt] > m[nt] + kLazy;
-        const float mnew = u ? pm[nt] : m[nt];
-        const float alpha = u ? exp2_hw(m[nt] - mnew) : 1.0f;  // 0 when m was -inf
-        m[nt] = mnew;
-        lsum[nt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[nt][dt] *= alpha;
-      }
-    }
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      const float ms = (m[nt] == -INFINITY) ? 0.0f : m[nt];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          z[kt][nt][i] = exp2_hw(z[kt][nt][i] - ms);
-          lsum[nt] += z[kt][nt][i];
-        }
-    }
-
-    // ---- O^T += V^T P^T: key half ks is key tiles 2ks, 2ks+1 (this lane's keys 4 q4 + i of each)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if constexpr (FMT == 0) {
-        f16x2 ph[NTW][4], pl[NTW][4];
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            split_f16(z[2 * ks + kk][nt][0], z[2 * ks + kk][nt][1], ph[nt][2 * kk], pl[nt][2 * kk]);
-            split_f16(z[2 * ks + kk][nt][2], z[2 * ks + kk][nt][3], ph[nt][2 * kk + 1], pl[nt][2 * kk + 1]);
-          }
-        // V scales (fp16) of this lane's keys in 64-dim group g: 8 values, element
-        // (q4*G64 + g)*16 + 8 ks .. of the page's V scales
-        const uint4 *vsp = &sl[buf][SCU];
-#pragma unroll
-        for (int g = 0; g < G64; ++g) {
-          const uint4 w = vsp[(q4 * G64 + g) * 2 + ks];
-          f16x2 sc[4] = {__builtin_bit_cast(f16x2, w.x), __builtin_bit_cast(f16x2, w.y), __builtin_bit_cast(f16x2, w.z),
-                         __builtin_bit_cast(f16x2, w.w)};
-          if (!full) {  // unwritten slots (weight 0) may hold NaN scales
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-              for (int e = 0; e < 2; ++e) {
-                const int key = p * kPage + 16 * (2 * ks + j / 2) + 4 * q4 + 2 * (j % 2) + e;
-                if (key >= L) sc[j][e] = _Float16(0);
-              }
-          }
-          f16x8 bh[NTW], bl[NTW];
-#pragma unroll
-          for (int nt = 0; nt < NTW; ++nt) {
-            f16x2 hi[4], lo[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) scale_pair(ph[nt][j], pl[nt][j], sc[j], hi[j], lo[j]);
-            bh[nt] = f16x8{hi[0][0], hi[0][1], hi[1][0], hi[1][1], hi[2][0], hi[2][1], hi[3][0], hi[3][1]};
-            bl[nt] = f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]};
-          }
-#pragma unroll
-          for (int dt = 4 * g; dt < 4 * g + 4; ++dt) {
-            const f16x8 va = lds_f16x8(&vl[buf][(dt * 2 + ks) * 64 + lane]);
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-              o[nt][dt] = mfma16(va, bh[nt], o[nt][dt]);
-              o[nt][dt] = mfma16(va, bl[nt], o[nt][dt]);
-            }
-          }
-        }
-      } else {  // FP8: one fp32 scale per key, the same for every dim
-        const float4 *vsp = reinterpret_cast<const float4 *>(static_cast<const float *>(a.v_scales) + pg * kPage);
-        f16x8 bh[NTW], bl[NTW];
-        float sv[2][4];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const float4 w = vsp[q4 * 4 + 2 * ks + kk];
-          sv[kk][0] = w.x;
-          sv[kk][1] = w.y;
-          sv[kk][2] = w.z;
-          sv[kk][3] = w.w;
-        }
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-          f16x2 hi[4], lo[4];
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            float pv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float pp = z[2 * ks + kk][nt][i];
-              pv[i] = (pp != 0.0f) ? pp * sv[kk][i] : 0.0f;  // unwritten slots: NaN scales
-            }
-            split_f16(pv[0], pv[1], hi[2 * kk], lo[2 * kk]);
-            split_f16(pv[2], pv[3], hi[2 * kk + 1], lo[2 * kk + 1]);
-          }
-          bh[nt] = f16x8{hi[0][0], hi[0][1], hi[1][0], hi[1][1], hi[2][0], hi[2][1], hi[3][0], hi[3][1]};
-          bl[nt] = f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]};
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const f16x8 va = lds_f16x8(&vl[buf][(dt * 2 + ks) * 64 + lane]);
-#pragma unroll
-          for (int nt = 0; nt < NTW; ++nt) {
-            o[nt][dt] = mfma16(va, bh[nt], o[nt][dt]);
-            o[nt][dt] = mfma16(va, bl[nt], o[nt][dt]);
-          }
-        }
-      }
-    }
-    __syncthreads();  // the next page's operands are in LDS; this page's buffer is free
-  }
-
-  // ---- rows: l summed over the 4 lanes of a row; normalized rows to out, or the partials
-#pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-    const float lt = sum_xor32(sum_xor16(lsum[nt]));
-    const int r = row0 + 16 * NTW * wave + 16 * nt + c16;
-    if (r >= R) continue;
-    const float l = any_bad ? NAN : lt;
-    if (a.direct_out != 0) {
-      const size_t orow = ((static_cast<size_t>(b) * a.T + r / a.group) * a.num_q_heads + kvh * a.group + r % a.group) * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const f32x4 v = o[nt][dt];
-        *reinterpret_cast<float4 *>(a.out + orow + 16 * dt + 4 * q4) = make_float4(v[0] / l, v[1] / l, v[2] / l, v[3] / l);
-      }
-    } else {
-      const size_t part = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits + split;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const f32x4 v = o[nt][dt];
-        *reinterpret_cast<float4 *>(a.ws_o + (part * R + r) * D + 16 * dt + 4 * q4) = make_float4(v[0], v[1], v[2], v[3]);
-      }
-      if (q4 == 0) {
-        a.ws_ml[(part * R + r) * 2 + 0] = m[nt];
-        a.ws_ml[(part * R + r) * 2 + 1] = l;
-      }
-    }
-  }
-}
-
-template <int D, int NT, int FMT, int QDT>
-hipError_t split_one(const AttnArgs &a, hipStream_t s) {
-  // fp32 queries need the hi+lo pair; bf16 queries are one exact f16, unless rotated (rk8v4)
-  constexpr int QLO = QDT == 0 ? 1 : ((FMT == 2 || FMT == 3) ? 2 : 0);
-  const dim3 grid(a.n_splits, a.num_kv_heads, a.num_seqs);
-  if (a.k_new != nullptr)
-    hipLaunchKernelGGL((attn_split_kernel<D, NT, FMT, QLO, kTeams, 1>), grid, dim3(256 * kTeams), 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_split_kernel<D, NT, FMT, QLO, kTeams, 0>), grid, dim3(256 * kTeams), 0, s, a);
-  return hipGetLastError();
-}
-
-template <int D, int FMT, int QDT>
-hipError_t prefill_one(const AttnArgs &a, hipStream_t s) {
-  if constexpr ((FMT == 0 || FMT == 1) && QDT == 1) {  // the prefill kernel: 128-row blocks
-    const dim3 grid(a.n_splits, a.num_kv_heads * a.row_blocks, a.num_seqs);
-    hipLaunchKernelGGL((prefill_kernel<D, FMT>), grid, dim3(64 * 8 / KVQ_PREFILL_NTW), 0, s, a);
-    return hipGetLastError();
-  }
-  constexpr int QLO = QDT == 0 ? 1 : ((FMT == 2 || FMT == 3) ? 2 : 0);
-  const dim3 grid(a.n_splits, a.num_kv_heads * a.row_blocks, a.num_seqs);
-  hipLaunchKernelGGL((attn_split_kernel<D, kPrefillNT, FMT, QLO, kPrefillTeams, 2>), grid, dim3(256 * kPrefillTeams),
-                     0, s, a);
-  return hipGetLastError();
-}
-
-template <int D>
-hipError_t merge_one(const AttnArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(a.num_seqs * a.T * a.num_q_heads * (D / 64)), dim3(64), 0, s, a);
-  return hipGetLastError();
-}
-
-}  // namespace
+hipError_t launch_attn_split_f0(int head_dim, int nt, int q_dtype, const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_split_f1(int head_dim, int nt, int q_dtype, const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_split_f2(int head_dim, int nt, int q_dtype, const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_split_f3(int head_dim, int nt, int q_dtype, const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_split_f4(int head_dim, int nt, int q_dtype, const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_prefill_f0(int head_dim, int q_dtype, const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_prefill_f1(int head_dim, int q_dtype, const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_prefill_f2(int head_dim, int q_dtype, const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_prefill_f3(int head_dim, int q_dtype, const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_prefill_f4(int head_dim, int q_dtype, const AttnArgs &a, hipStream_t s);
 
 hipError_t launch_attn_split(int format, int head_dim, int q_dtype, const AttnArgs &a, hipStream_t s) {
   const int nt = (a.rows + 15) / 16;
-#define KVQ_SPLIT_CASE(DD, NTT, F, Q) \
-  if (head_dim == DD && nt == NTT && format == F && q_dtype == Q) return split_one<DD, NTT, F, Q>(a, s);
-#define KVQ_SPLIT_DQ(DD, NTT) \
-  KVQ_SPLIT_CASE(DD, NTT, 0, 0) KVQ_SPLIT_CASE(DD, NTT, 0, 1) KVQ_SPLIT_CASE(DD, NTT, 1, 0) KVQ_SPLIT_CASE(DD, NTT, 1, 1) \
-  KVQ_SPLIT_CASE(DD, NTT, 2, 0) KVQ_SPLIT_CASE(DD, NTT, 2, 1) KVQ_SPLIT_CASE(DD, NTT, 3, 0) KVQ_SPLIT_CASE(DD, NTT, 3, 1) \
-  KVQ_SPLIT_CASE(DD, NTT, 4, 0) KVQ_SPLIT_CASE(DD, NTT, 4, 1)
-  KVQ_SPLIT_DQ(128, 1)
-  KVQ_SPLIT_DQ(128, 2)
-  KVQ_SPLIT_DQ(256, 1)
-  KVQ_SPLIT_DQ(256, 2)
-#undef KVQ_SPLIT_DQ
-#undef KVQ_SPLIT_CASE
-  return hipErrorInvalidValue;
+  switch (format) {
+    case 0: return launch_attn_split_f0(head_dim, nt, q_dtype, a, s);
+    case 1: return launch_attn_split_f1(head_dim, nt, q_dtype, a, s);
+    case 2: return launch_attn_split_f2(head_dim, nt, q_dtype, a, s);
+    case 3: return launch_attn_split_f3(head_dim, nt, q_dtype, a, s);
+    case 4: return launch_attn_split_f4(head_dim, nt, q_dtype, a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_attn_prefill(int format, int head_dim, int q_dtype, const AttnArgs &a, hipStream_t s) {
-#define KVQ_PF_CASE(DD, F, Q) \
-  if (head_dim == DD && format == F && q_dtype == Q) return prefill_one<DD, F, Q>(a, s);
-  KVQ_PF_CASE(128, 0, 0) KVQ_PF_CASE(128, 0, 1) KVQ_PF_CASE(128, 1, 0) KVQ_PF_CASE(128, 1, 1)
-  KVQ_PF_CASE(256, 0, 0) KVQ_PF_CASE(256, 0, 1) KVQ_PF_CASE(256, 1, 0) KVQ_PF_CASE(256, 1, 1)
-  KVQ_PF_CASE(128, 2, 0) KVQ_PF_CASE(128, 2, 1) KVQ_PF_CASE(256, 2, 0) KVQ_PF_CASE(256, 2, 1)
-  KVQ_PF_CASE(128, 3, 0) KVQ_PF_CASE(128, 3, 1) KVQ_PF_CASE(256, 3, 0) KVQ_PF_CASE(256, 3, 1)
-  KVQ_PF_CASE(128, 4, 0) KVQ_PF_CASE(128, 4, 1) KVQ_PF_CASE(256, 4, 0) KVQ_PF_CASE(256, 4, 1)
-#undef KVQ_PF_CASE
-  return hipErrorInvalidValue;
+  switch (format) {
+    case 0: return launch_attn_prefill_f0(head_dim, q_dtype, a, s);
+    case 1: return launch_attn_prefill_f1(head_dim, q_dtype, a, s);
+    case 2: return launch_attn_prefill_f2(head_dim, q_dtype, a, s);
+    case 3: return launch_attn_prefill_f3(head_dim, q_dtype, a, s);
+    case 4: return launch_attn_prefill_f4(head_dim, q_dtype, a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_attn_merge(int head_dim, const AttnArgs &a, hipStream_t s) {

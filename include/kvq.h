@@ -187,10 +187,15 @@ size_t paged_decode_attn_workspace_bytes(int32_t num_seqs, int32_t T, int32_t nu
  *   workspace  >= paged_decode_attn_workspace_bytes(...) bytes, no
  *              initialization needed; calls that share a workspace must be
  *              ordered on one stream.
- * Accuracy: K/V codes and bf16 queries enter the matrix cores exactly; the
- * softmax weights enter as an fp16 hi+lo pair; all sums are fp32.  Against an
- * fp64 evaluation of the same formula the error is a few 1e-5 at unit-scale
- * inputs.
+ * Accuracy: K/V codes enter the matrix cores exactly (converted to f16); each
+ * softmax weight times its V scale enters as an f16 hi+lo pair, kept inside
+ * f16's normal range by two powers of two (one folded into the weights and the
+ * row sums, one per wave set from the largest V scale it has seen and taken out
+ * of the accumulators at the end), so weights far below the row maximum, e.g.
+ * thousands of near-uniform keys under an attention sink, keep their share of
+ * the output; all sums are fp32.  Against an fp64 evaluation of the same
+ * formula the error is a few 1e-5 at unit-scale inputs and stays below 1e-4 on
+ * sink-shaped softmaxes up to 262,144 keys per chunk.
  */
 int paged_decode_attn(const kvq_cache_t *cache, const void *q, int32_t q_dtype, int32_t num_seqs,
                       int32_t T, int32_t num_q_heads, const int32_t *block_table,

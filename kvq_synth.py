@@ -174,6 +174,43 @@ def make(name_or_shape, seed: int | None = None, extra_blocks: int = 4) -> Workl
         v_src.append(_source(gen, s.lens[b], s.Hkv, s.D, s.src, s.outliers, v_ch))
     q = torch.randn((s.B, s.T, s.Hq, s.D), generator=gen, dtype=torch.float32)
     q = bf16_bits(q.to(torch.bfloat16)) if s.src == SRC_BF16 else q.numpy()
+    return _with_tables(s, gen, k_src, v_src, q, extra_blocks)
+
+
+def make_sink(s: Shape, gap_nats: float = 13.0, stride: int = 4096, seed: int = 0, v_mean: float = 1.0,
+              v_sd: float = 0.2, k_sd: float = 0.05, extra_blocks: int = 4) -> Workload:
+    """Inputs whose softmax has attention sinks: a few dominant keys over many near-uniform ones.
+
+    Every query row of KV head h is the same seeded +-1 pattern u_h.  Keys are
+    N(0, k_sd^2) except one key every `stride` positions (positions 0, stride, ...),
+    which is u_h * gap_nats / sqrt(D): with the softmax scale 1/sqrt(D) its logit lies
+    gap_nats above the others, whose logits are ~N(0, k_sd^2).  Values are
+    v_mean + v_sd * N(0, 1): a nonzero mean and small group scales, so the many tiny
+    weights of the near-uniform keys carry a visible share of the output.  s.outliers
+    is ignored.
+    """
+    gen = torch.Generator().manual_seed(0x51C0 + seed)
+    u = torch.randint(0, 2, (s.Hkv, s.D), generator=gen).to(torch.float32) * 2.0 - 1.0
+    a = gap_nats / math.sqrt(s.D)
+    k_src, v_src = [], []
+    for b in range(s.B):
+        L = s.lens[b]
+        k = torch.randn((L, s.Hkv, s.D), generator=gen, dtype=torch.float32) * k_sd
+        k[0:L:stride] = u * a
+        v = v_mean + v_sd * torch.randn((L, s.Hkv, s.D), generator=gen, dtype=torch.float32)
+        if s.src == SRC_BF16:
+            k_src.append(bf16_bits(k.to(torch.bfloat16)))
+            v_src.append(bf16_bits(v.to(torch.bfloat16)))
+        else:
+            k_src.append(k.numpy())
+            v_src.append(v.numpy())
+    G = s.Hq // s.Hkv
+    q = u.repeat_interleave(G, dim=0)[None, None].expand(s.B, s.T, s.Hq, s.D).contiguous()
+    q = bf16_bits(q.to(torch.bfloat16)) if s.src == SRC_BF16 else q.numpy()
+    return _with_tables(s, gen, k_src, v_src, q, extra_blocks)
+
+
+def _with_tables(s: Shape, gen: torch.Generator, k_src, v_src, q, extra_blocks: int) -> Workload:
     # shared pool: every (sequence, page) pair gets a shuffled physical block id
     pages = [math.ceil(L / PAGE) for L in s.lens]
     total = sum(pages)

@@ -187,6 +187,88 @@ __device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 // Rescaling threshold of the online softmax, log2 units (see the softmax phase).
 constexpr float kLazy = 8.0f;
 
+// ---- Exponent offsets of the P·V operands.
+//
+// The weight of key j enters the matrix cores as the f16 pair of p_j * s_j (p_j its softmax
+// weight against the running reference, s_j its V scale), and f16 has only ~40 binades,
+// 2^-24 .. 2^16.  Both factors span far more: weights reach down to where thousands of
+// near-uniform keys under a dominant one (an attention sink) still sum to a visible share
+// of the output, and scales are whatever the data make them.  Two powers of two keep the
+// products in the normal range without any per-key work:
+//   - kWeightExp: the weights are formed as exp2(z - m + kWeightExp), so with the lazy
+//     reference (weights <= 2^kLazy) they stay <= 2^15 and their f16 hi + lo pair carries
+//     21 bits down to p ~ 2^-11 and stays exact to 2^-31 absolute below; the row sums carry
+//     the same offset, so the normalized output does not see it.
+//   - the V-scale exponent E (per wave, only ever lowered within a chunk): the scales the
+//     products use are s * 2^E, with E set from the largest scale the wave has seen so
+//     that the largest product stays below 2^15; the accumulators carry 2^E, taken out
+//     when the chunk's output is written.  When a page brings a larger scale, E drops and
+//     the accumulators are rescaled (rare: once per chunk on typical data).
+// The FP8 pool keeps its weights in fp32 up to the product, so there both offsets fold into
+// the exponent of the weights and the row sums (E chosen so that p * s stays below 2^15).
+constexpr int kWeightExp = 15 - static_cast<int>(kLazy);  // 7
+constexpr int kVexpMax = 14, kVexpMin = -16;               // E range of fp16 scales (2^E is an f16)
+constexpr int kFp8ExpMax = 30, kFp8ExpMin = -60;           // E range of fp32 scales
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// The largest of the non-negative fp16 scales packed in n words, as fp16 bits in both
+// halves of every lane: an integer max (non-negative IEEE values order like their bit
+// patterns), a tree over the words, then over the four 16-lane groups of the wave.
+template <int N>
+__device__ inline uint32_t max_f16_scales(const uint32_t (&w)[N]) {
+  u16x2 t[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) t[i] = __builtin_bit_cast(u16x2, w[i]);
+#pragma unroll
+  for (int h = 1; h < N; h <<= 1)
+#pragma unroll
+    for (int i = 0; i + h < N; i += 2 * h) t[i] = __builtin_elementwise_max(t[i], t[i + h]);
+  u16x2 x = __builtin_elementwise_max(t[0], u16x2{t[0][1], t[0][0]});
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __builtin_elementwise_max(__builtin_bit_cast(u16x2, r[0]), __builtin_bit_cast(u16x2, r[1]));
+  u = __builtin_bit_cast(uint32_t, x);
+  r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = __builtin_elementwise_max(__builtin_bit_cast(u16x2, r[0]), __builtin_bit_cast(u16x2, r[1]));
+  return __builtin_bit_cast(uint32_t, x);
+}
+
+// The same for non-negative fp32 scales: the largest as fp32 bits in every lane.
+template <int N>
+__device__ inline uint32_t max_f32_scales(const uint32_t (&w)[N]) {
+  uint32_t t[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) t[i] = w[i];
+#pragma unroll
+  for (int h = 1; h < N; h <<= 1)
+#pragma unroll
+    for (int i = 0; i + h < N; i += 2 * h) t[i] = max(t[i], t[i + h]);
+  auto r = __builtin_amdgcn_permlane16_swap(t[0], t[0], false, false);
+  const uint32_t u = max(r[0], r[1]);
+  r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return max(r[0], r[1]);
+}
+
+// E for the largest scale (wave-uniform result): fp16 scales (bits h) get smax * 2^E in
+// [1/2, 1), so products with weights <= 2^15 stay below 2^15; fp32 (FP8) scales get
+// smax * 2^E in [2^6, 2^7), for weights <= 2^kLazy.  Zero or subnormal maxima take the top
+// of the range.  Clamped to the ranges above.
+__device__ inline int scale_exponent_f16(uint32_t hbits) {
+  const int ef = static_cast<int>(__builtin_amdgcn_readfirstlane(hbits) >> 10) & 0x1F;  // f16 exponent field
+  return max(min(14 - ef, kVexpMax), kVexpMin);
+}
+__device__ inline int scale_exponent_f32(uint32_t fbits) {
+  const int e = static_cast<int>(__builtin_amdgcn_readfirstlane(fbits) >> 23) & 0xFF;  // fp32 exponent field
+  return max(min(133 - e, kFp8ExpMax), kFp8ExpMin);
+}
+
+// 2^E as two packed f16 (E in [kVexpMin, kVexpMax]; 2^-15 and 2^-16 are subnormal).
+__device__ inline uint32_t f16x2_pow2(int E) {
+  const uint32_t h = (E >= -14) ? static_cast<uint32_t>(E + 15) << 10 : (0x400u >> (-14 - E));
+  return h | (h << 16);
+}
+
 // One wave's share of one page: its K tile (16 keys x all dims) and its V dim
 // tiles (all 64 keys), with their scales.  rk8v4 (FMT 2): K as INT8; V as 4-bit codes,
 // one 16-byte load per pair of dim tiles, and the fp16 scales of two 32-dim groups.
@@ -522,6 +604,63 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   float m[NT], lsum[NT];
   int last[NT];
   f32x4 o[NT][DPW];
+  // exponent offsets of the P·V operands (see kWeightExp): fp16-scale formats carry kWeightExp
+  // in the weights and row sums and the wave's V-scale exponent vexp in o; FP8 carries vexp
+  // in the weights, row sums and o alike; BF16 needs neither (its weights stay fp32-ranged)
+  constexpr bool F16PAIR = (FMT == 0 || FMT == 2 || FMT == 3);
+  int vexp = (FMT == 1) ? kFp8ExpMax : kVexpMax;  // wave-uniform
+  auto wexp = [&]() -> float { return F16PAIR ? static_cast<float>(kWeightExp) : (FMT == 1 ? static_cast<float>(vexp) : 0.0f); };
+  // V scales of slots at or past L (never written: poison) -> 0, on pages that hold such slots;
+  // the V-scale words of a lane group hold keys 16(2j + e/4) + 4 q4 + e%4 (e: the element of
+  // word j, 8 fp16 or 4 fp32 per uint4) for every format with scales
+  auto zero_unwritten_scales = [&](PageRegs<D, FMT> &pr, int p) {
+    const int kbase = p * kPage + 4 * q4;
+    if constexpr (FMT == 1) {  // vs[j]: keys 16 j + 4 q4 + i
+#pragma unroll
+      for (int j = 0; j < PageRegs<D, FMT>::VSN; ++j) {
+        pr.vs[j].x = (kbase + 16 * j + 0 < L) ? pr.vs[j].x : 0u;
+        pr.vs[j].y = (kbase + 16 * j + 1 < L) ? pr.vs[j].y : 0u;
+        pr.vs[j].z = (kbase + 16 * j + 2 < L) ? pr.vs[j].z : 0u;
+        pr.vs[j].w = (kbase + 16 * j + 3 < L) ? pr.vs[j].w : 0u;
+      }
+    } else if constexpr (F16PAIR) {
+      // word d of a uint4 holding key tiles kt0, kt0 + 1: keys 16 (kt0 + d/2) + 4 q4 + 2 (d%2) + {0, 1}
+#pragma unroll
+      for (int j = 0; j < PageRegs<D, FMT>::VSN; ++j) {
+        const int kt0 = (FMT == 0) ? 2 * j : 2 * (j % 2);
+        uint32_t mw[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int key = kbase + 16 * (kt0 + d / 2) + 2 * (d % 2);
+          mw[d] = ((key < L) ? 0x0000FFFFu : 0u) | ((key + 1 < L) ? 0xFFFF0000u : 0u);
+        }
+        pr.vs[j].x &= mw[0];
+        pr.vs[j].y &= mw[1];
+        pr.vs[j].z &= mw[2];
+        pr.vs[j].w &= mw[3];
+      }
+    }
+  };
+  // the largest V scale of this wave's share of page pr -> lower vexp if it asks for less;
+  // returns whether it did, with f the factor the accumulators (and, for FP8, the row sums)
+  // must be scaled by
+  auto lower_vexp = [&](PageRegs<D, FMT> &pr, float &f) -> bool {
+    constexpr int NW4 = 4 * PageRegs<D, FMT>::VSN;
+    uint32_t w[NW4];
+#pragma unroll
+    for (int j = 0; j < PageRegs<D, FMT>::VSN; ++j) {
+      w[4 * j] = pr.vs[j].x;
+      w[4 * j + 1] = pr.vs[j].y;
+      w[4 * j + 2] = pr.vs[j].z;
+      w[4 * j + 3] = pr.vs[j].w;
+    }
+    const int E = (FMT == 1) ? scale_exponent_f32(max_f32_scales(w)) : scale_exponent_f16(max_f16_scales(w));
+    const int cur = __builtin_amdgcn_readfirstlane(vexp);  // uniform: keep the test scalar
+    if (E >= cur) return false;
+    vexp = E;
+    f = __builtin_ldexpf(1.0f, E - cur);
+    return true;
+  };
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     m[nt] = -INFINITY;
@@ -832,10 +971,10 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int r = 16 * nt + c16;
-        const float msafe = (m[nt] == -INFINITY) ? 0.0f : m[nt];
+        const float mref = ((m[nt] == -INFINITY) ? 0.0f : m[nt]) - wexp();  // weights carry 2^wexp
         float pv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pv[i] = exp2_hw(z[nt][i] - msafe);
+        for (int i = 0; i < 4; ++i) pv[i] = exp2_hw(z[nt][i] - mref);
         psum[nt] = (pv[0] + pv[1]) + (pv[2] + pv[3]);
         if constexpr (FMT != 1 && FMT != 4) {
           // INT8 and rk8v4: the weights go out as f16 hi+lo pairs (the V scales, fp16, are
@@ -851,6 +990,22 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
         }
       }
     };
+    if constexpr (FMT == 1) {
+      // FP8: the V-scale exponent rides on the weights, so it is settled before they are
+      // written (all four waves of the team read the same 64 scales and agree on it)
+      if (valid) {
+        if (!full) zero_unwritten_scales(pr, p);
+        float f;
+        if (lower_vexp(pr, f)) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            lsum[nt] *= f;
+#pragma unroll
+            for (int j = 0; j < DPW; ++j) o[nt][j] *= f;
+          }
+        }
+      }
+    }
     bool over = false;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) over |= mloc[nt] > m[nt] + kLazy;  // m = -inf: any visible key
@@ -887,6 +1042,28 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
           const int r = (tid >> 6) + k * NW;
           if (r < n_rows && blk_r[k] >= 0 && blk_r[k] < a.num_blocks)
             store_row<FMT, D>(aa, xr[k], kvh, r & 1, static_cast<long>(L) - a.T + t_lo + (r >> 1), blk_r[k], lane);
+        }
+      }
+    }
+    if constexpr (F16PAIR) {
+      // this wave's V-scale exponent: lowered (and o rescaled) if the page's scales ask for
+      // it, then applied to the scales the products use
+      if (valid) {
+        if (!full) zero_unwritten_scales(pr, p);
+        float f;
+        if (lower_vexp(pr, f)) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int j = 0; j < DPW; ++j) o[nt][j] *= f;
+        }
+        const f16x2 e2 = __builtin_bit_cast(f16x2, f16x2_pow2(vexp));
+#pragma unroll
+        for (int j = 0; j < PageRegs<D, FMT>::VSN; ++j) {
+          pr.vs[j].x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, pr.vs[j].x) * e2);
+          pr.vs[j].y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, pr.vs[j].y) * e2);
+          pr.vs[j].z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, pr.vs[j].z) * e2);
+          pr.vs[j].w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, pr.vs[j].w) * e2);
         }
       }
     }
@@ -929,7 +1106,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       lds_l[team][wave][16 * nt + c16] = lsum[nt];
-      if (wave == 0) lds_m[team][16 * nt + c16] = m[nt];
+      if (wave == 0) lds_m[team][16 * nt + c16] = m[nt] - wexp();  // the reference of l (and o)
     }
   }
   const int any_bad = __syncthreads_or(bad ? 1 : 0);
@@ -949,7 +1126,8 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     }
     Mrow[nt] = M;
     Lrow[nt] = any_bad ? NAN : Lt;
-    fown[nt] = exp2f(m[nt] - Ms);
+    // this wave's o carries 2^(wexp + vexp) for the fp16-scale formats (l only 2^wexp)
+    fown[nt] = exp2f(m[nt] - wexp() - Ms) * (F16PAIR ? __builtin_ldexpf(1.0f, -vexp) : 1.0f);
   }
   // teams 1.. hand their scaled outputs to team 0 through LDS (fixed order: deterministic)
   float *fin = pbuf;
@@ -1091,6 +1269,10 @@ __global__ __launch_bounds__(64 * 8 / KVQ_PREFILL_NTW, 1) void prefill_kernel(At
   // so the waves read them from LDS (FP8 pools, one scale per key, read theirs directly)
   constexpr int SCU = (FMT == 0) ? D * 2 / 16 : 1;  // uint4 per scale array
   __shared__ uint4 sl[2][2 * SCU];
+  // per buffer: the V-scale exponent in force from that page on (the running minimum of the
+  // pages' exponents, see kWeightExp); every wave streams the same pages, so it is one
+  // value for the workgroup, kept by wave 0, which converts the scales
+  __shared__ int32_t sl_vexp[2];
   __shared__ int32_t lds_pg[kMaxPrefillChunkPages];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q4 = lane >> 4, c16 = lane & 15;
@@ -1130,6 +1312,8 @@ __global__ __launch_bounds__(64 * 8 / KVQ_PREFILL_NTW, 1) void prefill_kernel(At
 
   // ---- page codes: HBM -> registers -> f16 operands in LDS
   uint4 kc[CPT], vc[CPT], sc4 = make_uint4(0, 0, 0, 0);
+  [[maybe_unused]] uint4 vs4 = make_uint4(0, 0, 0, 0);  // FP8: 16 threads hold the page's 64 V scales
+  int cvexp = (FMT == 1) ? kFp8ExpMax : kVexpMax;       // wave 0: the exponent of the last converted page
   auto gload = [&](int i) {
     const size_t pg = static_cast<uint32_t>(lds_pg[i]);
     const uint4 *kp = reinterpret_cast<const uint4 *>(a.k_codes + pg * kPage * D);
@@ -1145,11 +1329,61 @@ __global__ __launch_bounds__(64 * 8 / KVQ_PREFILL_NTW, 1) void prefill_kernel(At
                                                           pg * D);
         sc4 = ld_stream(sp + (tid % SCU));
       }
+    } else {
+      if (tid < 16) vs4 = ld_stream(reinterpret_cast<const uint4 *>(static_cast<const float *>(a.v_scales) + pg * kPage) + tid);
     }
   };
-  auto convert = [&](int buf, int p) {
+  // wave 0: the page's largest V scale (slots at or past L skipped: they hold poison) sets the
+  // V-scale exponent; INT8 scales go to LDS already multiplied by 2^exponent
+  auto page_vexp = [&](int buf, int p) {
+    uint32_t mx = 0;
     if constexpr (FMT == 0) {
-      if (tid < 2 * SCU) sl[buf][tid] = sc4;
+      if (tid >= SCU && tid < 2 * SCU) {  // V-scale elements 8u .. 8u+7: (run * G64 + g) * 16 + pos
+        const int u = tid - SCU, run = (8 * u / 16) / G64;
+        const uint32_t w[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int pos = (8 * u + e) % 16, slot = 16 * (pos / 4) + 4 * run + pos % 4;
+          const uint32_t h = (w[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+          mx = (p * kPage + slot < L) ? max(mx, h) : mx;
+        }
+      }
+    } else {
+      if (tid < 16) {  // elements 4 tid + i: run tid / 4, pos 4 (tid % 4) + i
+        const uint32_t w[4] = {vs4.x, vs4.y, vs4.z, vs4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int slot = 16 * (tid % 4) + 4 * (tid / 4) + i;
+          mx = (p * kPage + slot < L) ? max(mx, w[i]) : mx;
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), o)));
+    auto r = __builtin_amdgcn_permlane16_swap(mx, mx, false, false);
+    mx = max(r[0], r[1]);
+    r = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
+    mx = max(r[0], r[1]);
+    const int E = (FMT == 1) ? scale_exponent_f32(mx) : scale_exponent_f16(mx);
+    cvexp = min(cvexp, E);
+    if (lane == 0) sl_vexp[buf] = cvexp;
+  };
+  auto convert = [&](int buf, int p) {
+    if (wave == 0) {
+      page_vexp(buf, p);
+      if constexpr (FMT == 0) {
+        if (tid < SCU) {
+          sl[buf][tid] = sc4;
+        } else if (tid < 2 * SCU) {  // V scales times 2^cvexp (exact: a power of two, normal results)
+          const f16x2 e2 = __builtin_bit_cast(f16x2, f16x2_pow2(cvexp));
+          uint4 v = sc4;
+          v.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, v.x) * e2);
+          v.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, v.y) * e2);
+          v.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, v.z) * e2);
+          v.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, v.w) * e2);
+          sl[buf][tid] = v;
+        }
+      }
     }
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
@@ -1211,6 +1445,9 @@ __global__ __launch_bounds__(64 * 8 / KVQ_PREFILL_NTW, 1) void prefill_kernel(At
 
   f32x4 o[NTW][DT];
   float m[NTW], lsum[NTW];
+  // exponent offsets of the P·V operands (see kWeightExp): INT8 weights and row sums carry
+  // 2^kWeightExp and o also the V-scale exponent vexp; FP8 weights, row sums and o carry vexp
+  int vexp = (FMT == 1) ? kFp8ExpMax : kVexpMax;  // uniform over the workgroup
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     m[nt] = -INFINITY;
@@ -1225,6 +1462,21 @@ __global__ __launch_bounds__(64 * 8 / KVQ_PREFILL_NTW, 1) void prefill_kernel(At
     if (it + 1 < npg) convert(buf ^ 1, p + 1);  // the next page, loaded one iteration ago
     if (it + 2 < npg) gload(it + 2);
     const bool full = (p * kPage + kPage - 1) <= lo_last;  // every real row sees every key of the page
+    {  // the page's V-scale exponent (set when it was converted): lower vexp, rescale if it moved
+      const int E = __builtin_amdgcn_readfirstlane(sl_vexp[buf]);
+      const int cur = __builtin_amdgcn_readfirstlane(vexp);
+      if (E < cur) {
+        const float f = __builtin_ldexpf(1.0f, E - cur);
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          if constexpr (FMT == 1) lsum[nt] *= f;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[nt][dt] *= f;
+        }
+        vexp = E;
+      }
+    }
+    const float wexp = (FMT == 1) ? static_cast<float>(vexp) : static_cast<float>(kWeightExp);
 
     // ---- S^T = K Q^T for the 4 key tiles x this wave's 2 row tiles, scales folded per 64 dims
     float z[4][NTW][4];
@@ -1320,7 +1572,7 @@ __global__ __launch_bounds__(64 * 8 / KVQ_PREFILL_NTW, 1) void prefill_kernel(At
     }
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
-      const float ms = (m[nt] == -INFINITY) ? 0.0f : m[nt];
+      const float ms = ((m[nt] == -INFINITY) ? 0.0f : m[nt]) - wexp;  // the weights carry 2^wexp
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -1421,7 +1673,11 @@ __global__ __launch_bounds__(64 * 8 / KVQ_PREFILL_NTW, 1) void prefill_kernel(At
     __syncthreads();  // the next page's operands are in LDS; this page's buffer is free
   }
 
-  // ---- rows: l summed over the 4 lanes of a row; normalized rows to out, or the partials
+  // ---- rows: l summed over the 4 lanes of a row; normalized rows to out, or the partials.
+  // The exponent offsets come out here: INT8 o carries 2^vexp more than l; the reference of
+  // l (and o) is m - kWeightExp (INT8) or m - vexp (FP8).
+  const float oscale = (FMT == 1) ? 1.0f : __builtin_ldexpf(1.0f, -vexp);
+  const float wexp_end = (FMT == 1) ? static_cast<float>(vexp) : static_cast<float>(kWeightExp);
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     const float lt = sum_xor32(sum_xor16(lsum[nt]));
@@ -1432,18 +1688,18 @@ __global__ __launch_bounds__(64 * 8 / KVQ_PREFILL_NTW, 1) void prefill_kernel(At
       const size_t orow = ((static_cast<size_t>(b) * a.T + r / a.group) * a.num_q_heads + kvh * a.group + r % a.group) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const f32x4 v = o[nt][dt];
+        const f32x4 v = o[nt][dt] * oscale;
         *reinterpret_cast<float4 *>(a.out + orow + 16 * dt + 4 * q4) = make_float4(v[0] / l, v[1] / l, v[2] / l, v[3] / l);
       }
     } else {
       const size_t part = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits + split;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const f32x4 v = o[nt][dt];
+        const f32x4 v = o[nt][dt] * oscale;
         *reinterpret_cast<float4 *>(a.ws_o + (part * R + r) * D + 16 * dt + 4 * q4) = make_float4(v[0], v[1], v[2], v[3]);
       }
       if (q4 == 0) {
-        a.ws_ml[(part * R + r) * 2 + 0] = m[nt];
+        a.ws_ml[(part * R + r) * 2 + 0] = m[nt] - wexp_end;
         a.ws_ml[(part * R + r) * 2 + 1] = l;
       }
     }

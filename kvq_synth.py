@@ -210,6 +210,38 @@ def make_sink(s: Shape, gap_nats: float = 13.0, stride: int = 4096, seed: int = 
     return _with_tables(s, gen, k_src, v_src, q, extra_blocks)
 
 
+def make_wide(s: Shape, span_log2: float = 8.0, seed: int = 0, small_run: int | None = None,
+              extra_blocks: int = 4) -> Workload:
+    """Inputs whose rows span a wide range of magnitudes.
+
+    Keys and queries ~ N(0, 1); each value row (token, KV head) is N(0, 1) times
+    2^u with u ~ U(-span_log2, span_log2) drawn per row, so the V scales of one
+    page differ by up to 2^(2 span_log2) and the largest of them falls on any slot.
+    With small_run = r (0..3), u is instead -span_log2 for the positions j with
+    (j % 16) // 4 == r and +span_log2 elsewhere: every 16-slot run of a page has
+    the same four small rows.  s.outliers is ignored.
+    """
+    gen = torch.Generator().manual_seed(0x3D0E + seed)
+    k_src, v_src = [], []
+    for b in range(s.B):
+        L = s.lens[b]
+        k = torch.randn((L, s.Hkv, s.D), generator=gen, dtype=torch.float32)
+        u = (torch.rand((L, s.Hkv, 1), generator=gen, dtype=torch.float32) * 2.0 - 1.0) * span_log2
+        if small_run is not None:
+            small = ((torch.arange(L) % 16) // 4 == small_run).to(torch.float32)[:, None, None]
+            u = span_log2 * (1.0 - 2.0 * small) + 0.0 * u
+        v = torch.randn((L, s.Hkv, s.D), generator=gen, dtype=torch.float32) * torch.exp2(u)
+        if s.src == SRC_BF16:
+            k_src.append(bf16_bits(k.to(torch.bfloat16)))
+            v_src.append(bf16_bits(v.to(torch.bfloat16)))
+        else:
+            k_src.append(k.numpy())
+            v_src.append(v.numpy())
+    q = torch.randn((s.B, s.T, s.Hq, s.D), generator=gen, dtype=torch.float32)
+    q = bf16_bits(q.to(torch.bfloat16)) if s.src == SRC_BF16 else q.numpy()
+    return _with_tables(s, gen, k_src, v_src, q, extra_blocks)
+
+
 def _with_tables(s: Shape, gen: torch.Generator, k_src, v_src, q, extra_blocks: int) -> Workload:
     # shared pool: every (sequence, page) pair gets a shuffled physical block id
     pages = [math.ceil(L / PAGE) for L in s.lens]

@@ -13,7 +13,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvq.so")
+# KVQ_LIBRARY names another build of the same sources (e.g. for A/B timing of two builds)
+LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(_HERE, "libkvq.so")
 
 INT8_G64 = 0
 FP8_E4M3_ROW = 1

@@ -38,23 +38,32 @@ def _run(cmd):
     return r.returncode, err
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
+def build(verbose: bool = False, jobs: int | None = None, out: str | None = None, src_dir: str | None = None,
+          defines: tuple = ()) -> str:
+    """Compile and link; `out`, `src_dir` and `defines` (-D flags) build a variant library
+    (another tree's sources, or a compile-time option) beside the default one."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    objs = [os.path.join(OBJ_DIR, os.path.basename(s)[:-4] + ".o") for s in SOURCES]
+    lib = out or LIB
+    obj_dir = OBJ_DIR if out is None else os.path.join(OBJ_DIR, os.path.basename(out)[:-3])
+    os.makedirs(obj_dir, exist_ok=True)
+    sources = SOURCES if src_dir is None else [os.path.join(src_dir, os.path.basename(s)) for s in SOURCES]
+    objs = [os.path.join(obj_dir, os.path.basename(s)[:-4] + ".o") for s in sources]
+    flags = HIPCC_FLAGS + [f"-D{d}" for d in defines]
+    if src_dir is not None:
+        flags += ["-I", os.path.join(src_dir, "..", "..", "include")]
     jobs = jobs or min(len(SOURCES), max(1, min(16, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        res = list(ex.map(lambda so: _run([hipcc] + HIPCC_FLAGS + ["-c", so[0], "-o", so[1]]), zip(SOURCES, objs)))
-    for (rc, err), src in zip(res, SOURCES):
+        res = list(ex.map(lambda so: _run([hipcc] + flags + ["-c", so[0], "-o", so[1]]), zip(sources, objs)))
+    for (rc, err), src in zip(res, sources):
         if rc != 0:
             raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n" + err)
         if verbose and err.strip():
             print(err, file=sys.stderr)
-    rc, err = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", LIB + ".tmp"])
+    rc, err = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", lib + ".tmp"])
     if rc != 0:
         raise RuntimeError("hipcc link failed:\n" + err)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 def stale() -> bool:

@@ -210,28 +210,40 @@ constexpr int kWeightExp = 15 - static_cast<int>(kLazy);  // 7
 constexpr int kVexpMax = 14, kVexpMin = -16;               // E range of fp16 scales (2^E is an f16)
 constexpr int kFp8ExpMax = 30, kFp8ExpMin = -60;           // E range of fp32 scales
 
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-// The largest of the non-negative fp16 scales packed in n words, as fp16 bits in both
-// halves of every lane: an integer max (non-negative IEEE values order like their bit
-// patterns), a tree over the words, then over the four 16-lane groups of the wave.
+// The largest of the finite non-negative fp16 scales packed in n words, as fp16 bits (low half)
+// in every lane: a three-input tree over the words (IEEE maximum: the scales are
+// finite, the poison of unwritten slots is zeroed before), the two halves, then the four
+// 16-lane groups of the wave (non-negative IEEE values order like their bit patterns).
 template <int N>
 __device__ inline uint32_t max_f16_scales(const uint32_t (&w)[N]) {
-  u16x2 t[N];
+  f16x2 t[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) t[i] = __builtin_bit_cast(u16x2, w[i]);
+  for (int i = 0; i < N; ++i) t[i] = __builtin_bit_cast(f16x2, w[i]);
+  int n = N;
 #pragma unroll
-  for (int h = 1; h < N; h <<= 1)
+  for (int round = 0; round < 4; ++round) {
+    if (n > 1) {
+      int k = 0;
 #pragma unroll
-    for (int i = 0; i + h < N; i += 2 * h) t[i] = __builtin_elementwise_max(t[i], t[i + h]);
-  u16x2 x = __builtin_elementwise_max(t[0], u16x2{t[0][1], t[0][0]});
-  uint32_t u = __builtin_bit_cast(uint32_t, x);
+      for (int i = 0; i < N; i += 3) {
+        if (i < n) {
+          f16x2 x = t[i];
+          if (i + 1 < n) x = __builtin_elementwise_maximum(x, t[i + 1]);
+          if (i + 2 < n) x = __builtin_elementwise_maximum(x, t[i + 2]);
+          t[k++] = x;
+        }
+      }
+      n = k;
+    }
+  }
+  const f16x2 x = __builtin_elementwise_maximum(t[0], f16x2{t[0][1], t[0][0]});
+  // across the lane groups as 32-bit integers (the fp16 bits zero-extended): hipcc 7.2 drops a
+  // packed 16-bit max of the two results of a lane swap, a 32-bit max it keeps
+  uint32_t u = __builtin_bit_cast(uint32_t, x) & 0xFFFFu;
   auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  x = __builtin_elementwise_max(__builtin_bit_cast(u16x2, r[0]), __builtin_bit_cast(u16x2, r[1]));
-  u = __builtin_bit_cast(uint32_t, x);
+  u = max(r[0], r[1]);
   r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  x = __builtin_elementwise_max(__builtin_bit_cast(u16x2, r[0]), __builtin_bit_cast(u16x2, r[1]));
-  return __builtin_bit_cast(uint32_t, x);
+  return max(r[0], r[1]);
 }
 
 // The same for non-negative fp32 scales: the largest as fp32 bits in every lane.
@@ -1011,6 +1023,29 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     for (int nt = 0; nt < NT; ++nt) over |= mloc[nt] > m[nt] + kLazy;  // m = -inf: any visible key
     const bool wave_over = __any(over);
     if (!wave_over) write_weights();  // a wave that is over rewrites below anyway
+    if constexpr (F16PAIR) {
+      // this wave's V-scale exponent: lowered (and o rescaled) if the page's scales ask for
+      // it, then applied to the scales the products use; done while the other waves still
+      // write their weights, so the chain stays off the path after the barrier
+      if (valid) {
+        if (!full) zero_unwritten_scales(pr, p);
+        float f;
+        if (lower_vexp(pr, f)) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int j = 0; j < DPW; ++j) o[nt][j] *= f;
+        }
+        const f16x2 e2 = __builtin_bit_cast(f16x2, f16x2_pow2(vexp));
+#pragma unroll
+        for (int j = 0; j < PageRegs<D, FMT>::VSN; ++j) {
+          pr.vs[j].x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, pr.vs[j].x) * e2);
+          pr.vs[j].y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, pr.vs[j].y) * e2);
+          pr.vs[j].z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, pr.vs[j].z) * e2);
+          pr.vs[j].w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, pr.vs[j].w) * e2);
+        }
+      }
+    }
     if (lane == 0) lds_over[buf][(tid >> 6)] = wave_over ? 1 : 0;
     __syncthreads();
     int any_over = 0;
@@ -1042,28 +1077,6 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
           const int r = (tid >> 6) + k * NW;
           if (r < n_rows && blk_r[k] >= 0 && blk_r[k] < a.num_blocks)
             store_row<FMT, D>(aa, xr[k], kvh, r & 1, static_cast<long>(L) - a.T + t_lo + (r >> 1), blk_r[k], lane);
-        }
-      }
-    }
-    if constexpr (F16PAIR) {
-      // this wave's V-scale exponent: lowered (and o rescaled) if the page's scales ask for
-      // it, then applied to the scales the products use
-      if (valid) {
-        if (!full) zero_unwritten_scales(pr, p);
-        float f;
-        if (lower_vexp(pr, f)) {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int j = 0; j < DPW; ++j) o[nt][j] *= f;
-        }
-        const f16x2 e2 = __builtin_bit_cast(f16x2, f16x2_pow2(vexp));
-#pragma unroll
-        for (int j = 0; j < PageRegs<D, FMT>::VSN; ++j) {
-          pr.vs[j].x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, pr.vs[j].x) * e2);
-          pr.vs[j].y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, pr.vs[j].y) * e2);
-          pr.vs[j].z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, pr.vs[j].z) * e2);
-          pr.vs[j].w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, pr.vs[j].w) * e2);
         }
       }
     }

@@ -1,4 +1,5 @@
-"""Parity on softmaxes with attention sinks, in every chunking mode.
+"""Parity where the P.V operands span a wide dynamic range: attention sinks, and value
+rows of widely different magnitudes, in every chunking mode.
 
 A few keys lie 13-16 nats above thousands of near-uniform keys whose values have
 a nonzero mean (kvq_synth.make_sink).  The near-uniform keys' weights are tiny
@@ -119,3 +120,39 @@ def test_sink_prefill_one_chunk(K, fmt, T, src):
     shp = S.tiny_shape(B=1, T=T, Hq=24, Hkv=4, D=256, lens=(65536,), src=src, fmt=FMTS[fmt])
     w = S.make_sink(shp, gap_nats=13.0, stride=16384, seed=5)
     check(K, w, rows_every_t(w, 2, ts=(0, T // 2, T - 1)), prefill=True, label=f"prefill T={T} {fmt} src={src}")
+
+
+# Value rows whose magnitudes span 2^-6 .. 2^6: the largest V scale of a page sits on any
+# slot, so an exponent taken from part of the page's scales would overflow the products.
+WIDE = {
+    "int8_t4": S.tiny_shape(B=1, T=4, Hq=24, Hkv=4, D=256, lens=(20000,), src=S.SRC_BF16),
+    "int8_t1_d128_f32": S.tiny_shape(B=2, T=1, Hq=8, Hkv=2, D=128, lens=(9000, 3000), src=S.SRC_F32),
+    "fp8_t4": S.tiny_shape(B=1, T=4, Hq=24, Hkv=4, D=256, lens=(20000,), src=S.SRC_BF16, fmt=S.FMT_FP8_ROW),
+    "rk8v4_t4": S.tiny_shape(B=1, T=4, Hq=24, Hkv=4, D=256, lens=(20000,), src=S.SRC_BF16, fmt=S.FMT_RK8V4),
+    "rk4v4_t1": S.tiny_shape(B=1, T=1, Hq=24, Hkv=4, D=256, lens=(20000,), src=S.SRC_BF16, fmt=S.FMT_RK4V4),
+    "bf16_t4": S.tiny_shape(B=1, T=4, Hq=24, Hkv=4, D=256, lens=(20000,), src=S.SRC_BF16, fmt=S.FMT_BF16),
+}
+
+
+@pytest.mark.parametrize("name", list(WIDE))
+def test_wide_value_rows(K, name):
+    w = S.make_wide(WIDE[name], span_log2=6.0, seed=list(WIDE).index(name))
+    check(K, w, rows_every_t(w, 4), chunk=4096, label=f"wide V rows {name}")
+
+
+@pytest.mark.parametrize("fmt,src", [("int8", S.SRC_BF16), ("fp8", S.SRC_BF16), ("int8", S.SRC_F32)])
+def test_wide_value_rows_prefill(K, fmt, src):
+    shp = S.tiny_shape(B=1, T=300, Hq=24, Hkv=4, D=256, lens=(6000,), src=src, fmt=FMTS[fmt])
+    w = S.make_wide(shp, span_log2=6.0, seed=7)
+    check(K, w, rows_every_t(w, 2, ts=(0, 150, 299)), chunk=4096, prefill=True, label=f"wide V rows prefill {fmt}")
+
+
+@pytest.mark.parametrize("run", [0, 1, 2, 3])
+@pytest.mark.parametrize("fmt", ["int8", "fp8", "rk8v4"])
+def test_striped_value_rows(K, fmt, run):
+    # every 16-slot run of a page holds the same four rows at 2^-6 and twelve at 2^6, so the
+    # four 16-lane groups of a wave see different largest V scales: the exponent must come
+    # from all of them, or the large rows' products overflow f16
+    shp = S.tiny_shape(B=1, T=4, Hq=24, Hkv=4, D=256, lens=(8192,), src=S.SRC_BF16, fmt=FMTS[fmt])
+    w = S.make_wide(shp, span_log2=6.0, seed=20 + run, small_run=run)
+    check(K, w, rows_every_t(w, 3), chunk=4096, label=f"striped V rows {fmt} small run {run}")

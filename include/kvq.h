@@ -188,6 +188,10 @@ size_t paged_decode_attn_workspace_bytes(int32_t num_seqs, int32_t T, int32_t nu
  *              initialization needed; calls that share a workspace must be
  *              ordered on one stream.
  * Accuracy: K/V codes enter the matrix cores exactly (converted to f16); each
+ * query row enters scaled by a power of two that puts its largest element in
+ * [2^14, 2^15) (its scores take the power of two back), so a bf16 row whose
+ * elements lie within 2^28 of its largest is exact in f16 at any magnitude (an
+ * fp32 row enters as an f16 hi+lo pair); each
  * softmax weight times its V scale enters as an f16 hi+lo pair, kept inside
  * f16's normal range by two powers of two (one folded into the weights and the
  * row sums, one per wave set from the largest V scale it has seen and taken out

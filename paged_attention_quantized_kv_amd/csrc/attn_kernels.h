@@ -275,6 +275,17 @@ __device__ inline int scale_exponent_f32(uint32_t fbits) {
   return max(min(133 - e, kFp8ExpMax), kFp8ExpMin);
 }
 
+// Query rows enter the matrix cores as f16, whose range (2^-24 .. 65504) is far narrower than
+// bf16's or fp32's.  Each row is scaled by 2^-s before the conversion, s chosen from its
+// largest |element| (fp32 bits mbits) so that the largest lands in [2^14, 2^15); the row's
+// scores take 2^s back.  A bf16 row whose elements all lie within 2^28 of its largest thus
+// enters exactly (and an fp32 row as its hi + lo pair); smaller elements, whose products
+// are below 2^-28 of the largest one's, keep 2^-24 of it absolute.  An all-zero row takes s = 0.
+__device__ inline int q_row_exp(uint32_t mbits) {
+  if (mbits == 0) return 0;
+  return max(min(static_cast<int>((mbits >> 23) & 0xFFu) - 127 - 14, 100), -100);
+}
+
 // 2^E as two packed f16 (E in [kVexpMin, kVexpMax]; 2^-15 and 2^-16 are subnormal).
 __device__ inline uint32_t f16x2_pow2(int E) {
   const uint32_t h = (E >= -14) ? static_cast<uint32_t>(E + 15) << 10 : (0x400u >> (-14 - E));
@@ -428,6 +439,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   __shared__ float lds_m[NTEAM][ROWS];
   constexpr int MAXPG = (APP == 2) ? kMaxPrefillChunkPages : kMaxChunkPages;
   __shared__ int32_t lds_pg[MAXPG];  // pool page (block * Hkv + kvh) of each page of the chunk
+  __shared__ uint32_t lds_qmax[ROWS];  // per query row: the largest |element| (fp32 bits)
   float *pbuf = reinterpret_cast<float *>(pbuf4);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = (tid >> 6) & 3, team = tid >> 8;
@@ -466,6 +478,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     bad |= !ok;
     lds_pg[i] = (ok ? blk : 0) * a.num_kv_heads + kvh;
   }
+  if (tid < ROWS) lds_qmax[tid] = 0u;
   bad = __syncthreads_or(bad ? 1 : 0) != 0;
 
   const int n_it = (page1 - page0 + NTEAM - 1) / NTEAM;
@@ -522,55 +535,88 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 
   // ---- queries -> LDS in B-operand order: entry (nt, cg, hk, hl, lane) holds dims
   // 64cg + 16(lane/16) + 8hk + 0..7 of row 16nt + lane%16, as f16 hi (hl=0) or lo (hl=1).
+  // Two passes: the largest |element| of every row (LDS max), then the rows scaled by
+  // 2^-q_row_exp into f16 (the BF16 pool takes bf16 operands and needs no scaling).
   if constexpr (FMT == 2 || FMT == 3) {
     // rk8v4, rk4v4: the keys are stored rotated by H64/8 per 64-dim group, so each 64-dim group
     // of a query row is rotated by the same matrix (butterflies in fp32, one thread per
     // (row, group)) before it is split into f16 hi + lo
-    for (int task = tid; task < ROWS * G64; task += 256 * NTEAM) {
-      const int rl = task / G64, cg = task % G64, r = row0 + rl;
-      float v[64];
-      if (r < R) {
-        const int t = r / a.group, hq = kvh * a.group + r % a.group;
-        const size_t qb = ((static_cast<size_t>(b) * a.T + t) * a.num_q_heads + hq) * D + 64 * cg;
+    static_assert(ROWS * G64 <= 256 * NTEAM, "one rotation task per thread");
+    const int rl = tid / G64, cg = tid % G64, r = row0 + rl;
+    const bool live = tid < ROWS * G64;
+    float v[64];
+    if (live && r < R) {
+      const int t = r / a.group, hq = kvh * a.group + r % a.group;
+      const size_t qb = ((static_cast<size_t>(b) * a.T + t) * a.num_q_heads + hq) * D + 64 * cg;
 #pragma unroll
-        for (int i = 0; i < 64; ++i) v[i] = load_q<QLO != 1>(a.q, qb + i);
-      } else {
+      for (int i = 0; i < 64; ++i) v[i] = load_q<QLO != 1>(a.q, qb + i);
+    } else {
 #pragma unroll
-        for (int i = 0; i < 64; ++i) v[i] = 0.0f;
-      }
+      for (int i = 0; i < 64; ++i) v[i] = 0.0f;
+    }
 #pragma unroll
-      for (int hh = 1; hh < 64; hh <<= 1)
+    for (int hh = 1; hh < 64; hh <<= 1)
 #pragma unroll
-        for (int i = 0; i < 64; ++i)
-          if ((i & hh) == 0) {
-            const float u = v[i], w = v[i + hh];
-            v[i] = u + w;
-            v[i + hh] = u - w;
-          }
+      for (int i = 0; i < 64; ++i)
+        if ((i & hh) == 0) {
+          const float u = v[i], w = v[i + hh];
+          v[i] = u + w;
+          v[i + hh] = u - w;
+        }
+    uint32_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) mx = max(mx, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+    if (live) atomicMax(&lds_qmax[rl], mx);
+    __syncthreads();
+    if (live) {
+      // the rotation's 1/8 and the row's 2^-s in one power of two
+      const float f = __builtin_ldexpf(0.125f, -q_row_exp(__float_as_uint(__uint_as_float(lds_qmax[rl]) * 0.125f)));
 #pragma unroll
       for (int jh = 0; jh < 8; ++jh) {  // dims 8jh .. 8jh+7 of the group: lane 16(jh/2) + rl%16, hk = jh%2
         f16x2 hi[4], lo[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) split_f16(v[8 * jh + 2 * j] * 0.125f, v[8 * jh + 2 * j + 1] * 0.125f, hi[j], lo[j]);
+        for (int j = 0; j < 4; ++j) split_f16(v[8 * jh + 2 * j] * f, v[8 * jh + 2 * j + 1] * f, hi[j], lo[j]);
         const int idx = (((rl / 16) * G64 + cg) * 2 + (jh & 1)) * QP * 64 + 16 * (jh >> 1) + (rl % 16);
         qs[idx] = __builtin_bit_cast(uint4, f16x8{hi[0][0], hi[0][1], hi[1][0], hi[1][1], hi[2][0], hi[2][1], hi[3][0], hi[3][1]});
         qs[idx + 64] = __builtin_bit_cast(uint4, f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]});
       }
     }
-  }
-  for (int e = tid; e < ((FMT == 2 || FMT == 3) ? 0 : NT * G64 * 2 * 64); e += 256 * NTEAM) {
-    const int ln = e & 63, hk = (e >> 6) & 1, cg = (e >> 7) % G64, nt = (e >> 7) / G64;
-    const int r = row0 + 16 * nt + (ln & 15);
-    const int d0 = 64 * cg + 16 * (ln >> 4) + 8 * hk;
-    f16x2 hi[4], lo[4];
-    if (r < R) {
-      const int t = r / a.group, hq = kvh * a.group + r % a.group;
-      const size_t qb = ((static_cast<size_t>(b) * a.T + t) * a.num_q_heads + hq) * D + d0;
+  } else {
+    constexpr int QN = NT * G64 * 2 * 64, QIT = (QN + 256 * NTEAM - 1) / (256 * NTEAM);
+    float xq[QIT][8];
+#pragma unroll
+    for (int k = 0; k < QIT; ++k) {
+      const int e = tid + k * 256 * NTEAM;
+      const int ln = e & 63, hk = (e >> 6) & 1, cg = (e >> 7) % G64, nt = (e >> 7) / G64;
+      const int r = row0 + 16 * nt + (ln & 15);
+      const int d0 = 64 * cg + 16 * (ln >> 4) + 8 * hk;
+      uint32_t mx = 0;
+      if (e < QN && r < R) {
+        const int t = r / a.group, hq = kvh * a.group + r % a.group;
+        const size_t qb = ((static_cast<size_t>(b) * a.T + t) * a.num_q_heads + hq) * D + d0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          xq[k][j] = load_q<QLO != 1>(a.q, qb + j);
+          mx = max(mx, __float_as_uint(xq[k][j]) & 0x7FFFFFFFu);
+        }
+        if constexpr (FMT != 4) atomicMax(&lds_qmax[16 * nt + (ln & 15)], mx);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xq[k][j] = 0.0f;
+      }
+    }
+    if constexpr (FMT != 4) __syncthreads();
+#pragma unroll
+    for (int k = 0; k < QIT; ++k) {
+      const int e = tid + k * 256 * NTEAM;
+      if (e >= QN) continue;
+      const int ln = e & 63, hk = (e >> 6) & 1, cg = (e >> 7) % G64, nt = (e >> 7) / G64;
+      const float f = (FMT == 4) ? 1.0f : __builtin_ldexpf(1.0f, -q_row_exp(lds_qmax[16 * nt + (ln & 15)]));
+      f16x2 hi[4], lo[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        // QLO = 1 for fp32 queries (hi + lo), 2 for rotated bf16 queries (hi + lo), 0 for
-        // bf16 queries (one exact f16)
-        const float x0 = load_q<QLO != 1>(a.q, qb + 2 * j), x1 = load_q<QLO != 1>(a.q, qb + 2 * j + 1);
+        // QLO = 1 for fp32 queries (hi + lo), 0 for bf16 queries (one f16, exact once scaled)
+        const float x0 = xq[k][2 * j] * f, x1 = xq[k][2 * j + 1] * f;
         if constexpr (FMT == 4) {
           // BF16 pool: bf16 operands; a bf16 query is exact, an fp32 one is bf16 hi (cut)
           // + lo (the exact residual rounded)
@@ -581,18 +627,15 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
         } else if constexpr (QLO) {
           split_f16(x0, x1, hi[j], lo[j]);
         } else {
-          hi[j] = f16x2{static_cast<_Float16>(x0), static_cast<_Float16>(x1)};  // RNE; exact for bf16 in range
+          hi[j] = f16x2{static_cast<_Float16>(x0), static_cast<_Float16>(x1)};
           lo[j] = f16x2{0, 0};
         }
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) hi[j] = lo[j] = f16x2{0, 0};
+      const int idx = ((nt * G64 + cg) * 2 + hk) * QP * 64 + ln;
+      qs[idx] = __builtin_bit_cast(uint4, f16x8{hi[0][0], hi[0][1], hi[1][0], hi[1][1], hi[2][0], hi[2][1], hi[3][0], hi[3][1]});
+      if constexpr (QLO)
+        qs[idx + 64] = __builtin_bit_cast(uint4, f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]});
     }
-    const int idx = ((nt * G64 + cg) * 2 + hk) * QP * 64 + ln;
-    qs[idx] = __builtin_bit_cast(uint4, f16x8{hi[0][0], hi[0][1], hi[1][0], hi[1][1], hi[2][0], hi[2][1], hi[3][0], hi[3][1]});
-    if constexpr (QLO)
-      qs[idx + 64] = __builtin_bit_cast(uint4, f16x8{lo[0][0], lo[0][1], lo[1][0], lo[1][1], lo[2][0], lo[2][1], lo[3][0], lo[3][1]});
   }
   if constexpr (APP == 1) {
     if (!defer) {
@@ -613,7 +656,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   if (!early && n_it > 0) load_page<D, FMT>(rA, a, page_of(0), wave, lane, q4);
 
   // ---- per-lane state; this lane's query row is 16nt + c16
-  float m[NT], lsum[NT];
+  float m[NT], lsum[NT], qsc[NT];
   int last[NT];
   f32x4 o[NT][DPW];
   // exponent offsets of the P·V operands (see kWeightExp): fp16-scale formats carry kWeightExp
@@ -679,6 +722,9 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     lsum[nt] = 0.0f;
     const int r = row0 + 16 * nt + c16;
     last[nt] = (r < R) ? (L - a.T + r / a.group) : -1;  // -1: padding row, sees nothing
+    // the row's scores take back the 2^-s its query was scaled by (none for the BF16 pool)
+    qsc[nt] = (FMT == 4) ? a.qk_scale_log2 : __builtin_ldexpf(a.qk_scale_log2, q_row_exp(
+        (FMT == 2 || FMT == 3) ? __float_as_uint(__uint_as_float(lds_qmax[16 * nt + c16]) * 0.125f) : lds_qmax[16 * nt + c16]));
 #pragma unroll
     for (int j = 0; j < DPW; ++j) o[nt][j] = f32x4{0, 0, 0, 0};
   }
@@ -771,7 +817,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float v = z[nt][i] * a.qk_scale_log2;
+        float v = z[nt][i] * qsc[nt];
         if constexpr (MASKED) v = (key0 + i <= last[nt]) ? v : -INFINITY;
         z[nt][i] = v;
         mx = fmaxf(mx, v);
@@ -1431,24 +1477,42 @@ __global__ __launch_bounds__(64 * 8 / KVQ_PREFILL_NTW, 1) void prefill_kernel(At
   };
   if (npg > 0) gload(0);
 
-  // ---- this wave's queries (bf16, exact in f16) -> registers: B operand of dim block kb
+  // ---- this wave's queries (bf16) -> registers: B operand of dim block kb.  Each row is
+  // scaled by 2^-q_row_exp of its largest |element| (the four lane groups of a row share
+  // it), which makes it exact in f16; the row's scores take the power of two back (qsc).
   f16x8 qf[NTW][KB];
   int last[NTW];
+  float qsc[NTW];
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     const int r = row0 + 16 * NTW * wave + 16 * nt + c16;
     last[nt] = (r < R) ? (L - a.T + r / a.group) : -1;  // -1: padding row, sees nothing
     const size_t qb = ((static_cast<size_t>(b) * a.T + r / a.group) * a.num_q_heads + kvh * a.group + r % a.group) * D;
+    uint4 u[KB];
+    uint32_t mx = 0;  // largest |element| of the row, bf16 bits
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (r < R) u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + qb + 32 * kb + 8 * q4);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      u[kb] = make_uint4(0, 0, 0, 0);
+      if (r < R) u[kb] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + qb + 32 * kb + 8 * q4);
+      const uint32_t w[4] = {u[kb].x, u[kb].y, u[kb].z, u[kb].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = max(mx, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+    }
+    auto sw = __builtin_amdgcn_permlane16_swap(mx, mx, false, false);
+    mx = max(sw[0], sw[1]);
+    sw = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
+    mx = max(sw[0], sw[1]);
+    const int qe = q_row_exp(mx << 16);
+    const float f = __builtin_ldexpf(1.0f, -qe);
+    qsc[nt] = __builtin_ldexpf(a.qk_scale_log2, qe);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const uint32_t w[4] = {u[kb].x, u[kb].y, u[kb].z, u[kb].w};
       f16x2 h[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        h[j] = f16x2{static_cast<_Float16>(__uint_as_float(w[j] << 16)),
-                     static_cast<_Float16>(__uint_as_float(w[j] & 0xFFFF0000u))};
+        h[j] = f16x2{static_cast<_Float16>(__uint_as_float(w[j] << 16) * f),
+                     static_cast<_Float16>(__uint_as_float(w[j] & 0xFFFF0000u) * f)};
       qf[nt][kb] = f16x8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
     }
   }
@@ -1559,7 +1623,7 @@ __global__ __launch_bounds__(64 * 8 / KVQ_PREFILL_NTW, 1) void prefill_kernel(At
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = z[kt][nt][i] * a.qk_scale_log2;
+          float v = z[kt][nt][i] * qsc[nt];
           if (!full) v = (p * kPage + 16 * kt + 4 * q4 + i <= last[nt]) ? v : -INFINITY;
           z[kt][nt][i] = v;
           mx = fmaxf(mx, v);

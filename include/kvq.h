@@ -187,6 +187,10 @@ size_t paged_decode_attn_workspace_bytes(int32_t num_seqs, int32_t T, int32_t nu
  *   workspace  >= paged_decode_attn_workspace_bytes(...) bytes, no
  *              initialization needed; calls that share a workspace must be
  *              ordered on one stream.
+ * The context of each (sequence, KV head) is cut into chunks attended in
+ * parallel and merged with log-sum-exp weights; when one chunk per (sequence,
+ * KV head) already fills the chip (paged_decode_attn_num_splits() == 1), the
+ * chunks write their normalized rows and no merge runs.
  * Accuracy: K/V codes enter the matrix cores exactly (converted to f16); each
  * query row enters scaled by a power of two that puts its largest element in
  * [2^14, 2^15) (its scores take the power of two back), so a bf16 row whose

@@ -448,14 +448,12 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   const int row0 = (blockIdx.y / a.num_kv_heads) * ROWS;  // first query row (t*G + g) of this block
   const int L = a.seq_lens[b];
   if (L < a.T || L > a.max_seq_len || L > a.max_blocks * kPage) {  // the merge writes NaN rows
-    if constexpr (APP == 2) {
-      if (a.direct_out != 0 && split == 0) {  // no merge: write them here
-        for (int e = threadIdx.x; e < ROWS * D; e += blockDim.x) {
-          const int r = row0 + e / D;
-          if (r < a.rows)
-            a.out[((static_cast<size_t>(b) * a.T + r / a.group) * a.num_q_heads + kvh * a.group + r % a.group) * D +
-                  e % D] = NAN;
-        }
+    if (a.direct_out != 0 && split == 0) {  // no merge: write them here
+      for (int e = threadIdx.x; e < ROWS * D; e += blockDim.x) {
+        const int r = row0 + e / D;
+        if (r < a.rows)
+          a.out[((static_cast<size_t>(b) * a.T + r / a.group) * a.num_q_heads + kvh * a.group + r % a.group) * D +
+                e % D] = NAN;
       }
     }
     return;
@@ -1209,8 +1207,8 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     for (int nt = 0; nt < NT; ++nt) {
       const int rl = 16 * nt + c16, r = row0 + rl;
       if (r < R) {
-        // prefill with one chunk: the normalized row goes to out[b][t][h] (t*G + g = r)
-        const bool direct = (APP == 2) && (a.direct_out != 0);
+        // one chunk per row block: the normalized row goes to out[b][t][h] (t*G + g = r)
+        const bool direct = a.direct_out != 0;
         const size_t orow = ((static_cast<size_t>(b) * a.T + r / a.group) * a.num_q_heads + kvh * a.group +
                              r % a.group) * D;
 #pragma unroll

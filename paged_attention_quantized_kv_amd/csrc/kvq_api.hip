@@ -156,14 +156,16 @@ int attn_call(Phase phase, const kvq_cache_t *cache, const void *q, int32_t q_dt
   a.tokens_per_split = s.tokens_per_split;
   a.n_splits = s.n_splits;
   a.row_blocks = 1;
-  a.direct_out = 0;
+  // one call with one chunk per (sequence, KV head): the split kernel writes the normalized
+  // rows itself and no merge runs (the two phases called apart keep the partials)
+  a.direct_out = (phase == Phase::kBoth && s.n_splits == 1) ? 1 : 0;
   a.qk_scale_log2 = softmax_scale * 1.4426950408889634f;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (phase != Phase::kMerge) {
     if (kvq::launch_attn_split(cache->format, cache->head_dim, q_dtype, a, st) != hipSuccess) return KVQ_ERR_LAUNCH;
   }
-  if (phase != Phase::kSplit) {
+  if (phase != Phase::kSplit && a.direct_out == 0) {
     if (kvq::launch_attn_merge(cache->head_dim, a, st) != hipSuccess) return KVQ_ERR_LAUNCH;
   }
   return KVQ_OK;

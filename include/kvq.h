@@ -248,6 +248,25 @@ int paged_decode_step(const kvq_cache_t *cache, const void *k_new, const void *v
                       float *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * paged_decode_attn_noalloc -- paged_decode_attn for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, whose place takes a fixed device
+ * array inside the library (paged_decode_attn_noalloc_max_bytes() bytes, 16 MiB; each GPU
+ * the library runs on holds its own copy until the process ends).  Nothing is allocated.
+ * Same kernels and results as paged_decode_attn.  Returns KVQ_ERR_WORKSPACE when the
+ * shape's workspace (paged_decode_attn_workspace_bytes) exceeds the array, e.g. 128K-token
+ * T=4 calls of one sequence with 24 query / 4 KV heads need ~6.3 MB; KVQ_ERR_LAUNCH if the
+ * array's device address cannot be obtained.  All calls on one GPU share the array: calls
+ * that may overlap on one GPU (different streams, threads without ordering) race and must
+ * not be issued; calls ordered on one stream are safe.
+ */
+int paged_decode_attn_noalloc(const kvq_cache_t *cache, const void *q, int32_t q_dtype, int32_t num_seqs,
+                              int32_t T, int32_t num_q_heads, const int32_t *block_table,
+                              int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t max_seq_len,
+                              float softmax_scale, float *out, void *stream);
+size_t paged_decode_attn_noalloc_max_bytes(void);
+
+/*
  * paged_prefill_attn -- the same attention for a prefill chunk: T query rows per sequence
  * with any T (1 <= T <= max_seq_len; T * (num_q_heads / num_kv_heads) rows per KV head),
  * causal among themselves exactly as in paged_decode_attn (row t sees keys 0 ..

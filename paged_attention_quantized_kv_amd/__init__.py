@@ -27,7 +27,8 @@ PAGE = 64
 
 _EXPORTS = ("kv_append_quant", "paged_decode_attn", "paged_decode_attn_split", "paged_decode_attn_merge",
             "paged_decode_step", "paged_decode_attn_workspace_bytes", "paged_decode_attn_num_splits",
-            "paged_prefill_attn", "paged_prefill_attn_workspace_bytes", "kvq_check_tables", "kvq_status_string")
+            "paged_prefill_attn", "paged_prefill_attn_workspace_bytes", "kvq_check_tables", "kvq_status_string",
+            "paged_decode_attn_noalloc", "paged_decode_attn_noalloc_max_bytes")
 
 
 class KvqError(RuntimeError):
@@ -55,6 +56,10 @@ def _load():
     for name in ("paged_decode_attn", "paged_decode_attn_split", "paged_decode_attn_merge", "paged_prefill_attn"):
         getattr(L, name).argtypes = attn
         getattr(L, name).restype = C.c_int
+    L.paged_decode_attn_noalloc.argtypes = attn[:12] + [vp]
+    L.paged_decode_attn_noalloc.restype = C.c_int
+    L.paged_decode_attn_noalloc_max_bytes.argtypes = []
+    L.paged_decode_attn_noalloc_max_bytes.restype = C.c_size_t
     L.paged_decode_step.argtypes = [P, vp, vp, vp, i32, i32, i32, i32, vp, i32, vp, i32, C.c_float, vp, vp,
                                     C.c_size_t, vp]
     L.paged_decode_step.restype = C.c_int
@@ -220,6 +225,21 @@ def paged_decode_attn(cache, q, block_table, seq_lens, max_seq_len, softmax_scal
     """out[B, T, Hq, D] (fp32) = softmax(q k^T * softmax_scale) v over the paged cache."""
     return _attn(lib.paged_decode_attn, cache, q, block_table, seq_lens, max_seq_len, softmax_scale, out, workspace,
                  stream)
+
+
+def paged_decode_attn_noalloc(cache, q, block_table, seq_lens, max_seq_len, softmax_scale, out, stream=None):
+    """paged_decode_attn without a workspace: the library's fixed device array takes its place
+    (nothing is allocated; calls that overlap on one GPU race)."""
+    _check_attn(cache, q, block_table, seq_lens, out, out)
+    B, T, Hq = q.shape[0], q.shape[1], q.shape[2]
+    _check(lib.paged_decode_attn_noalloc(cache.desc, _ptr(q), _dtype_code(q), B, T, Hq, _ptr(block_table),
+                                         block_table.shape[1], _ptr(seq_lens), int(max_seq_len), float(softmax_scale),
+                                         _ptr(out), _stream(stream)))
+    return out
+
+
+def noalloc_max_bytes() -> int:
+    return int(lib.paged_decode_attn_noalloc_max_bytes())
 
 
 def paged_decode_attn_split(cache, q, block_table, seq_lens, max_seq_len, softmax_scale, out, workspace, stream=None):

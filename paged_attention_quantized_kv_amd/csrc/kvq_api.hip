@@ -7,6 +7,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "internal.h"
 
@@ -171,9 +172,53 @@ int attn_call(Phase phase, const kvq_cache_t *cache, const void *q, int32_t q_dt
   return KVQ_OK;
 }
 
+// ---- Scratch of paged_decode_attn_noalloc: a fixed device array instead of a caller's
+// workspace.  Every GPU the library runs on holds its own copy until the process ends.  In
+// host code `scratch` names a host-side stand-in, so its device address is looked up once
+// per device (hipGetSymbolAddress, with that device current) and only that address is used.
+constexpr size_t kScratchBytes = 16u << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+
+// The scratch address on the current device, or null if it cannot be had.
+void *scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t paged_decode_attn_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int paged_decode_attn_noalloc(const kvq_cache_t *cache, const void *q, int32_t q_dtype, int32_t num_seqs, int32_t T,
+                              int32_t num_q_heads, const int32_t *block_table, int32_t max_blocks_per_seq,
+                              const int32_t *seq_lens, int32_t max_seq_len, float softmax_scale, float *out,
+                              void *stream) {
+  if (cache == nullptr) return KVQ_ERR_INVALID_ARG;
+  // shapes whose partials exceed the scratch are refused before anything else
+  {
+    const size_t need = paged_decode_attn_workspace_bytes(num_seqs, T, num_q_heads, cache->num_kv_heads,
+                                                          cache->head_dim, max_seq_len);
+    if (need > kScratchBytes) return KVQ_ERR_WORKSPACE;
+  }
+  void *ws = scratch_ptr();
+  if (ws == nullptr) return KVQ_ERR_LAUNCH;
+  return attn_call(Phase::kBoth, cache, q, q_dtype, num_seqs, T, num_q_heads, block_table, max_blocks_per_seq,
+                   seq_lens, max_seq_len, softmax_scale, out, ws, kScratchBytes, stream);
+}
+
 
 const char *kvq_status_string(int status) {
   switch (status) {

@@ -177,3 +177,22 @@ def test_bf16_pool_needs_no_scales(K):
     assert _attn(K, d) == -5  # valid: reaches the runtime, which has no device here
     d = K.CacheDesc(0, 16, 64, 4, 256, 0, 0x1000, 0x2000, 0, 0)
     assert _attn(K, d) == -1  # the INT8 pool does
+
+
+def test_noalloc_validation(K):
+    """The allocation-free call: its scratch size is fixed, shapes whose workspace exceeds it
+    are refused with KVQ_ERR_WORKSPACE before the device is touched, a null cache is invalid,
+    and a valid call with no GPU reaches the runtime (KVQ_ERR_LAUNCH)."""
+    cap = K.noalloc_max_bytes()
+    assert cap == 16 << 20
+    f = K.lib.paged_decode_attn_noalloc
+
+    def call(d, B=1, T=4, Hq=24, L=131072):
+        return f(C.byref(d) if d is not None else None, C.c_void_p(0x5000), 1, B, T, Hq, C.c_void_p(0x7000),
+                 (L + 63) // 64, C.c_void_p(0x8000), L, 0.0625, C.c_void_p(0x9000), None)
+    d = _desc(K)
+    assert K.workspace_bytes(1, 4, 24, 4, 256, 131072) <= cap  # the headline shape fits
+    big = next(L for L in (1 << 20, 1 << 21, 1 << 22) if K.workspace_bytes(8, 4, 32, 4, 256, L) > cap)
+    assert call(d, B=8, T=4, Hq=32, L=big) == -3
+    assert call(None) == -1
+    assert call(d) == -5  # valid shape, no device here

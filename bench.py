@@ -19,6 +19,7 @@ Prints ONE JSON line.  --gpus N > 1 exits: the library runs on one GPU (multi-GP
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -88,7 +89,7 @@ class Run:
 
     def __init__(self, K, S, H, torch, name, device):
         self.K, self.S, self.H, self.torch = K, S, H, torch
-        self.name, self.dev = name, device
+        self.name, self.dev = (name if isinstance(name, str) else name.name), device
         w = S.make(name)
         self.w = w
         s = w.shape
@@ -157,9 +158,10 @@ class Run:
         self.g_all = self._graph(self.step, allc)
         self.g_all_two = self._graph(self.step_two_calls, allc)
         self.g_split = self._graph(lambda i: self.K.paged_decode_attn_split(*self.attn_args(i)), allc)
+        self.g_attn = self._graph(lambda i: self.K.paged_decode_attn(*self.attn_args(i)), allc)
         # the first replay of a graph also uploads it to the device: do that for every graph
         # here, so no timed region pays it
-        for g in self.g_one + [self.g_all, self.g_all_two, self.g_split]:
+        for g in self.g_one + [self.g_all, self.g_all_two, self.g_split, self.g_attn]:
             g.replay()
         torch.cuda.synchronize()
 
@@ -232,7 +234,26 @@ class Run:
         # the split kernel alone: events on the replay stream around back-to-back launches
         split_ms = self._events(self.g_split, reps, self.n_copies)
         two_ms = self._events(self.g_all_two, reps, self.n_copies)
+        # the whole paged_decode_attn call (split + merge), no append
+        self.attn_ms = self._events(self.g_attn, reps, self.n_copies)
+        # the distribution: each step timed alone (events around one replay of one step)
+        self.step_pct_us = self.step_percentiles(steps)
         return gpu_ms / steps, split_ms, two_ms
+
+    def step_percentiles(self, steps):
+        """p10 / p50 / p90 of the steps of a back-to-back run: an event between every two
+        consecutive one-step graph replays, all enqueued before one synchronization."""
+        torch = self.torch
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(steps):
+            self.g_one[i % self.n_copies].replay()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        t = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps))
+        q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
+        return {"p10": round(q(0.1), 2), "p50": round(q(0.5), 2), "p90": round(q(0.9), 2)}
 
     def measure_chunk_append(self, reps=20):
         """kv_append_quant of the last prefill chunk (rewriting the same rows with the same
@@ -299,9 +320,14 @@ class Run:
 
 
 def cpu_baseline(S, H, name, rows_target_s=12.0):
-    """The oracle as it stands, single-threaded, on a bounded sample: a few query rows
-    of the same workload (each row re-reads its KV head's whole context, as the
-    oracle does for every row), scaled to the whole call."""
+    """The oracle as it stands (plain C, fp64) on the same workload, two ways:
+    - one thread on a bounded sample of query rows (each row re-reads its KV head's whole
+      context, as the oracle does for every row), scaled to the whole call;
+    - every query row of the call over all host cores, one oracle call per row on a pool
+      of threads (the oracle releases the interpreter while it runs), timed whole.
+    Returns the all-cores figure with the one-thread figure beside it."""
+    import concurrent.futures as cf
+
     import numpy as np
     import oracle as O
 
@@ -309,22 +335,95 @@ def cpu_baseline(S, H, name, rows_target_s=12.0):
     s = w.shape
     pool = H.oracle_pool(O, w)
     total_rows = s.B * s.T * s.Hq
-    rows = []
-    t_sum = 0.0
-    for r in range(total_rows):
-        t0 = time.perf_counter()
+
+    def one(r):
         pool.paged_attn(w.q, s.src, s.T, s.Hq, w.block_table, w.seq_lens, w.softmax_scale,
                         rows=np.array([r], np.int32))
+
+    t_sum, n1 = 0.0, 0
+    for r in range(total_rows):  # one thread (also builds any lazily made tables first)
+        t0 = time.perf_counter()
+        one(r)
         t_sum += time.perf_counter() - t0
-        rows.append(r)
+        n1 += 1
         if t_sum >= rows_target_s:
             break
-    per_row = t_sum / len(rows)
-    call_s = per_row * total_rows
-    return {"value": round(w.kv_bytes() / call_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(rows)} of {total_rows} query rows of {name} (fp64 oracle, {per_row:.2f} s/row), "
-                      f"scaled to the whole call ({call_s:.1f} s)",
-            "tok_per_s": round(s.B * s.T / call_s, 4)}
+    call_1 = t_sum / n1 * total_rows
+    cores = min(os.cpu_count() or 1, total_rows)
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(cores) as ex:
+        list(ex.map(one, range(total_rows)))
+    call_all = time.perf_counter() - t0
+    kv = w.kv_bytes()
+    return {"value": round(kv / call_all / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"all {total_rows} query rows of {name} (the whole call), fp64 oracle, one oracle call per "
+                      f"row on {cores} threads: {call_all:.1f} s",
+            "tok_per_s": round(s.B * s.T / call_all, 4),
+            "single_thread": {"value": round(kv / call_1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"{n1} of {total_rows} query rows ({t_sum / n1:.2f} s/row), scaled to the "
+                                        f"whole call ({call_1:.1f} s)"}}
+
+
+def hbm_probe(K, torch, dev, mib=2048, reps=20):
+    """Measured streaming ceilings of this GPU on a 2 GiB buffer, each the median of `reps`
+    timed runs (events): the library's streaming-read probe kernel (kvq_probe.h) at several
+    grid sizes (the best is the read ceiling) and torch's copy (read + write bytes)."""
+    n = mib * 2 ** 20
+    a = torch.empty(n // 4, dtype=torch.float32, device=dev)
+    b = torch.empty(n // 4, dtype=torch.float32, device=dev)
+    a.fill_(1.0)
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)
+    out = {}
+    probes = [(f"read_wg{wg}", (lambda wg=wg: K.hbm_read_probe(a, wg, sink)), n) for wg in (256, 512, 1024, 2048)]
+    for kind, fn, nbytes in probes + [("copy", lambda: b.copy_(a), 2 * n)]:
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) * 1e-3)
+        t.sort()
+        out[f"{kind}_gbs"] = round(nbytes / t[len(t) // 2] / 1e9, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    out["read_gbs"] = max(v for k, v in out.items() if k.startswith("read_wg"))
+    out["buffer_mib"] = mib
+    out["kernels"] = ("kvq_hbm_read_probe (non-temporal 16-byte loads, 256-thread workgroups) at 256..2048 "
+                      "workgroups; torch copy_ (read+write bytes); median of 20 each")
+    return out
+
+
+def depth_sweep(K, S, H, torch, dev, steps):
+    """Split-kernel time against context depth (INT8 group-64, B=1, Hq=24, Hkv=4, D=256, 64
+    chunks per KV head at every depth): T=1 and T=4 at 32K..256K, and the least-squares line
+    us = fixed + per_page * pages per team (pages a 4-wave team streams = L / 64 / 64 / 2)."""
+    res = {}
+    for T in (1, 4):
+        pts = []
+        for L in (32768, 65536, 131072, 196608, 262144):
+            shp = dataclasses.replace(S.shape("mtp128k"), T=T, lens=[L], name=f"sweep_t{T}_{L}")
+            print(f"[bench] depth sweep T={T} L={L}", file=sys.stderr, flush=True)
+            run = Run(K, S, H, torch, shp, dev)
+            run.build_graphs()
+            t0 = time.perf_counter()  # settle the clocks, as the main measurement does
+            while time.perf_counter() - t0 < SETTLE_S:
+                run.g_split.replay()
+                torch.cuda.synchronize()
+            ms = run._events(run.g_split, max(1, steps // run.n_copies), run.n_copies)[1]
+            pts.append((L // 64 // 64 // 2, ms * 1e3))
+            del run
+            torch.cuda.empty_cache()
+        n = len(pts)
+        mx = sum(p for p, _ in pts) / n
+        my = sum(u for _, u in pts) / n
+        slope = sum((p - mx) * (u - my) for p, u in pts) / sum((p - mx) ** 2 for p, _ in pts)
+        res[f"T={T}"] = {"split_us_by_context": {str(p * 8192): round(u, 2) for p, u in pts},
+                         "per_page_us": round(slope, 3), "fixed_us": round(my - slope * mx, 2)}
+    return res
 
 
 def main():
@@ -339,6 +438,9 @@ def main():
     ap.add_argument("--headline-only", action="store_true", help="skip the other depths")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs (for counter collection)")
+    ap.add_argument("--depth-sweep", action="store_true",
+                    help="also time the split kernel against context depth (T=1 and T=4, 32K..256K)")
+    ap.add_argument("--no-hbm-probe", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB once (a known-size kernel for counters)")
     args = ap.parse_args()
@@ -390,6 +492,8 @@ def main():
             "n_splits": run.n_splits,
             "tokens_per_split": run.tps,
             "two_call_ms": (sum(two_ms) / len(two_ms)) if two_ms else None,
+            "attn_ms": (sum(run.attn_ms) / len(run.attn_ms)) if getattr(run, "attn_ms", None) else None,
+            "step_pct_us": getattr(run, "step_pct_us", None),
             "wall_ms": getattr(run, "wall_ms", None),
             "chunk_ms": chunk_ms,
             "chunk_bytes": chunk_bytes,
@@ -429,11 +533,17 @@ def main():
                      "frac": round(head["split_gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(args.workload),
                      "kernel": "attn_split_kernel", "launch_avg_us": round(head["split_ms_avg"] * 1e3, 2),
-                     "alg_bytes_per_launch": head["split_alg_bytes"]},
+                     "alg_bytes_per_launch": head["split_alg_bytes"],
+                     # the whole paged_decode_attn call (split + merge kernels, no append)
+                     "attn_call_us": round(head["attn_ms"] * 1e3, 2) if head["attn_ms"] else None,
+                     "attn_call_frac": round(head["split_alg_bytes"] / (head["attn_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                     if head["attn_ms"] else None},
         "depths": {n: {"kv_gbs": round(r["kv_gbs"], 1), "pct_hbm_peak": round(100 * r["kv_gbs"] / HBM_PEAK_GBS, 2),
                        "tok_per_s": round(r["tok_per_s"], 1), "us_per_step": round(r["ms_per_step"] * 1e3, 2),
                        "split_us": round(r["split_ms_avg"] * 1e3, 2), "split_gbs": round(r["split_gbs"], 1),
                        "us_per_step_two_calls": round(r["two_call_ms"] * 1e3, 2) if r["two_call_ms"] else None,
+                       "us_per_step_pct": r["step_pct_us"],
+                       "attn_call_us": round(r["attn_ms"] * 1e3, 2) if r["attn_ms"] else None,
                        "us_per_step_host_wall": round(r["wall_ms"] * 1e3, 2) if r["wall_ms"] else None,
                        "n_splits": r["n_splits"], "pool_copies": r["n_copies"],
                        **({"append_chunk_rows": 4096, "append_chunk_us": round(r["chunk_ms"] * 1e3, 2),
@@ -445,10 +555,16 @@ def main():
                                                                 / (MFMA_F16_PEAK_TFLOPS * 1e12), 4)}
                           if r["prefill_ms"] else {})} for n, r in results.items()},
         "host": {"cpu": model, "nproc": ncpu},
+        "step_us_pct": head["step_pct_us"],
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a bounded sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(S, H, args.workload)
+    if not args.no_hbm_probe and not args.eager:
+        print("[bench] HBM read/copy probe", file=sys.stderr, flush=True)
+        line["hbm_probe"] = hbm_probe(K, torch, dev)
+    if args.depth_sweep:
+        line["depth_sweep"] = depth_sweep(K, S, H, torch, dev, args.steps)
     print(json.dumps(line), flush=True)
 
 

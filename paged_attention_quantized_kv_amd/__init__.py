@@ -56,6 +56,8 @@ def _load():
     for name in ("paged_decode_attn", "paged_decode_attn_split", "paged_decode_attn_merge", "paged_prefill_attn"):
         getattr(L, name).argtypes = attn
         getattr(L, name).restype = C.c_int
+    L.kvq_hbm_read_probe.argtypes = [vp, C.c_size_t, i32, vp, vp]
+    L.kvq_hbm_read_probe.restype = C.c_int
     L.paged_decode_attn_noalloc.argtypes = attn[:12] + [vp]
     L.paged_decode_attn_noalloc.restype = C.c_int
     L.paged_decode_attn_noalloc_max_bytes.argtypes = []
@@ -236,6 +238,14 @@ def paged_decode_attn_noalloc(cache, q, block_table, seq_lens, max_seq_len, soft
                                          block_table.shape[1], _ptr(seq_lens), int(max_seq_len), float(softmax_scale),
                                          _ptr(out), _stream(stream)))
     return out
+
+
+def hbm_read_probe(buf, workgroups, sink, stream=None):
+    """Read the whole of `buf` once with the library's streaming-read probe kernel."""
+    rc = lib.kvq_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), int(workgroups), _ptr(sink),
+                                _stream(stream))
+    if rc != 0:
+        raise KvqError(rc, "kvq_hbm_read_probe: invalid arguments or launch refused")
 
 
 def noalloc_max_bytes() -> int:

@@ -17,9 +17,9 @@ LIB = os.path.join(HERE, "libkvq.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 SOURCES = [os.path.join(HERE, "csrc", f) for f in
            ("kvq_api.hip", "append.hip", "attn.hip", "attn_f0.hip", "attn_f1.hip", "attn_f2.hip", "attn_f3.hip",
-            "attn_f4.hip", "check.hip")]
+            "attn_f4.hip", "check.hip", "probe.hip")]
 HEADERS = [os.path.join(HERE, "csrc", f) for f in ("internal.h", "quant_row.h", "attn_kernels.h")] + \
-          [os.path.join(ROOT, "include", "kvq.h")]
+          [os.path.join(ROOT, "include", "kvq.h"), os.path.join(ROOT, "include", "kvq_probe.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -16,7 +16,8 @@ def K():
 
 
 def _declared():
-    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    inc = os.path.join(ROOT, "include")
+    text = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
 
@@ -24,7 +25,7 @@ def _declared():
 def test_every_declared_function_is_exported(K):
     names = _declared()
     assert {"kv_append_quant", "paged_decode_attn", "paged_decode_attn_workspace_bytes",
-            "kvq_status_string"} <= set(names)
+            "kvq_status_string", "paged_decode_attn_noalloc", "kvq_hbm_read_probe"} <= set(names)
     raw = C.CDLL(K.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n

@@ -407,6 +407,64 @@ __device__ inline void f16x2_to_f32(uint32_t w, float &x, float &y) {
   y = static_cast<float>(h[1]);
 }
 
+// Balanced chunking of a call of 2..kMaxBalancedSeqs sequences.  Every (sequence, KV head)
+// is cut into chunks of one common length of pp pages (an even count, whole rounds of the
+// teams), the smallest for which the call's chunks, sum over (b, kvh) of ceil(pages_b / pp),
+// number at most kTargetWgs (one workgroup per compute unit, so they all run at once), and at
+// most kMaxChunkPages.  A sequence so gets chunks in proportion to its own length.  Chunk c of
+// unit (b, kvh) is split workgroup and partial slot first_b + kvh * n_b + c, first_b =
+// Hkv * (n_0 + .. + n_{b-1}).  A sequence whose length is out of range counts as one chunk of
+// no pages (its rows come out NaN).  Lane b of the wave gets sequence b's first_b and n_b;
+// every lane the common chunk length and the slot count.
+struct BalancedChunks {
+  int tps, first, n, total;
+};
+__device__ inline int wave_sum(int x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ inline BalancedChunks balanced_chunks(const AttnArgs &a, int lane) {
+  int pages = 0;
+  if (lane < a.num_seqs) {
+    const int L = a.seq_lens[lane];
+    if (L >= a.T && L <= a.max_seq_len && L <= a.max_blocks * kPage) pages = (L + kPage - 1) / kPage;
+  }
+  auto even = [](int x) { return x + (x & 1); };
+  auto count = [&](int q) {  // the call's chunks at q pages per chunk
+    return wave_sum(lane < a.num_seqs ? max(1, (pages + q - 1) / q) : 0) * a.num_kv_heads;
+  };
+  const long P = static_cast<long>(wave_sum(pages)) * a.num_kv_heads;
+  int pp = max(even(static_cast<int>((P + kTargetWgs - 1) / kTargetWgs)), kTeams);
+  if (count(pp) > kTargetWgs) {  // rounding up per unit added chunks: search the smallest length that fits
+    int hi = pages;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) hi = max(hi, __shfl_xor(hi, o));
+    hi = max(even(hi), pp);  // one chunk per unit: the fewest chunks there can be
+    int lo = pp;             // count(lo) > kTargetWgs
+    while (hi - lo > 2) {
+      const int mid = even((lo + hi) / 2);
+      if (mid >= hi) break;
+      if (count(mid) <= kTargetWgs) hi = mid; else lo = mid;
+    }
+    pp = hi;
+  }
+  pp = min(pp, kMaxChunkPages);
+  const int n = (lane < a.num_seqs) ? max(1, (pages + pp - 1) / pp) : 0;
+  int incl = n * a.num_kv_heads;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  BalancedChunks c;
+  c.tps = pp * kPage;
+  c.first = incl - n * a.num_kv_heads;
+  c.n = n;
+  c.total = __shfl(incl, 63);
+  return c;
+}
+
 template <int D, int NT, int NTEAM, int QP>
 struct Smem {
   static constexpr int ROWS = 16 * NT, PST = 64 + 4, G64 = D / 64;
@@ -444,8 +502,24 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = (tid >> 6) & 3, team = tid >> 8;
   const int q4 = lane >> 4, c16 = lane & 15;
-  const int split = blockIdx.x, kvh = blockIdx.y % a.num_kv_heads, b = blockIdx.z;
+  int split = blockIdx.x, kvh = blockIdx.y % a.num_kv_heads, b = blockIdx.z;
   const int row0 = (blockIdx.y / a.num_kv_heads) * ROWS;  // first query row (t*G + g) of this block
+  int tps = a.tokens_per_split;
+  size_t part = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits + split;  // partial slot
+  if constexpr (APP != 2) {
+    if (a.balanced != 0) {  // this workgroup's (sequence, KV head, chunk) from the actual lengths
+      const BalancedChunks c = balanced_chunks(a, lane);
+      const int w = blockIdx.x;
+      const unsigned long long m = __ballot(lane < a.num_seqs && c.first <= w && w < c.first + c.n * a.num_kv_heads);
+      if (m == 0) return;  // past the call's chunks
+      b = __ffsll(static_cast<long long>(m)) - 1;
+      const int first = __shfl(c.first, b), nb = __shfl(c.n, b);
+      kvh = (w - first) / nb;
+      split = (w - first) % nb;
+      tps = c.tps;
+      part = w;
+    }
+  }
   const int L = a.seq_lens[b];
   if (L < a.T || L > a.max_seq_len || L > a.max_blocks * kPage) {  // the merge writes NaN rows
     if (a.direct_out != 0 && split == 0) {  // no merge: write them here
@@ -462,9 +536,9 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   // keys this block's rows can see: row r = t*G + g sees positions 0 .. L - T + t
   const int lim = (APP == 2) ? L - a.T + (min(row0 + ROWS, R) - 1) / a.group + 1 : L;
   const int lo_last = L - a.T + row0 / a.group;  // the last key the block's first row sees
-  const int tok0 = split * a.tokens_per_split;
+  const int tok0 = split * tps;
   if (tok0 >= lim) return;  // chunk past every key of these rows: the merge skips it
-  const int tok1 = min(tok0 + a.tokens_per_split, lim);
+  const int tok1 = min(tok0 + tps, lim);
   const int page0 = tok0 / kPage, page1 = (tok1 + kPage - 1) / kPage;
 
   // ---- the chunk's block ids -> pool pages in LDS (an invalid id reads block 0 and flags the chunk)
@@ -1202,7 +1276,6 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     __syncthreads();
   }
   if (team == 0) {
-    const size_t part = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits + split;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int rl = 16 * nt + c16, r = row0 + rl;
@@ -1251,7 +1324,14 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
   const int h = row % a.num_q_heads, t = (row / a.num_q_heads) % a.T, b = row / (a.num_q_heads * a.T);
   float *dst = a.out + static_cast<size_t>(row) * D + 64 * qs;
   const int kvh = h / a.group, r = t * a.group + h % a.group;
-  const size_t part0 = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits;
+  size_t part0 = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits;  // slot of chunk 0
+  int nsl = a.n_splits, tps = a.tokens_per_split;  // chunk slots of this (sequence, KV head), chunk length
+  if (a.balanced != 0) {
+    const BalancedChunks c = balanced_chunks(a, lane);
+    nsl = __shfl(c.n, b);
+    part0 = static_cast<size_t>(__shfl(c.first, b)) + static_cast<size_t>(kvh) * nsl;
+    tps = c.tps;
+  }
   const int c4 = lane & 15, sg = lane >> 4, col = qs * 16 + c4;
   const float2 *ml2 = reinterpret_cast<const float2 *>(a.ws_ml);
   auto o_at = [&](int s) { return reinterpret_cast<const float4 *>(a.ws_o + ((part0 + s) * a.rows + r) * D)[col]; };
@@ -1260,7 +1340,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
   float2 ml[MPER];
 #pragma unroll
   for (int k = 0; k < MPER; ++k) {
-    const int s = min(sg + 4 * k, a.n_splits - 1);
+    const int s = min(sg + 4 * k, nsl - 1);
     x[k] = o_at(s);
     ml[k] = ml2[(part0 + s) * a.rows + r];
   }
@@ -1270,7 +1350,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
     return;
   }
   // chunks holding keys this row sees (later chunks were skipped or hold none of them)
-  const int ns = (L - a.T + t + a.tokens_per_split) / a.tokens_per_split;
+  const int ns = (L - a.T + t + tps) / tps;
   float mloc = -INFINITY;
 #pragma unroll
   for (int k = 0; k < MPER; ++k)
@@ -1785,7 +1865,7 @@ template <int D, int NT, int FMT, int QDT>
 hipError_t split_one(const AttnArgs &a, hipStream_t s) {
   // fp32 queries need the hi+lo pair; bf16 queries are one exact f16, unless rotated (rk8v4)
   constexpr int QLO = QDT == 0 ? 1 : ((FMT == 2 || FMT == 3) ? 2 : 0);
-  const dim3 grid(a.n_splits, a.num_kv_heads, a.num_seqs);
+  const dim3 grid = a.balanced ? dim3(a.n_splits) : dim3(a.n_splits, a.num_kv_heads, a.num_seqs);
   if (a.k_new != nullptr)
     hipLaunchKernelGGL((attn_split_kernel<D, NT, FMT, QLO, kTeams, 1>), grid, dim3(256 * kTeams), 0, s, a);
   else

@@ -56,7 +56,19 @@ struct AttnArgs {
   int32_t row_blocks;   // blocks of 16*NT query rows per KV head (grid y = row_blocks * num_kv_heads)
   int32_t direct_out;   // one chunk per row block: write normalized rows to out, no merge
   float qk_scale_log2;  // softmax_scale * log2(e)
+  // balanced != 0 (decode, 2..kMaxBalancedSeqs sequences): chunks of one common length set on
+  // the device from the actual lengths (balanced_chunks); n_splits is then the number of
+  // partial slots and split workgroups (grid x), not the chunks per (sequence, KV head)
+  int32_t balanced;
 };
+constexpr int kMaxBalancedSeqs = 32;
+// partial slots (and split workgroups) of a balanced call: one per chunk at most, where every
+// (sequence, KV head) may round up by one chunk and a chunk holds at most kMaxChunkPages pages
+inline long balanced_slots(long num_seqs, long num_kv_heads, long max_seq_len) {
+  const long pages = num_seqs * num_kv_heads * ((max_seq_len + kPage - 1) / kPage);
+  const long by_cap = (pages + kMaxChunkPages - 1) / kMaxChunkPages;
+  return (by_cap > kTargetWgs ? by_cap : kTargetWgs) + num_seqs * num_kv_heads;
+}
 
 // Launch arguments of kvq_check_tables, validated on the host.
 struct CheckArgs {

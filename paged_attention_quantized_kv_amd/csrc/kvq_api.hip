@@ -44,6 +44,8 @@ int32_t chunk_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len
 
 struct AttnShape {
   int32_t group, rows, tokens_per_split, n_splits;
+  bool balanced;  // 2..kMaxBalancedSeqs sequences: chunk length set on the device from the lengths
+  int32_t slots;  // partial slots (= split workgroups when balanced)
   size_t ml_bytes, o_bytes;
 };
 
@@ -62,7 +64,12 @@ int attn_shape(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_
   s->rows = T * group;
   s->tokens_per_split = chunk_tokens(num_seqs, num_kv_heads, max_seq_len);
   s->n_splits = (max_seq_len + s->tokens_per_split - 1) / s->tokens_per_split;
-  const size_t parts = static_cast<size_t>(num_seqs) * num_kv_heads * s->n_splits * s->rows;
+  s->balanced = num_seqs >= 2 && num_seqs <= kvq::kMaxBalancedSeqs;
+  const long slots = s->balanced ? kvq::balanced_slots(num_seqs, num_kv_heads, max_seq_len)
+                                 : static_cast<long>(num_seqs) * num_kv_heads * s->n_splits;
+  if (slots > 0x7FFFFFFFL) return KVQ_ERR_UNSUPPORTED;
+  s->slots = static_cast<int32_t>(slots);
+  const size_t parts = static_cast<size_t>(slots) * s->rows;
   s->ml_bytes = ((parts * 2 * sizeof(float)) + 255) & ~static_cast<size_t>(255);
   s->o_bytes = parts * head_dim * sizeof(float);
   return KVQ_OK;
@@ -155,11 +162,12 @@ int attn_call(Phase phase, const kvq_cache_t *cache, const void *q, int32_t q_dt
   a.max_blocks = max_blocks_per_seq;
   a.max_seq_len = max_seq_len;
   a.tokens_per_split = s.tokens_per_split;
-  a.n_splits = s.n_splits;
+  a.balanced = s.balanced ? 1 : 0;
+  a.n_splits = s.balanced ? s.slots : s.n_splits;
   a.row_blocks = 1;
   // one call with one chunk per (sequence, KV head): the split kernel writes the normalized
   // rows itself and no merge runs (the two phases called apart keep the partials)
-  a.direct_out = (phase == Phase::kBoth && s.n_splits == 1) ? 1 : 0;
+  a.direct_out = (phase == Phase::kBoth && !s.balanced && s.n_splits == 1) ? 1 : 0;
   a.qk_scale_log2 = softmax_scale * 1.4426950408889634f;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -369,6 +377,7 @@ int paged_prefill_attn(const kvq_cache_t *cache, const void *q, int32_t q_dtype,
   a.tokens_per_split = s.tokens_per_split;
   a.n_splits = s.n_splits;
   a.row_blocks = s.row_blocks;
+  a.balanced = 0;
   a.direct_out = s.direct ? 1 : 0;
   a.qk_scale_log2 = softmax_scale * 1.4426950408889634f;
 

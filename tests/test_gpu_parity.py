@@ -357,3 +357,36 @@ def test_merge_of_more_than_64_chunks(K, shp):
     w = S.make(shp, seed=S.seed_of("tiny") + 800 + shp.B)
     check(K, w)
     _fused_check(K, w)
+
+
+BALANCED = {
+    "skew_b8": S.tiny_shape(B=8, T=1, Hq=24, Hkv=4, D=256, lens=(131072, 64, 65, 100, 200, 1, 2, 3000),
+                            src=S.SRC_BF16, outliers=True, name="skew_b8"),
+    "b32_t4": S.tiny_shape(B=32, T=4, Hq=12, Hkv=2, D=128, lens=tuple(int(x) for x in
+                                                                     np.random.default_rng(9).integers(4, 9000, 32)),
+                           src=S.SRC_F32, fmt=S.FMT_FP8_ROW, name="b32_t4"),
+    "b2_t4_rk8v4": S.tiny_shape(B=2, T=4, Hq=24, Hkv=4, D=256, lens=(30000, 29000), src=S.SRC_BF16,
+                                fmt=S.FMT_RK8V4, outliers=True, name="b2_t4_rk8v4"),
+}
+
+
+@pytest.mark.parametrize("name", list(BALANCED))
+def test_balanced_chunking(K, name):
+    """Cohorts of 2..32 sequences: chunks of one common length set on the device from the
+    actual lengths, so a sequence's chunk count follows its own length (a 131,072-token
+    sequence beside tiny ones takes nearly all the workgroups).  Parity with the oracle,
+    the two phases called apart equal to the one call bit for bit, and the fused step."""
+    shp = BALANCED[name]
+    w = S.make(shp, seed=S.seed_of("tiny") + 900 + list(BALANCED).index(name))
+    rows = _sample_rows(w, 2)
+    cache, bt, out, _ = check(K, w, rows=rows)
+    s = w.shape
+    q = H.src_tensor(w.q, s.src, DEV)
+    sl = torch.from_numpy(w.seq_lens).to(DEV)
+    two = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    ws = K.alloc_workspace(cache, s.B, s.T, s.Hq, w.max_seq_len, device=DEV)
+    K.paged_decode_attn_split(cache, q, bt, sl, w.max_seq_len, w.softmax_scale, two, ws)
+    K.paged_decode_attn_merge(cache, q, bt, sl, w.max_seq_len, w.softmax_scale, two, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(two, out)
+    _fused_check(K, w, rows=rows)

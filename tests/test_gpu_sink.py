@@ -8,8 +8,8 @@ carry a visible share of the output, so a kernel that loses or biases small
 weights in P.V misses the 2e-3 bar here even though it passes on N(0,1) data.
 The sinks sit at chunk starts, so every context chunk of the split has one.
 
-Modes: 64 chunks per KV head (128K T=4, 256K T=1), 8 chunks per (sequence, KV
-head) in the C=8-shaped cohort, one chunk per (sequence, KV head) in a 64-sequence
+Modes: 64 chunks per KV head (128K T=4, 256K T=1), chunks of a common length set
+from the lengths in the C=8-shaped cohort, one chunk per (sequence, KV head) in a 64-sequence
 cohort, and prefill with one chunk over the whole context (the prefill kernel and
 the split kernel's prefill instance).  Codes and scales are compared byte for
 byte, attention element by element against the fp64 oracle on every query row t
@@ -91,12 +91,21 @@ def test_sink_256k_t1_64_chunks(K, fmt):
     check(K, w, rows_every_t(w, 3), label=f"256K T=1 {fmt}")
 
 
+def balanced_chunk_tokens(lens, Hkv, W=256):
+    """Chunk length of a 2..32-sequence call: the smallest even page count (at most 256) for
+    which the call's chunks, sum of ceil(pages / length) over (sequence, KV head), fit in W."""
+    pages = [(L + 63) // 64 for L in lens]
+    count = lambda q: Hkv * sum(max(1, -(-p // q)) for p in pages)
+    pp = next(q for q in range(2, max(pages) + 3, 2) if count(q) <= W)
+    return min(pp, 256) * 64
+
+
 @pytest.mark.parametrize("fmt,gap", [("int8", 13.0), ("fp8", 13.0), ("int8", 16.0), ("rk8v4", 13.0)])
 def test_sink_cohort_8_chunks(K, fmt, gap):
     g = np.random.default_rng(3)
     lens = [int(x) for x in g.integers(4096, 65536 + 1, 8)]
     shp = S.tiny_shape(B=8, T=4, Hq=24, Hkv=4, D=256, lens=lens, src=S.SRC_BF16, fmt=FMTS[fmt])
-    tps = K.num_splits(8, 4, 24, 4, 256, max(lens))[1]
+    tps = balanced_chunk_tokens(lens, 4)
     w = S.make_sink(shp, gap_nats=gap, stride=tps, seed=3)
     check(K, w, rows_every_t(w, 1), label=f"C=8 {fmt} gap {gap} ({tps}-token chunks)")
 

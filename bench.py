@@ -39,7 +39,7 @@ DEPTHS = ["qwen32k", "mtp128k", "c8", "full256k_int8", "full256k_fp8", "mtp128k_
           "full256k_bf16", "full256k_rk8v4", "full256k_rk4v4"]
 SETTLE_S = 0.2  # seconds of untimed back-to-back steps before the warmup steps
 FLUSH_BYTES = 1.5 * 2 ** 30  # bytes read between two reads of one pool copy (> 256 MB MALL)
-KERNEL_SOURCES = ("internal.h", "quant_row.h", "attn_kernels.h")  # what the split kernel is built from
+KERNEL_SOURCES = ("internal.h", "shape.h", "quant_row.h", "attn_kernels.h")  # what the split kernel is built from
 
 
 def kernel_sources_sha256():

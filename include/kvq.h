@@ -68,8 +68,8 @@
  *
  * Supported shapes: block_size 64; head_dim 128 or 256; 1 <= T <= 8;
  * num_q_heads a multiple of num_kv_heads with T * (num_q_heads/num_kv_heads)
- * <= 32; 1 <= num_seqs <= 1024 (paged_prefill_attn takes any T, see there).
- * Anything else returns KVQ_ERR_UNSUPPORTED.
+ * <= 32; 1 <= num_seqs <= 1024 (paged_prefill_attn takes any T, see there);
+ * max_seq_len <= 2^30 tokens.  Anything else returns KVQ_ERR_UNSUPPORTED.
  */
 #ifndef KVQ_H
 #define KVQ_H

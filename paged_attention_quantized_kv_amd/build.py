@@ -17,8 +17,8 @@ LIB = os.path.join(HERE, "libkvq.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 SOURCES = [os.path.join(HERE, "csrc", f) for f in
            ("kvq_api.hip", "append.hip", "attn.hip", "attn_f0.hip", "attn_f1.hip", "attn_f2.hip", "attn_f3.hip",
-            "attn_f4.hip", "check.hip", "probe.hip")]
-HEADERS = [os.path.join(HERE, "csrc", f) for f in ("internal.h", "quant_row.h", "attn_kernels.h")] + \
+            "attn_f4.hip", "check.hip", "probe.hip", "shape.cpp")]
+HEADERS = [os.path.join(HERE, "csrc", f) for f in ("internal.h", "shape.h", "quant_row.h", "attn_kernels.h")] + \
           [os.path.join(ROOT, "include", "kvq.h"), os.path.join(ROOT, "include", "kvq_probe.h")]
 
 HIPCC_FLAGS = [
@@ -47,7 +47,7 @@ def build(verbose: bool = False, jobs: int | None = None, out: str | None = None
     obj_dir = OBJ_DIR if out is None else os.path.join(OBJ_DIR, os.path.basename(out)[:-3])
     os.makedirs(obj_dir, exist_ok=True)
     sources = SOURCES if src_dir is None else [os.path.join(src_dir, os.path.basename(s)) for s in SOURCES]
-    objs = [os.path.join(obj_dir, os.path.basename(s)[:-4] + ".o") for s in sources]
+    objs = [os.path.join(obj_dir, os.path.splitext(os.path.basename(s))[0] + ".o") for s in sources]
     flags = HIPCC_FLAGS + [f"-D{d}" for d in defines]
     if src_dir is not None:
         flags += ["-I", os.path.join(src_dir, "..", "..", "include")]

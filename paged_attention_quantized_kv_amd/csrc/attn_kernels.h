@@ -428,7 +428,7 @@ __device__ inline BalancedChunks balanced_chunks(const AttnArgs &a, int lane) {
   int pages = 0;
   if (lane < a.num_seqs) {
     const int L = a.seq_lens[lane];
-    if (L >= a.T && L <= a.max_seq_len && L <= a.max_blocks * kPage) pages = (L + kPage - 1) / kPage;
+    if (L >= a.T && L <= a.max_seq_len && L <= static_cast<long>(a.max_blocks) * kPage) pages = (L + kPage - 1) / kPage;
   }
   auto even = [](int x) { return x + (x & 1); };
   auto count = [&](int q) {  // the call's chunks at q pages per chunk
@@ -521,7 +521,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     }
   }
   const int L = a.seq_lens[b];
-  if (L < a.T || L > a.max_seq_len || L > a.max_blocks * kPage) {  // the merge writes NaN rows
+  if (L < a.T || L > a.max_seq_len || L > static_cast<long>(a.max_blocks) * kPage) {  // the merge writes NaN rows
     if (a.direct_out != 0 && split == 0) {  // no merge: write them here
       for (int e = threadIdx.x; e < ROWS * D; e += blockDim.x) {
         const int r = row0 + e / D;
@@ -1345,7 +1345,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
     ml[k] = ml2[(part0 + s) * a.rows + r];
   }
   const int L = a.seq_lens[b];
-  if (L < a.T || L > a.max_seq_len || L > a.max_blocks * kPage) {
+  if (L < a.T || L > a.max_seq_len || L > static_cast<long>(a.max_blocks) * kPage) {
     dst[lane] = NAN;
     return;
   }
@@ -1417,7 +1417,7 @@ __global__ __launch_bounds__(64 * 8 / KVQ_PREFILL_NTW, 1) void prefill_kernel(At
   const int row0 = (blockIdx.y / a.num_kv_heads) * ROWS;
   const int L = a.seq_lens[b];
   const int R = a.rows;
-  if (L < a.T || L > a.max_seq_len || L > a.max_blocks * kPage) {  // the merge writes NaN rows
+  if (L < a.T || L > a.max_seq_len || L > static_cast<long>(a.max_blocks) * kPage) {  // the merge writes NaN rows
     if (a.direct_out != 0 && split == 0) {                        // no merge: write them here
       for (int e = tid; e < ROWS * D; e += NTH) {
         const int r = row0 + e / D;

@@ -5,30 +5,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "shape.h"
+
 namespace kvq {
-
-#ifndef KVQ_NT_LOADS
-#define KVQ_NT_LOADS 1
-#endif
-#ifndef KVQ_TEAMS
-#define KVQ_TEAMS 2
-#endif
-
-constexpr int kPage = 64;                   // token slots per page
-constexpr int kTeams = KVQ_TEAMS;           // 4-wave teams per attention workgroup
-constexpr int kTargetWgs = 512 / KVQ_TEAMS; // 8 waves per compute unit of the 256-CU chip
-constexpr int kMaxChunkPages = 256;   // pages of one decode attention chunk (block ids staged in LDS)
-constexpr int kMaxPrefillChunkPages = 4096;  // the same for prefill (262,144 tokens per chunk)
-#ifndef KVQ_PREFILL_NT
-#define KVQ_PREFILL_NT 4
-#endif
-#ifndef KVQ_PREFILL_TEAMS
-#define KVQ_PREFILL_TEAMS KVQ_TEAMS
-#endif
-constexpr int kPrefillNT = KVQ_PREFILL_NT;        // 16-row tiles of a prefill row block
-constexpr int kPrefillTeams = KVQ_PREFILL_TEAMS;  // 4-wave teams of a prefill workgroup
-constexpr int kPrefillRows = 16 * kPrefillNT;   // query rows (t*G + g) of a prefill row block
-constexpr int kBulkAppendRows = 64;   // appends of at least this many rows per sequence go page by page
 
 // Launch arguments of kv_append_quant, validated on the host.
 struct AppendArgs {
@@ -61,14 +40,6 @@ struct AttnArgs {
   // partial slots and split workgroups (grid x), not the chunks per (sequence, KV head)
   int32_t balanced;
 };
-constexpr int kMaxBalancedSeqs = 32;
-// partial slots (and split workgroups) of a balanced call: one per chunk at most, where every
-// (sequence, KV head) may round up by one chunk and a chunk holds at most kMaxChunkPages pages
-inline long balanced_slots(long num_seqs, long num_kv_heads, long max_seq_len) {
-  const long pages = num_seqs * num_kv_heads * ((max_seq_len + kPage - 1) / kPage);
-  const long by_cap = (pages + kMaxChunkPages - 1) / kMaxChunkPages;
-  return (by_cap > kTargetWgs ? by_cap : kTargetWgs) + num_seqs * num_kv_heads;
-}
 
 // Launch arguments of kvq_check_tables, validated on the host.
 struct CheckArgs {

@@ -1,0 +1,99 @@
+// shape.cpp -- host-side shape logic (shape.h): descriptor checks, chunking, workspace sizes.
+#include "shape.h"
+
+namespace kvq {
+
+namespace {
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+}  // namespace
+
+int check_cache(const kvq_cache_t *c) {
+  if (!c) return KVQ_ERR_INVALID_ARG;
+  if (c->format < KVQ_INT8_G64 || c->format > KVQ_BF16_KV) return KVQ_ERR_INVALID_ARG;
+  if (c->num_blocks < 1 || c->num_kv_heads < 1 || c->block_size < 1) return KVQ_ERR_INVALID_ARG;
+  if (c->block_size != kPage) return KVQ_ERR_UNSUPPORTED;
+  if (c->head_dim != 128 && c->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
+  const void *p[4] = {c->k_codes, c->v_codes, c->k_scales, c->v_scales};
+  const int n = (c->format == KVQ_BF16_KV) ? 2 : 4;  // the BF16 pool has no scales
+  for (int i = 0; i < n; ++i)
+    if (!p[i] || !aligned16(p[i])) return KVQ_ERR_INVALID_ARG;
+  return KVQ_OK;
+}
+
+// Chunking of the context: a pure function of the shape.  Pages per chunk are
+// chosen so that num_seqs * num_kv_heads * chunks is about one workgroup per
+// compute unit, rounded to whole rounds of the workgroup's teams.
+int32_t chunk_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len) {
+  const long pages = (static_cast<long>(max_seq_len) + kPage - 1) / kPage;
+  const long total = pages * num_seqs * num_kv_heads;
+  long pps = (total + kTargetWgs - 1) / kTargetWgs;
+  pps = ((pps + kTeams - 1) / kTeams) * kTeams;
+  if (pps < kTeams) pps = kTeams;
+  if (pps > kMaxChunkPages) pps = kMaxChunkPages;
+  return static_cast<int32_t>(pps * kPage);
+}
+
+int attn_shape(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+               int32_t max_seq_len, AttnShape *s) {
+  if (num_seqs < 1 || T < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_seq_len < 1) return KVQ_ERR_INVALID_ARG;
+  if (head_dim != 128 && head_dim != 256) return KVQ_ERR_UNSUPPORTED;
+  if (num_q_heads % num_kv_heads != 0) return KVQ_ERR_UNSUPPORTED;
+  if (T > 8 || num_seqs > 1024 || num_kv_heads > 65535 || max_seq_len > kMaxSeqLen) return KVQ_ERR_UNSUPPORTED;
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (static_cast<long>(T) * group > 32) return KVQ_ERR_UNSUPPORTED;
+  // the merge launches one workgroup per 64-dim slice of every output row
+  if (static_cast<long>(num_seqs) * T * num_q_heads * (head_dim / 64) > 0x7FFFFFFFL) return KVQ_ERR_UNSUPPORTED;
+  if (max_seq_len < T) return KVQ_ERR_INVALID_ARG;
+  s->group = group;
+  s->rows = T * group;
+  s->tokens_per_split = chunk_tokens(num_seqs, num_kv_heads, max_seq_len);
+  s->n_splits = static_cast<int32_t>((static_cast<long>(max_seq_len) + s->tokens_per_split - 1) / s->tokens_per_split);
+  s->balanced = num_seqs >= 2 && num_seqs <= kMaxBalancedSeqs;
+  const long slots = s->balanced ? balanced_slots(num_seqs, num_kv_heads, max_seq_len)
+                                 : static_cast<long>(num_seqs) * num_kv_heads * s->n_splits;
+  if (slots > 0x7FFFFFFFL) return KVQ_ERR_UNSUPPORTED;
+  s->slots = static_cast<int32_t>(slots);
+  const size_t parts = static_cast<size_t>(slots) * s->rows;
+  s->ml_bytes = ((parts * 2 * sizeof(float)) + 255) & ~static_cast<size_t>(255);
+  s->o_bytes = parts * head_dim * sizeof(float);
+  return KVQ_OK;
+}
+
+// Prefill: any number of query rows T*G per KV head, in blocks of kPrefillRows (16-row
+// tiles); the context of each (sequence, KV head, row block) is cut into as few chunks
+// as give about one workgroup per compute unit (at most kMaxPrefillChunkPages pages
+// each).  With one chunk the split kernel writes the rows itself (no merge, no partials).
+int prefill_shape(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t max_seq_len, int block_rows, PrefillShape *s) {
+  if (num_seqs < 1 || T < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_seq_len < 1) return KVQ_ERR_INVALID_ARG;
+  if (head_dim != 128 && head_dim != 256) return KVQ_ERR_UNSUPPORTED;
+  if (num_q_heads % num_kv_heads != 0) return KVQ_ERR_UNSUPPORTED;
+  if (num_seqs > 1024 || num_kv_heads > 65535 || max_seq_len > kMaxSeqLen) return KVQ_ERR_UNSUPPORTED;
+  if (max_seq_len < T) return KVQ_ERR_INVALID_ARG;
+  const int32_t group = num_q_heads / num_kv_heads;
+  const long rows = static_cast<long>(T) * group;
+  const long row_blocks = (rows + block_rows - 1) / block_rows;
+  if (rows > 0x7FFFFFFFL || row_blocks * num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (static_cast<long>(num_seqs) * T * num_q_heads * (head_dim / 64) > 0x7FFFFFFFL) return KVQ_ERR_UNSUPPORTED;
+  const long pages = (static_cast<long>(max_seq_len) + kPage - 1) / kPage;
+  const long units = static_cast<long>(num_seqs) * num_kv_heads * row_blocks;
+  long n = (kTargetWgs + units - 1) / units;
+  const long nmin = (pages + kMaxPrefillChunkPages - 1) / kMaxPrefillChunkPages;
+  if (n < nmin) n = nmin;
+  long pps = (pages + n - 1) / n;
+  pps = ((pps + kPrefillTeams - 1) / kPrefillTeams) * kPrefillTeams;
+  if (pps > kMaxPrefillChunkPages) pps = kMaxPrefillChunkPages;
+  s->group = group;
+  s->rows = static_cast<int32_t>(rows);
+  s->row_blocks = static_cast<int32_t>(row_blocks);
+  s->tokens_per_split = static_cast<int32_t>(pps * kPage);
+  s->n_splits = static_cast<int32_t>((pages + pps - 1) / pps);
+  s->direct = (s->n_splits == 1);
+  const size_t parts = s->direct ? 0 : static_cast<size_t>(num_seqs) * num_kv_heads * s->n_splits * s->rows;
+  s->ml_bytes = ((parts * 2 * sizeof(float)) + 255) & ~static_cast<size_t>(255);
+  if (s->ml_bytes == 0) s->ml_bytes = 256;
+  s->o_bytes = parts * head_dim * sizeof(float);
+  return KVQ_OK;
+}
+
+}  // namespace kvq

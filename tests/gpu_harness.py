@@ -6,6 +6,9 @@ value produced here on the GPU ever feeds the oracle.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -88,6 +91,25 @@ def oracle_pool(O, w: S.Workload):
         pool.append(w.rows("k", b, 0, L), w.rows("v", b, 0, L), s.src, w.block_table[b:b + 1],
                     np.array([0], np.int32))
     return pool
+
+
+def oracle_attn(pool, w: S.Workload, rows=None, q=None, threads: int = 16) -> np.ndarray:
+    """The oracle's attention rows (all, or the given output rows), computed on several host
+    threads: rows are independent, and the C oracle releases the interpreter while it runs.
+    The first row runs alone, since the oracle fills its lookup tables on first use."""
+    s = w.shape
+    q = w.q if q is None else q
+    rows = np.arange(s.B * s.T * s.Hq, dtype=np.int32) if rows is None else np.asarray(rows, np.int32)
+
+    def call(r):
+        return pool.paged_attn(q, s.src, s.T, s.Hq, w.block_table, w.seq_lens, w.softmax_scale, rows=r)
+
+    if rows.size <= 1:
+        return call(rows)
+    first = call(rows[:1])
+    parts = np.array_split(rows[1:], min(threads, os.cpu_count() or 1, rows.size - 1))
+    with ThreadPoolExecutor(len(parts)) as ex:
+        return np.concatenate([first] + list(ex.map(call, parts)))
 
 
 def pool_equal(cache, pool) -> dict:

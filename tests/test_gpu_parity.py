@@ -45,7 +45,7 @@ def check(K, w, rows=None, chunk=8192, prefill=False):
     mism = H.pool_equal(cache, pool)
     assert mism == {"k_codes": 0, "v_codes": 0, "k_scales": 0, "v_scales": 0}, mism
     got = out.cpu().numpy().reshape(-1, s.D)
-    ref = pool.paged_attn(w.q, s.src, s.T, s.Hq, w.block_table, w.seq_lens, w.softmax_scale, rows=rows)
+    ref = H.oracle_attn(pool, w, rows)
     if rows is not None:
         got = got[np.asarray(rows)]
     assert np.all(np.isfinite(got))
@@ -232,7 +232,7 @@ def _fused_check(K, w, rows=None):
     mism = H.pool_equal(cache, pool)
     assert mism == {"k_codes": 0, "v_codes": 0, "k_scales": 0, "v_scales": 0}, mism
     got = out.cpu().numpy().reshape(-1, s.D)
-    ref = pool.paged_attn(w.q, s.src, s.T, s.Hq, w.block_table, w.seq_lens, w.softmax_scale, rows=rows)
+    ref = H.oracle_attn(pool, w, rows)
     if rows is not None:
         got = got[np.asarray(rows)]
     err = float(np.abs(got - ref).max())

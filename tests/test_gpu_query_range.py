@@ -57,7 +57,7 @@ def check(K, w, prefill=False, label=""):
     torch.cuda.synchronize()
     pool = H.oracle_pool(O, w)
     got = out.cpu().numpy().reshape(-1, s.D)
-    ref = pool.paged_attn(w.q, s.src, s.T, s.Hq, w.block_table, w.seq_lens, w.softmax_scale)
+    ref = H.oracle_attn(pool, w)
     assert np.all(np.isfinite(got))
     err = float(np.abs(got - ref).max())
     say(f"[qrange] {label}: max-abs err {err:.3e} over {got.size} outputs")

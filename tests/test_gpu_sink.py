@@ -68,7 +68,7 @@ def check(K, w, rows, chunk=65536, prefill=False, label=""):
     mism = H.pool_equal(cache, pool)
     assert mism == {"k_codes": 0, "v_codes": 0, "k_scales": 0, "v_scales": 0}, mism
     got = out.cpu().numpy().reshape(-1, s.D)[rows]
-    ref = pool.paged_attn(w.q, s.src, s.T, s.Hq, w.block_table, w.seq_lens, w.softmax_scale, rows=rows)
+    ref = H.oracle_attn(pool, w, rows)
     assert np.all(np.isfinite(got))
     err = float(np.abs(got - ref).max())
     say(f"[sink] {label}: max-abs err {err:.3e} over {got.size} outputs")

@@ -49,7 +49,7 @@ def test_noalloc_matches_workspace_call_twice(K):
         torch.cuda.synchronize()
         assert torch.equal(out, ref)
         pool = H.oracle_pool(O, w)
-        exp = pool.paged_attn(w.q, s.src, s.T, s.Hq, w.block_table, w.seq_lens, w.softmax_scale)
+        exp = H.oracle_attn(pool, w)
         err = float(np.abs(out.cpu().numpy().reshape(exp.shape) - exp).max())
         say(f"[noalloc] call {i}: equal to the workspace call; max-abs err vs oracle {err:.3e}")
         assert err <= TOL

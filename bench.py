@@ -255,10 +255,22 @@ class Run:
         q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
         return {"p10": round(q(0.1), 2), "p50": round(q(0.5), 2), "p90": round(q(0.9), 2)}
 
-    def measure_chunk_append(self, reps=20):
+    def _launcher(self, fn, eager):
+        """Something with replay() that runs fn(i) once per pool copy: a HIP graph, or (eager)
+        the plain launches, each its own dispatch (for counter collection)."""
+        if not eager:
+            return self._graph(fn, range(self.n_copies))
+
+        class _Eager:
+            def replay(_self):
+                for i in range(self.n_copies):
+                    fn(i)
+        return _Eager()
+
+    def measure_chunk_append(self, reps=20, eager=False):
         """kv_append_quant of the last prefill chunk (rewriting the same rows with the same
-        values), events around a graph of one append per pool copy.  Returns (ms per call,
-        bytes read + written by definition)."""
+        values), events around a graph of one append per pool copy (or the plain launches).
+        Returns (ms per call, bytes read + written by definition)."""
         if not hasattr(self, "chunk_k"):
             return None, None
         K, torch = self.K, self.torch
@@ -269,7 +281,7 @@ class Run:
         for i in range(self.n_copies):
             app(i)
         torch.cuda.synchronize()
-        g = self._graph(app, range(self.n_copies))
+        g = self._launcher(app, eager)
         g.replay()
         torch.cuda.synchronize()
         ms = self._events(g, reps, self.n_copies)[1]
@@ -279,10 +291,11 @@ class Run:
         dst = 2 * rows * (s.D + (2 * s.D // 64 if s.fmt == 0 else 4))
         return ms, src + dst
 
-    def measure_prefill_chunk(self, reps=2):
+    def measure_prefill_chunk(self, reps=2, eager=False):
         """paged_prefill_attn of the last prefill chunk where it sits in the context: its
         rows (seeded queries, N(0,1) in the source dtype) see every earlier key and the
-        chunk's own rows up to themselves.  Events around a graph of one call per pool copy.
+        chunk's own rows up to themselves.  Events around a graph of one call per pool copy
+        (or the plain launches).
         Returns (ms per call, flops by definition: 4 * D per visible (row, key) pair)."""
         if not hasattr(self, "chunk_k"):
             return None, None
@@ -303,7 +316,7 @@ class Run:
         for i in range(self.n_copies):
             pf(i)
         torch.cuda.synchronize()
-        gr = self._graph(pf, range(self.n_copies))
+        gr = self._launcher(pf, eager)
         gr.replay()
         torch.cuda.synchronize()
         ms = self._events(gr, reps, self.n_copies)[1]
@@ -475,8 +488,8 @@ def main():
         w = run.w
         s = w.shape
         split_avg = sum(split_ms) / len(split_ms)
-        chunk_ms, chunk_bytes = (None, None) if args.eager else run.measure_chunk_append()
-        pf_ms, pf_flops = (None, None) if args.eager else run.measure_prefill_chunk()
+        chunk_ms, chunk_bytes = run.measure_chunk_append(eager=args.eager)
+        pf_ms, pf_flops = run.measure_prefill_chunk(eager=args.eager)
         alg = run.algorithmic_split_bytes()
         results[name] = {
             "ms_per_step": ms,

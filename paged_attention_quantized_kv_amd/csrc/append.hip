@@ -59,6 +59,33 @@ __device__ inline void h64_rotate_threads(float (&x)[16], int c16) {
   for (int e = 0; e < 16; ++e) x[e] = static_cast<float>(y[e] * 0.125);
 }
 
+// c[e] = rint(fl(x[e] / sc)) clamped to +-lim, as the row quantizer computes it, for the 16
+// values of a thread whose quotients are bounded by lim (1 + 2^-11) < 128 (sc is the fp16
+// scale of their group's maximum).  One division per thread instead of one per value:
+// q0 = x * fl(1/sc) lies within 2^-23 |q| <= 2^-16 of q = x / sc, and fl(q) within 2^-18 of q,
+// so rint(q0) is rint(fl(q)) whenever q0 is more than 2^-15 from a half-integer.  Only a
+// thread holding a value that close divides its values out (about 2^-14 of values on random
+// data, so a few percent of waves take that branch).
+template <int LIM>
+__device__ inline void rint_quotients(const float (&x)[16], float sc, uint32_t (&c)[16], uint32_t mask) {
+  float r[16];
+  const float rs = 1.0f / sc;
+  bool amb = false;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float q0 = x[e] * rs;
+    r[e] = rintf(q0);
+    amb |= (0.5f - fabsf(q0 - r[e])) <= 0x1p-15f;
+  }
+  if (amb) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) r[e] = rintf(x[e] / sc);
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    c[e] = static_cast<uint32_t>(static_cast<int32_t>(fminf(fmaxf(r[e], -static_cast<float>(LIM)), static_cast<float>(LIM)))) & mask;
+}
+
 // Bulk appends (prefill chunks): one workgroup per (page, KV head, K|V, sequence), one
 // thread per (slot, 16 dims): 64 * D/16 threads.  Each thread quantizes its 16 values
 // with the same arithmetic as quant_row (so the codes are identical), the group or row
@@ -81,14 +108,11 @@ __global__ __launch_bounds__(kPage * D / 16) void append_page_kernel(AppendArgs 
   const int s_lo = static_cast<int>(max(pos0, pg * kPage) - pg * kPage);
   const int s_hi = static_cast<int>(min(pos_end, pg * kPage + kPage) - pg * kPage);
   const bool full = (s_lo == 0) && (s_hi == kPage);
-  const int blk = a.block_table[static_cast<long>(b) * a.max_blocks + pg];
-  if (blk < 0 || blk >= a.num_blocks) return;
   const bool mine = (sl >= s_lo) && (sl < s_hi);
-  const size_t page = static_cast<size_t>(blk) * a.num_kv_heads + h;
-  uint8_t *codes = (which ? a.v_codes : a.k_codes) + page * kPage * D;
   const int run = (sl % 16) / 4, spos = (sl / 16) * 4 + sl % 4;
 
-  // ---- this thread's 16 source values (zeros for slots outside the chunk)
+  // ---- this thread's 16 source values (zeros for slots outside the chunk); the page's block
+  // id is read after these loads are issued, so its latency overlaps theirs
   float x[16];
   if (mine) {
     const void *src = which ? a.v_new : a.k_new;
@@ -121,6 +145,10 @@ __global__ __launch_bounds__(kPage * D / 16) void append_page_kernel(AppendArgs 
 #pragma unroll
     for (int e = 0; e < 16; ++e) x[e] = 0.0f;
   }
+  const int blk = a.block_table[static_cast<long>(b) * a.max_blocks + pg];
+  if (blk < 0 || blk >= a.num_blocks) return;  // uniform per workgroup
+  const size_t page = static_cast<size_t>(blk) * a.num_kv_heads + h;
+  uint8_t *codes = (which ? a.v_codes : a.k_codes) + page * kPage * D;
   if constexpr (FMT == 4) {  // BF16: no quantization, the INT8 element order at two bytes each
     uint32_t hw[8];
 #pragma unroll
@@ -175,11 +203,11 @@ __global__ __launch_bounds__(kPage * D / 16) void append_page_kernel(AppendArgs 
     amax = fmaxf(amax, __shfl_xor(amax, 1));
     const _Float16 s16 = static_cast<_Float16>(amax / 7.0f);
     const float sc = static_cast<float>(s16);
+    if (sc != 0.0f) {
+      rint_quotients<7>(x, sc, c, 0xFu);
+    } else {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float r = 0.0f;
-      if (sc != 0.0f) r = fminf(fmaxf(rintf(x[e] / sc), -7.0f), 7.0f);
-      c[e] = static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFu;
+      for (int e = 0; e < 16; ++e) c[e] = 0u;
     }
     if (mine && (c16 & 1) == 0)
       static_cast<_Float16 *>(a.v_scales)[page * (kPage * D / 32) + (run * (D / 32) + c16 / 2) * 16 + spos] = s16;
@@ -188,15 +216,14 @@ __global__ __launch_bounds__(kPage * D / 16) void append_page_kernel(AppendArgs 
     amax = fmaxf(amax, __shfl_xor(amax, 2));
     const _Float16 s16 = static_cast<_Float16>(amax / 127.0f);
     const float sc = static_cast<float>(s16);
+    if constexpr (FMT == 3) {  // rk4v4 key: the level index
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      if constexpr (FMT == 3) {  // rk4v4 key: the level index
-        c[e] = rk4_index(sc != 0.0f ? x[e] / sc : 0.0f);
-      } else {
-        float r = 0.0f;
-        if (sc != 0.0f) r = fminf(fmaxf(rintf(x[e] / sc), -127.0f), 127.0f);
-        c[e] = static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu;
-      }
+      for (int e = 0; e < 16; ++e) c[e] = rk4_index(sc != 0.0f ? x[e] / sc : 0.0f);
+    } else if (sc != 0.0f) {
+      rint_quotients<127>(x, sc, c, 0xFFu);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) c[e] = 0u;
     }
     if (mine && (c16 & 3) == 0) {
       const int g = c16 / 4;

@@ -75,14 +75,18 @@ def test_small_shapes(K, name):
     check(K, w, chunk=100)
 
 
-def _sample_rows(w, n_per_seq):
+def _sample_rows(w, n_per_kv=1):
+    """Output rows (b, t, h) for every sequence b and every query row t, with n_per_kv query
+    heads drawn from the group of each KV head, so every KV head of every row is compared."""
     s = w.shape
+    G = s.Hq // s.Hkv
     g = np.random.default_rng(7)
     rows = []
     for b in range(s.B):
-        for t in sorted({0, s.T - 1}):
-            hs = g.choice(s.Hq, size=min(n_per_seq, s.Hq), replace=False)
-            rows += [(b * s.T + t) * s.Hq + int(h) for h in hs]
+        for t in range(s.T):
+            for kvh in range(s.Hkv):
+                hs = kvh * G + g.choice(G, size=min(n_per_kv, G), replace=False)
+                rows += [(b * s.T + t) * s.Hq + int(h) for h in hs]
     return np.array(sorted(set(rows)), np.int32)
 
 
@@ -92,7 +96,7 @@ def test_qwen32k_full(K):
 
 def test_mtp128k_sampled(K):
     w = S.make("mtp128k")
-    check(K, w, rows=_sample_rows(w, 3))
+    check(K, w, rows=_sample_rows(w, 2))
 
 
 def test_cohort_c8_sampled(K):
@@ -338,7 +342,7 @@ def test_many_sequences(K, name):
     n_splits, _ = K.num_splits(shp.B, shp.T, shp.Hq, shp.Hkv, shp.D, max(shp.lens))
     assert n_splits == 1
     w = S.make(shp, seed=S.seed_of("tiny") + 500 + list(MANY).index(name))
-    rows = _sample_rows(w, 2)  # two heads of the first and last row of every sequence
+    rows = _sample_rows(w, 1)  # one head per KV head of every row of every sequence
     check(K, w, rows=rows)
     _fused_check(K, w, rows=rows)
 

@@ -48,7 +48,7 @@ def test_rk8v4_prefill(K):
 
 def test_rk8v4_mtp128k_sampled(K):
     w = S.make("mtp128k_rk8v4")
-    check(K, w, rows=_sample_rows(w, 3), chunk=65536)
+    check(K, w, rows=_sample_rows(w, 2), chunk=65536)
 
 
 def test_rk8v4_single_row_appends_share_nibble_words(K):

@@ -23,7 +23,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   rest /= a.num_kv_heads;
   const int t = static_cast<int>(rest % a.n_new);
   const int b = static_cast<int>(rest / a.n_new);
-  const long pos = static_cast<long>(a.start_pos[b]) + t;
+  const long L0 = a.start_pos[b];
+  if (a.start_back > 0 && (L0 < a.start_back || L0 > a.max_len || L0 > static_cast<long>(a.max_blocks) * kPage))
+    return;
+  const long pos = L0 - a.start_back + t;
   if (pos < 0 || pos >= static_cast<long>(a.max_blocks) * kPage) return;
   const int blk = a.block_table[static_cast<long>(b) * a.max_blocks + pos / kPage];
   if (blk < 0 || blk >= a.num_blocks) return;
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(kPage * D / 16) void append_page_kernel(AppendArgs 
   __shared__ __align__(16) uint8_t vstage[kPage * D * (FMT == 4 ? 2 : 1)];  // V codes, row-major [slot][dim]
   const int tid = threadIdx.x, sl = tid / NC, c16 = tid % NC;
   const int h = blockIdx.y, which = blockIdx.z & 1, b = blockIdx.z >> 1;
-  const long pos0 = a.start_pos[b];
+  const long pos0 = static_cast<long>(a.start_pos[b]) - a.start_back;
   if (pos0 < 0) return;
   const long pos_end = pos0 + a.n_new;           // exclusive
   const long pg = pos0 / kPage + blockIdx.x;

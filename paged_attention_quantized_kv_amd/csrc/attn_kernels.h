@@ -579,6 +579,8 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     aa.v_scales = const_cast<void *>(a.v_scales);
     aa.block_table = a.block_table;
     aa.start_pos = nullptr;
+    aa.start_back = 0;
+    aa.max_len = 0;
     aa.num_seqs = a.num_seqs;
     aa.n_new = a.T;
     aa.num_kv_heads = a.num_kv_heads;

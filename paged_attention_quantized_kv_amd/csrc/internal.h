@@ -16,6 +16,9 @@ struct AppendArgs {
   void *k_scales, *v_scales;
   const int32_t *block_table;
   const int32_t *start_pos;
+  int32_t start_back;  // sequence b's rows go to positions start_pos[b] - start_back + t
+  int32_t max_len;     // start_back > 0 (start_pos = lengths): a length outside [start_back,
+                       // min(max_len, max_blocks * 64)] skips the sequence, as the fused step does
   int32_t num_seqs, n_new, num_kv_heads, max_blocks, num_blocks;
 };
 

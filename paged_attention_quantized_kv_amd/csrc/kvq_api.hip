@@ -75,6 +75,29 @@ int attn_call(Phase phase, const kvq_cache_t *cache, const void *q, int32_t q_dt
   a.qk_scale_log2 = softmax_scale * 1.4426950408889634f;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // The step's rows are quantized inside the split launch, except for the rotated formats with
+  // more than 16 query rows per KV head, whose fused instance runs out of registers (the 4-bit
+  // row quantizer beside two row tiles) and is slower than the row kernel launched first.
+  if (k_new && (cache->format == KVQ_RK8V4 || cache->format == KVQ_RK4V4) && s.rows > 16) {
+    kvq::AppendArgs ap;
+    ap.k_new = k_new;
+    ap.v_new = v_new;
+    ap.k_codes = static_cast<uint8_t *>(cache->k_codes);
+    ap.v_codes = static_cast<uint8_t *>(cache->v_codes);
+    ap.k_scales = cache->k_scales;
+    ap.v_scales = cache->v_scales;
+    ap.block_table = block_table;
+    ap.start_pos = seq_lens;  // positions seq_lens[b] - T + t
+    ap.start_back = T;
+    ap.max_len = max_seq_len;
+    ap.num_seqs = num_seqs;
+    ap.n_new = T;
+    ap.num_kv_heads = cache->num_kv_heads;
+    ap.max_blocks = max_blocks_per_seq;
+    ap.num_blocks = cache->num_blocks;
+    if (kvq::launch_append(cache->format, cache->head_dim, q_dtype, ap, st) != hipSuccess) return KVQ_ERR_LAUNCH;
+    a.k_new = a.v_new = nullptr;
+  }
   if (phase != Phase::kMerge) {
     if (kvq::launch_attn_split(cache->format, cache->head_dim, q_dtype, a, st) != hipSuccess) return KVQ_ERR_LAUNCH;
   }
@@ -167,6 +190,8 @@ int kv_append_quant(const kvq_cache_t *cache, const void *k_new, const void *v_n
   a.v_scales = cache->v_scales;
   a.block_table = block_table;
   a.start_pos = start_pos;
+  a.start_back = 0;
+  a.max_len = 0;
   a.num_seqs = num_seqs;
   a.n_new = n_new;
   a.num_kv_heads = cache->num_kv_heads;

@@ -74,3 +74,39 @@ def test_rk8v4_single_row_appends_share_nibble_words(K):
     mism = H.pool_equal(cache, pool)
     say(f"[rk8v4 rows] mismatches {mism}")
     assert mism == {"k_codes": 0, "v_codes": 0, "k_scales": 0, "v_scales": 0}, mism
+
+
+@pytest.mark.parametrize("fmt", [RK, S.FMT_RK4V4, S.FMT_INT8_G64])
+def test_step_skips_sequences_with_bad_lengths(K, fmt):
+    """paged_decode_step with one sequence longer than max_seq_len: that sequence's new rows
+    are not written and its output rows are NaN; the other sequences' rows land exactly
+    where kv_append_quant puts them.  With 24 query rows per KV head the rotated formats
+    append through a separate launch first, INT8 inside the split launch: same outcome."""
+    w = S.make(S.tiny_shape(B=3, T=4, Hq=24, Hkv=4, D=256, lens=(300, 500, 200), src=S.SRC_BF16, fmt=fmt,
+                            outliers=True), seed=S.seed_of("tiny") + 790 + fmt)
+    s = w.shape
+    bt = torch.from_numpy(w.block_table).to(DEV)
+    caches = [H.new_cache(K, w, DEV), H.new_cache(K, w, DEV)]
+    for cache in caches:  # every context row but the T new ones
+        for b in range(s.B):
+            L = int(w.seq_lens[b])
+            k = H.src_tensor(w.rows("k", b, 0, L - s.T), s.src, DEV)
+            v = H.src_tensor(w.rows("v", b, 0, L - s.T), s.src, DEV)
+            K.kv_append_quant(cache, k, v, bt[b:b + 1].contiguous(), torch.tensor([0], dtype=torch.int32, device=DEV))
+    kn = H.src_tensor(w.new_rows("k"), s.src, DEV)
+    vn = H.src_tensor(w.new_rows("v"), s.src, DEV)
+    # reference pool: the new rows of sequences 0 and 1 only, through kv_append_quant
+    sp = torch.from_numpy(w.seq_lens[:2] - s.T).to(DEV)
+    K.kv_append_quant(caches[1], kn[:2].contiguous(), vn[:2].contiguous(), bt[:2].contiguous(), sp)
+    q = H.src_tensor(w.q, s.src, DEV)
+    sl = torch.from_numpy(w.seq_lens).to(DEV)
+    sl[2] = w.max_seq_len + 5  # beyond max_seq_len: the sequence is skipped
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    ws = K.alloc_workspace(caches[0], s.B, s.T, s.Hq, w.max_seq_len, device=DEV)
+    K.paged_decode_step(caches[0], kn, vn, q, bt, sl, w.max_seq_len, w.softmax_scale, out, ws)
+    torch.cuda.synchronize()
+    say(f"[step bad length] fmt={fmt}")
+    for a, b in zip(caches[0].tensors(), caches[1].tensors()):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    assert torch.isnan(out[2]).all()
+    assert torch.isfinite(out[:2]).all()

@@ -94,11 +94,12 @@ def test_prefill_t_le_8_matches_decode(K):
     bt = H.fill_gpu(K, w, cache, DEV)
     dec = H.run_attn(K, w, cache, bt, DEV)
     pre = H.run_attn(K, w, cache, bt, DEV, prefill=True)
-    # the two kernels sum in different orders (chunks, wave ownership): agreement well inside the
-    # 2e-3 bar each holds against the oracle
+    # the two kernels sum in different orders (chunks, wave ownership); both are deterministic,
+    # and on this seeded case they differ by 7.6e-6 at most: the bound leaves 4x room for a
+    # change of summation order, far inside the 2e-3 bar each holds against the oracle
     diff = float((dec - pre).abs().max())
     say(f"[prefill vs decode] T=4 max-abs difference {diff:.3e}")
-    assert diff <= 1e-4
+    assert diff <= 3e-5
 
 
 def test_prefill_repeat_is_bit_identical(K):

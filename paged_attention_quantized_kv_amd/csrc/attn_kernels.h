@@ -210,12 +210,12 @@ constexpr int kWeightExp = 15 - static_cast<int>(kLazy);  // 7
 constexpr int kVexpMax = 14, kVexpMin = -16;               // E range of fp16 scales (2^E is an f16)
 constexpr int kFp8ExpMax = 30, kFp8ExpMin = -60;           // E range of fp32 scales
 
-// The largest of the finite non-negative fp16 scales packed in n words, as fp16 bits (low half)
-// in every lane: a three-input tree over the words (IEEE maximum: the scales are
-// finite, the poison of unwritten slots is zeroed before), the two halves, then the four
-// 16-lane groups of the wave (non-negative IEEE values order like their bit patterns).
+// The largest of the finite non-negative fp16 scales packed in N words of this lane, as fp16
+// bits in the low half (the high half zero): a three-input tree over the words (IEEE
+// maximum: the scales are finite, the poison of unwritten slots is zeroed before), then
+// the two halves.
 template <int N>
-__device__ inline uint32_t max_f16_scales(const uint32_t (&w)[N]) {
+__device__ inline uint32_t lane_max_f16_scales(const uint32_t (&w)[N]) {
   f16x2 t[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) t[i] = __builtin_bit_cast(f16x2, w[i]);
@@ -237,18 +237,12 @@ __device__ inline uint32_t max_f16_scales(const uint32_t (&w)[N]) {
     }
   }
   const f16x2 x = __builtin_elementwise_maximum(t[0], f16x2{t[0][1], t[0][0]});
-  // across the lane groups as 32-bit integers (the fp16 bits zero-extended): hipcc 7.2 drops a
-  // packed 16-bit max of the two results of a lane swap, a 32-bit max it keeps
-  uint32_t u = __builtin_bit_cast(uint32_t, x) & 0xFFFFu;
-  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  u = max(r[0], r[1]);
-  r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return max(r[0], r[1]);
+  return __builtin_bit_cast(uint32_t, x) & 0xFFFFu;
 }
 
-// The same for non-negative fp32 scales: the largest as fp32 bits in every lane.
+// The same for non-negative fp32 scales: this lane's largest as fp32 bits.
 template <int N>
-__device__ inline uint32_t max_f32_scales(const uint32_t (&w)[N]) {
+__device__ inline uint32_t lane_max_f32_scales(const uint32_t (&w)[N]) {
   uint32_t t[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) t[i] = w[i];
@@ -256,8 +250,15 @@ __device__ inline uint32_t max_f32_scales(const uint32_t (&w)[N]) {
   for (int h = 1; h < N; h <<= 1)
 #pragma unroll
     for (int i = 0; i + h < N; i += 2 * h) t[i] = max(t[i], t[i + h]);
-  auto r = __builtin_amdgcn_permlane16_swap(t[0], t[0], false, false);
-  const uint32_t u = max(r[0], r[1]);
+  return t[0];
+}
+
+// The largest u of the wave, in every lane: across the four 16-lane groups with lane swaps,
+// as 32-bit integers (non-negative IEEE values order like their bit patterns; hipcc 7.2
+// drops a packed 16-bit max of the two results of a lane swap, a 32-bit max it keeps).
+__device__ inline uint32_t wave_max_u32(uint32_t u) {
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  u = max(r[0], r[1]);
   r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return max(r[0], r[1]);
 }
@@ -273,6 +274,15 @@ __device__ inline int scale_exponent_f16(uint32_t hbits) {
 __device__ inline int scale_exponent_f32(uint32_t fbits) {
   const int e = static_cast<int>(__builtin_amdgcn_readfirstlane(fbits) >> 23) & 0xFF;  // fp32 exponent field
   return max(min(133 - e, kFp8ExpMax), kFp8ExpMin);
+}
+// The smallest scale bits whose exponent asks for an E below cur: for fp16 scales
+// E < cur <=> 14 - ef < cur <=> bits >= (15 - cur) << 10; for fp32 scales E < cur <=>
+// 133 - e < cur <=> bits >= (134 - cur) << 23 (no bits do at the bottom of the range).
+__device__ inline uint32_t lower_threshold_f16(int cur) {
+  return cur <= kVexpMin ? 0xFFFFFFFFu : static_cast<uint32_t>(15 - cur) << 10;
+}
+__device__ inline uint32_t lower_threshold_f32(int cur) {
+  return cur <= kFp8ExpMin ? 0xFFFFFFFFu : static_cast<uint32_t>(134 - cur) << 23;
 }
 
 // Query rows enter the matrix cores as f16, whose range (2^-24 .. 65504) is far narrower than
@@ -739,6 +749,10 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   constexpr bool F16PAIR = (FMT == 0 || FMT == 2 || FMT == 3);
   int vexp = (FMT == 1) ? kFp8ExpMax : kVexpMax;  // wave-uniform
   auto wexp = [&]() -> float { return F16PAIR ? static_cast<float>(kWeightExp) : (FMT == 1 ? static_cast<float>(vexp) : 0.0f); };
+  // wave-uniform companions of vexp, recomputed only when it moves: the scale bits from
+  // which a page asks for a lower exponent, and 2^vexp as two packed f16
+  uint32_t vth = (FMT == 1) ? lower_threshold_f32(vexp) : lower_threshold_f16(vexp);
+  uint32_t e2bits = f16x2_pow2(F16PAIR ? vexp : 0);
   // V scales of slots at or past L (never written: poison) -> 0, on pages that hold such slots;
   // the V-scale words of a lane group hold keys 16(2j + e/4) + 4 q4 + e%4 (e: the element of
   // word j, 8 fp16 or 4 fp32 per uint4) for every format with scales
@@ -773,6 +787,8 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   // the largest V scale of this wave's share of page pr -> lower vexp if it asks for less;
   // returns whether it did, with f the factor the accumulators (and, for FP8, the row sums)
   // must be scaled by
+  // (a vote on each lane's own largest scale against vth; the wave's largest is only
+  // taken when some scale asks for a lower exponent, about once per chunk)
   auto lower_vexp = [&](PageRegs<D, FMT> &pr, float &f) -> bool {
     constexpr int NW4 = 4 * PageRegs<D, FMT>::VSN;
     uint32_t w[NW4];
@@ -783,10 +799,15 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
       w[4 * j + 2] = pr.vs[j].z;
       w[4 * j + 3] = pr.vs[j].w;
     }
-    const int E = (FMT == 1) ? scale_exponent_f32(max_f32_scales(w)) : scale_exponent_f16(max_f16_scales(w));
-    const int cur = __builtin_amdgcn_readfirstlane(vexp);  // uniform: keep the test scalar
+    const uint32_t lm = (FMT == 1) ? lane_max_f32_scales(w) : lane_max_f16_scales(w);
+    if (!__any(lm >= vth)) return false;
+    const uint32_t wm = wave_max_u32(lm);
+    const int E = (FMT == 1) ? scale_exponent_f32(wm) : scale_exponent_f16(wm);
+    const int cur = __builtin_amdgcn_readfirstlane(vexp);
     if (E >= cur) return false;
     vexp = E;
+    vth = __builtin_amdgcn_readfirstlane((FMT == 1) ? lower_threshold_f32(E) : lower_threshold_f16(E));
+    if constexpr (F16PAIR) e2bits = __builtin_amdgcn_readfirstlane(f16x2_pow2(E));
     f = __builtin_ldexpf(1.0f, E - cur);
     return true;
   };
@@ -1156,7 +1177,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
 #pragma unroll
             for (int j = 0; j < DPW; ++j) o[nt][j] *= f;
         }
-        const f16x2 e2 = __builtin_bit_cast(f16x2, f16x2_pow2(vexp));
+        const f16x2 e2 = __builtin_bit_cast(f16x2, e2bits);
 #pragma unroll
         for (int j = 0; j < PageRegs<D, FMT>::VSN; ++j) {
           pr.vs[j].x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, pr.vs[j].x) * e2);

@@ -86,7 +86,8 @@ enum {
   KVQ_ERR_INVALID_ARG = -1, /* null / misaligned pointer, negative size, bad enum */
   KVQ_ERR_UNSUPPORTED = -2, /* shape outside the supported set above */
   KVQ_ERR_WORKSPACE = -3,   /* workspace_bytes below paged_decode_attn_workspace_bytes() */
-  KVQ_ERR_CAPACITY = -4,    /* max_seq_len (or start+n_new bound) beyond max_blocks_per_seq * 64 */
+  KVQ_ERR_CAPACITY = -4,    /* max_seq_len (or start+n_new bound) beyond max_blocks_per_seq * 64;
+                               kvq_capacity_check states the shortfall in bytes */
   KVQ_ERR_LAUNCH = -5       /* the HIP runtime refused a launch (no device, bad stream, ...) */
 };
 
@@ -322,6 +323,33 @@ const char *kvq_status_string(int status);
  * returns 0 for an unsupported shape. */
 int32_t paged_decode_attn_num_splits(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_heads,
                                      int32_t head_dim, int32_t max_seq_len, int32_t *tokens_per_split);
+
+/*
+ * Capacity planning, host only (nothing is enqueued).  The engine the pages describe
+ * refuses a context that does not fit its pool at startup, stating the shortfall to
+ * the byte (NInfer-4090 README, "The tradeoff").  Here the caller owns the pool and
+ * the block table, so the check takes the planned context lengths and reports what
+ * is missing from either.
+ *
+ * kvq_page_bytes: the pool bytes one page (64 token slots of one KV head) takes in
+ * `format` at head_dim, over the four arrays of kvq_cache_t (codes and scales, in the
+ * layout above); 0 for an unsupported format or head_dim.
+ *
+ * kvq_capacity_check: context_lens [num_seqs] int32 in HOST memory, the lengths each
+ * sequence will reach.  Sequence b needs ceil(context_lens[b] / 64) blocks, each
+ * holding one page per KV head.  *deficit_bytes (host, always written) receives
+ *   max(0, sum of blocks - cache->num_blocks) * num_kv_heads * kvq_page_bytes
+ *     (pool bytes missing)
+ * + max(0, max_b blocks_b - max_blocks_per_seq) * num_seqs * 4
+ *     (block-table bytes missing: the [num_seqs][max_blocks_per_seq] int32 table must widen),
+ * saturated at INT64_MAX.
+ * Returns KVQ_OK when it is 0, KVQ_ERR_CAPACITY otherwise; KVQ_ERR_INVALID_ARG for a bad
+ * descriptor, a negative length or null pointers; KVQ_ERR_UNSUPPORTED for a length
+ * beyond 2^30 or more than 2^20 sequences.
+ */
+size_t kvq_page_bytes(int32_t format, int32_t head_dim);
+int kvq_capacity_check(const kvq_cache_t *cache, int32_t num_seqs, const int32_t *context_lens,
+                       int32_t max_blocks_per_seq, int64_t *deficit_bytes);
 
 #ifdef __cplusplus
 }

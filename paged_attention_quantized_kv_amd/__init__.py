@@ -10,6 +10,7 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,7 +29,8 @@ PAGE = 64
 _EXPORTS = ("kv_append_quant", "paged_decode_attn", "paged_decode_attn_split", "paged_decode_attn_merge",
             "paged_decode_step", "paged_decode_attn_workspace_bytes", "paged_decode_attn_num_splits",
             "paged_prefill_attn", "paged_prefill_attn_workspace_bytes", "kvq_check_tables", "kvq_status_string",
-            "paged_decode_attn_noalloc", "paged_decode_attn_noalloc_max_bytes")
+            "paged_decode_attn_noalloc", "paged_decode_attn_noalloc_max_bytes", "kvq_page_bytes",
+            "kvq_capacity_check")
 
 
 class KvqError(RuntimeError):
@@ -75,10 +77,33 @@ def _load():
     L.kvq_check_tables.restype = C.c_int
     L.kvq_status_string.argtypes = [C.c_int]
     L.kvq_status_string.restype = C.c_char_p
+    L.kvq_page_bytes.argtypes = [i32, i32]
+    L.kvq_page_bytes.restype = C.c_size_t
+    L.kvq_capacity_check.argtypes = [P, i32, vp, i32, C.POINTER(C.c_int64)]
+    L.kvq_capacity_check.restype = C.c_int
     return L
 
 
 lib = _load()
+
+
+def page_bytes(fmt: int, head_dim: int) -> int:
+    """Pool bytes one page (64 slots of one KV head) takes in the format (kvq_page_bytes)."""
+    return int(lib.kvq_page_bytes(fmt, head_dim))
+
+
+def capacity_check(cache, context_lens, max_blocks_per_seq: int) -> int:
+    """Host-side capacity plan (kvq_capacity_check): the bytes the pool and block table lack
+    for sequences reaching context_lens (0 when they fit).  `cache` may be a Cache or a
+    CacheDesc (only its shape fields are read)."""
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    deficit = C.c_int64(0)
+    desc = cache.desc if isinstance(cache, Cache) else C.byref(cache)
+    rc = lib.kvq_capacity_check(desc, int(lens.size), lens.ctypes.data_as(C.c_void_p), int(max_blocks_per_seq),
+                                C.byref(deficit))
+    if rc not in (0, -4):
+        raise KvqError(rc, status_string(rc))
+    return int(deficit.value)
 
 
 def status_string(status: int) -> str:

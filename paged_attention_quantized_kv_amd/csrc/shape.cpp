@@ -96,4 +96,51 @@ int prefill_shape(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_
   return KVQ_OK;
 }
 
+// Pool bytes of one page (64 slots of one KV head) over the four arrays of the layout.
+size_t page_bytes(int32_t format, int32_t head_dim) {
+  if (head_dim != 128 && head_dim != 256) return 0;
+  const size_t d = static_cast<size_t>(head_dim), n = kPage;
+  switch (format) {
+    case KVQ_INT8_G64: return n * (2 * d + 2 * 2 * (d / 64));                   // codes, fp16 group-64 scales
+    case KVQ_FP8_E4M3_ROW: return n * (2 * d + 2 * 4);                          // codes, fp32 row scales
+    case KVQ_RK8V4: return n * (d + d / 2 + 2 * (d / 64) + 2 * (d / 32));       // int8 K, 4-bit V
+    case KVQ_RK4V4: return n * (d / 2 + d / 2 + 2 * (d / 64) + 2 * (d / 32));   // 4-bit K and V
+    case KVQ_BF16_KV: return n * 2 * 2 * d;                                     // bf16 K and V, no scales
+    default: return 0;
+  }
+}
+
+int capacity_check(const kvq_cache_t *c, int32_t num_seqs, const int32_t *lens, int32_t max_blocks_per_seq,
+                   int64_t *deficit) {
+  if (!deficit) return KVQ_ERR_INVALID_ARG;
+  *deficit = 0;
+  const int rc = check_cache(c);
+  if (rc) return rc;
+  if (num_seqs < 1 || !lens || max_blocks_per_seq < 1) return KVQ_ERR_INVALID_ARG;
+  if (num_seqs > (1 << 20)) return KVQ_ERR_UNSUPPORTED;
+  long long blocks = 0, widest = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    if (lens[b] < 0) return KVQ_ERR_INVALID_ARG;
+    if (lens[b] > kMaxSeqLen) return KVQ_ERR_UNSUPPORTED;
+    const long long pg = (static_cast<long long>(lens[b]) + kPage - 1) / kPage;
+    blocks += pg;
+    if (pg > widest) widest = pg;
+  }
+  const long long pool_short = blocks > c->num_blocks ? blocks - c->num_blocks : 0;
+  const long long table_short = widest > max_blocks_per_seq ? widest - max_blocks_per_seq : 0;
+  // in 128 bits (2^20 sequences of 2^24 pages over 2^31 heads exceed 64), saturated
+  const __int128 d = static_cast<__int128>(pool_short) * c->num_kv_heads * page_bytes(c->format, c->head_dim) +
+                     static_cast<__int128>(table_short) * num_seqs * 4;
+  *deficit = d > static_cast<__int128>(INT64_MAX) ? INT64_MAX : static_cast<int64_t>(d);
+  return *deficit == 0 ? KVQ_OK : KVQ_ERR_CAPACITY;
+}
+
 }  // namespace kvq
+
+extern "C" {
+size_t kvq_page_bytes(int32_t format, int32_t head_dim) { return kvq::page_bytes(format, head_dim); }
+int kvq_capacity_check(const kvq_cache_t *cache, int32_t num_seqs, const int32_t *context_lens,
+                       int32_t max_blocks_per_seq, int64_t *deficit_bytes) {
+  return kvq::capacity_check(cache, num_seqs, context_lens, max_blocks_per_seq, deficit_bytes);
+}
+}

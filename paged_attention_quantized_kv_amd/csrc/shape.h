@@ -68,4 +68,9 @@ struct PrefillShape {
 int prefill_shape(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                   int32_t max_seq_len, int block_rows, PrefillShape *s);
 
+// Capacity planning (kvq_page_bytes, kvq_capacity_check in kvq.h).
+size_t page_bytes(int32_t format, int32_t head_dim);
+int capacity_check(const kvq_cache_t *c, int32_t num_seqs, const int32_t *lens, int32_t max_blocks_per_seq,
+                   int64_t *deficit);
+
 }  // namespace kvq

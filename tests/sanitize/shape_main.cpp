@@ -90,6 +90,28 @@ int main() {
     CHECK(kvq::prefill_shape(1, 1, 8, 1, 128, kvq::kMaxSeqLen + 1, 64, &p) == KVQ_ERR_UNSUPPORTED);
   }
   CHECK(kvq::balanced_slots(32, 8, INT_MAX) > kvq::kTargetWgs);
+  // capacity planning over extreme lengths and pool sizes
+  {
+    int64_t deficit = -1;
+    std::vector<int32_t> lens = {0, 1, 64, 65, kvq::kMaxSeqLen, INT_MAX, -1};
+    for (int fmt = 0; fmt <= 5; ++fmt)
+      for (int D : {64, 128, 256}) CHECK(kvq::page_bytes(fmt, D) % 64 == 0);
+    for (int32_t nblk : {1, 1000, INT_MAX}) {
+      kvq_cache_t cc = c;
+      cc.num_blocks = nblk;
+      cc.num_kv_heads = 65535;
+      for (size_t i = 0; i < lens.size(); ++i) {
+        const int rc = kvq::capacity_check(&cc, 1, &lens[i], 1, &deficit);
+        CHECK(rc == KVQ_OK || rc == KVQ_ERR_CAPACITY || rc == KVQ_ERR_INVALID_ARG || rc == KVQ_ERR_UNSUPPORTED);
+        CHECK(deficit >= 0);
+      }
+      std::vector<int32_t> many(1 << 12, kvq::kMaxSeqLen);
+      const int rc = kvq::capacity_check(&cc, static_cast<int32_t>(many.size()), many.data(), INT_MAX, &deficit);
+      CHECK((rc == KVQ_OK) == (deficit == 0) && deficit >= 0);
+    }
+    CHECK(kvq::capacity_check(&c, 1, nullptr, 1, &deficit) == KVQ_ERR_INVALID_ARG);
+    CHECK(kvq::capacity_check(&c, 1, &lens[0], 1, nullptr) == KVQ_ERR_INVALID_ARG);
+  }
   printf("shape logic: %ld supported shapes checked, %d failures\n", supported, fails);
   if (fails == 0) printf("shape ok\n");
   return fails == 0 ? 0 : 1;

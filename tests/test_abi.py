@@ -197,3 +197,47 @@ def test_noalloc_validation(K):
     assert call(d, B=8, T=4, Hq=32, L=big) == -3
     assert call(None) == -1
     assert call(d) == -5  # valid shape, no device here
+
+
+def test_page_bytes_match_the_format_table(K):
+    """kvq_page_bytes against the pages' bytes-per-token table (NInfer-3090 README, "Choosing
+    a KV format"; 16 layers x 4 KV heads at head_dim 256): a page is 64 tokens of one KV head
+    of one layer.  FP8 follows this library's layout (fp32 row scales: 8 bytes per token per
+    head where the table's total implies 4), and 0 marks an unsupported format or head_dim."""
+    table = {}
+    for line in open(os.path.join(ROOT, "tests", "golden", "kv_format_table.txt")):
+        f = line.split()
+        if f and not line.startswith("#") and f[0] in ("bf16", "int8", "fp8", "rk8v4", "rk4v4"):
+            table[f[0]] = int(f[1])
+    per_head_layer = {k: v // (16 * 4) for k, v in table.items()}
+    assert K.page_bytes(K.INT8_G64, 256) == 64 * per_head_layer["int8"]
+    assert K.page_bytes(K.RK8V4, 256) == 64 * per_head_layer["rk8v4"]
+    assert K.page_bytes(K.RK4V4, 256) == 64 * per_head_layer["rk4v4"]
+    assert K.page_bytes(K.BF16_KV, 256) == 64 * per_head_layer["bf16"]
+    assert K.page_bytes(K.FP8_E4M3_ROW, 256) == 64 * (2 * 256 + 2 * 4)
+    assert K.page_bytes(K.INT8_G64, 128) == 64 * (2 * 128 + 2 * 2 * 2)
+    assert K.page_bytes(K.INT8_G64, 64) == 0 and K.page_bytes(7, 256) == 0
+
+
+def test_capacity_check_states_the_exact_deficit(K):
+    """A pool of 100 blocks (4 KV heads, INT8, head_dim 256) and a 40-entry block table."""
+    d = _desc(K, fmt=K.INT8_G64, D=256, H=4, nblk=100)
+    page = K.page_bytes(K.INT8_G64, 256)
+    assert K.capacity_check(d, [64 * 40, 64 * 60], 60) == 0            # 100 blocks exactly
+    assert K.capacity_check(d, [64 * 40, 64 * 60 + 1], 61) == 4 * page  # one block more: 4 pages
+    assert K.capacity_check(d, [64 * 40, 64 * 60], 40) == 20 * 2 * 4   # rows 20 entries short
+    assert K.capacity_check(d, [0, 1, 63, 64], 1) == 0
+    # a 41-page sequence: the pool fits (41 + 40 blocks) but every table row needs one more entry
+    assert K.capacity_check(d, [64 * 41, 64 * 40], 40) == 2 * 4
+    # both short: 3 blocks and 5 table entries per row for 3 sequences
+    assert K.capacity_check(d, [64 * 45, 64 * 29, 64 * 29], 40) == 3 * 4 * page + 5 * 3 * 4
+    out = C.c_int64(-1)
+    lens = (C.c_int32 * 2)(64 * 40, 64 * 61)
+    assert K.lib.kvq_capacity_check(C.byref(d), 2, lens, 61, C.byref(out)) == -4 and out.value == 4 * page
+    assert K.lib.kvq_capacity_check(C.byref(d), 2, lens, 40, None) == -1
+    assert K.lib.kvq_capacity_check(C.byref(d), 0, lens, 40, C.byref(out)) == -1 and out.value == 0
+    bad = (C.c_int32 * 1)(-1)
+    assert K.lib.kvq_capacity_check(C.byref(d), 1, bad, 40, C.byref(out)) == -1
+    big = (C.c_int32 * 1)((1 << 30) + 1)
+    assert K.lib.kvq_capacity_check(C.byref(d), 1, big, 40, C.byref(out)) == -2
+    assert K.lib.kvq_capacity_check(C.byref(_desc(K, fmt=9)), 1, lens, 40, C.byref(out)) == -1

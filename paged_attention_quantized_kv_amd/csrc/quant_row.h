@@ -20,21 +20,17 @@ __device__ inline float load_src<1>(const void *p, size_t i) {  // bf16: exact w
 
 // OCP FP8 E4M3FN of v, round to nearest even, magnitudes >= 448 saturate to
 // 448, NaN -> 0x7F, sign kept (a negative value that rounds to zero -> 0x80).
+// One branch-free form covers every range: with e = max(exponent of |v|, -6), the code
+// is (e + 7) * 8 - 8 + rint(|v| * 2^(3 - e)), the significand in eighths for the normal
+// codes and |v| in units of 2^-9 (the subnormal spacing) below 2^-6; a rounding that
+// carries into the next binade lands on that binade's first code, and the minimum with
+// 126 (448) saturates, infinities included.  The sum is exact below 2^24.
 __device__ inline uint32_t e4m3fn_rne_sat(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const uint32_t u = __float_as_uint(v), sign = (u >> 24) & 0x80u;
   const float ax = fabsf(v);
-  if (!(ax == ax)) return 0x7Fu;
-  uint32_t code;
-  if (ax >= 448.0f) {
-    code = 0x7Eu;
-  } else if (ax < 0.015625f) {  // below 2^-6: subnormals, multiples of 2^-9
-    code = static_cast<uint32_t>(rintf(ax * 512.0f));  // 8 lands on 2^-6 = code 0x08
-  } else {
-    const int e = static_cast<int>((__float_as_uint(ax) >> 23) & 0xFFu) - 127;  // -6..8
-    const float r = rintf(ldexpf(ax, 3 - e));  // significand * 8 in [8, 16]
-    code = static_cast<uint32_t>((e + 7) * 8) + static_cast<uint32_t>(r) - 8u;  // r == 16 carries
-  }
-  return sign | code;
+  const int e = max(static_cast<int>((u >> 23) & 0xFFu) - 127, -6);
+  const float code = fminf(static_cast<float>((e + 7) * 8 - 8) + rintf(ldexpf(ax, 3 - e)), 126.0f);
+  return (ax == ax) ? (sign | static_cast<uint32_t>(code)) : 0x7Fu;
 }
 
 // rk8v4 keys: the 64-dim groups of a key row are rotated by H64/8 (Sylvester-order

@@ -1332,18 +1332,22 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   }
 }
 
-// Merge kernel: one wave per 64-dim slice of an output row (b, t, h).  Lane l holds
-// float4 column l % 16 of the slice for the chunks s = l / 16 + 4k, with each chunk's
-// maximum and sum; every load is issued at once, beside the sequence length.  All
-// n_splits chunk slots lie in the workspace; slots past the chunks that hold the row's
-// keys carry stale values and are dropped by selection.  The log-sum-exp weights and
-// the sums over the four chunk groups use cross-lane swaps only (no LDS, no barrier),
-// in a fixed order (deterministic).
-template <int D>
-__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
-  constexpr int NQ = D / 64;  // 64-dim slices of a row, one wave each
-  constexpr int MPER = 16;    // chunks per lane held in registers (all of them up to 64 chunks)
-  const int row = blockIdx.x / NQ, qs = blockIdx.x % NQ, lane = threadIdx.x;
+// Merge kernel: MW waves per 64-dim slice of an output row (b, t, h).  Lane l of wave w
+// holds float4 column l % 16 of the slice for the chunks s = 64 w + l / 16 + 4k (k < 16),
+// with each chunk's maximum and sum; every load is issued at once, beside the sequence
+// length.  Chunks beyond the first 64 MW come in further batches of 64 per wave, each
+// batch issued at once.  All n_splits chunk slots lie in the workspace; slots past the
+// chunks that hold the row's keys carry stale values and are dropped by selection.  The
+// log-sum-exp weights and the sums over a wave's four chunk groups use cross-lane swaps;
+// with MW > 1 the waves' maxima and sums meet in LDS, summed in wave order.  The order is
+// fixed for a given MW (deterministic).  MW = 1 (no LDS, no barrier) serves calls of at
+// most 64 chunks per (sequence, KV head), and balanced calls whatever their counts.
+template <int D, int MW>
+__global__ __launch_bounds__(64 * MW) void attn_merge_kernel(AttnArgs a) {
+  constexpr int NQ = D / 64;       // 64-dim slices of a row
+  constexpr int MPER = 16;         // chunks per lane and batch, held in registers
+  constexpr int BATCH = 4 * MPER;  // chunks per wave and batch
+  const int row = blockIdx.x / NQ, qs = blockIdx.x % NQ, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int h = row % a.num_q_heads, t = (row / a.num_q_heads) % a.T, b = row / (a.num_q_heads * a.T);
   float *dst = a.out + static_cast<size_t>(row) * D + 64 * qs;
   const int kvh = h / a.group, r = t * a.group + h % a.group;
@@ -1363,13 +1367,13 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
   float2 ml[MPER];
 #pragma unroll
   for (int k = 0; k < MPER; ++k) {
-    const int s = min(sg + 4 * k, nsl - 1);
+    const int s = min(BATCH * w + sg + 4 * k, nsl - 1);
     x[k] = o_at(s);
     ml[k] = ml2[(part0 + s) * a.rows + r];
   }
   const int L = a.seq_lens[b];
-  if (L < a.T || L > a.max_seq_len || L > static_cast<long>(a.max_blocks) * kPage) {
-    dst[lane] = NAN;
+  if (L < a.T || L > a.max_seq_len || L > static_cast<long>(a.max_blocks) * kPage) {  // uniform per workgroup
+    if (w == 0) dst[lane] = NAN;
     return;
   }
   // chunks holding keys this row sees (later chunks were skipped or hold none of them)
@@ -1377,29 +1381,73 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
   float mloc = -INFINITY;
 #pragma unroll
   for (int k = 0; k < MPER; ++k)
-    if (sg + 4 * k < ns) mloc = fmaxf(mloc, ml[k].x);
-  for (int s = sg + 4 * MPER; s < ns; s += 4) mloc = fmaxf(mloc, ml2[(part0 + s) * a.rows + r].x);
-  const float M = max_xor32(max_xor16(mloc));
+    if (BATCH * w + sg + 4 * k < ns) mloc = fmaxf(mloc, ml[k].x);
+  // later batches (few KV heads, long contexts): one memory latency per batch, not per chunk
+  for (int s0 = BATCH * (w + MW); s0 < ns; s0 += BATCH * MW) {
+    float mb[MPER];
+#pragma unroll
+    for (int k = 0; k < MPER; ++k) mb[k] = ml2[(part0 + min(s0 + sg + 4 * k, ns - 1)) * a.rows + r].x;
+#pragma unroll
+    for (int k = 0; k < MPER; ++k)
+      if (s0 + sg + 4 * k < ns) mloc = fmaxf(mloc, mb[k]);
+  }
+  float M = max_xor32(max_xor16(mloc));
+  __shared__ float red_m[MW], red_l[MW];
+  __shared__ float4 red_acc[MW][16];
+  if constexpr (MW > 1) {
+    if (lane == 0) red_m[w] = M;
+    __syncthreads();
+    M = red_m[0];
+#pragma unroll
+    for (int i = 1; i < MW; ++i) M = fmaxf(M, red_m[i]);
+  }
   const float Ms = (M == -INFINITY) ? 0.0f : M;
   float4 acc = make_float4(0, 0, 0, 0);
   float lt = 0.0f;
   auto add = [&](float2 st, float4 y) {
-    const float w = exp2f(st.x - Ms);
-    lt += w * st.y;
-    acc.x += w * y.x;
-    acc.y += w * y.y;
-    acc.z += w * y.z;
-    acc.w += w * y.w;
+    const float wt = exp2f(st.x - Ms);
+    lt += wt * st.y;
+    acc.x += wt * y.x;
+    acc.y += wt * y.y;
+    acc.z += wt * y.z;
+    acc.w += wt * y.w;
   };
 #pragma unroll
   for (int k = 0; k < MPER; ++k)
-    if (sg + 4 * k < ns) add(ml[k], x[k]);
-  for (int s = sg + 4 * MPER; s < ns; s += 4) add(ml2[(part0 + s) * a.rows + r], o_at(s));  // long contexts
+    if (BATCH * w + sg + 4 * k < ns) add(ml[k], x[k]);
+  for (int s0 = BATCH * (w + MW); s0 < ns; s0 += BATCH * MW) {  // the same batches, added in chunk order
+#pragma unroll
+    for (int k = 0; k < MPER; ++k) {
+      const int s = min(s0 + sg + 4 * k, ns - 1);
+      x[k] = o_at(s);
+      ml[k] = ml2[(part0 + s) * a.rows + r];
+    }
+#pragma unroll
+    for (int k = 0; k < MPER; ++k)
+      if (s0 + sg + 4 * k < ns) add(ml[k], x[k]);
+  }
   lt = sum_xor32(sum_xor16(lt));
   acc.x = sum_xor32(sum_xor16(acc.x));
   acc.y = sum_xor32(sum_xor16(acc.y));
   acc.z = sum_xor32(sum_xor16(acc.z));
   acc.w = sum_xor32(sum_xor16(acc.w));
+  if constexpr (MW > 1) {
+    if (sg == 0) red_acc[w][c4] = acc;
+    if (lane == 0) red_l[w] = lt;
+    __syncthreads();
+    if (w != 0) return;
+    acc = red_acc[0][c4];
+    lt = red_l[0];
+#pragma unroll
+    for (int i = 1; i < MW; ++i) {
+      const float4 o = red_acc[i][c4];
+      acc.x += o.x;
+      acc.y += o.y;
+      acc.z += o.z;
+      acc.w += o.w;
+      lt += red_l[i];
+    }
+  }
   if (sg == 0) reinterpret_cast<float4 *>(dst)[c4] = make_float4(acc.x / lt, acc.y / lt, acc.z / lt, acc.w / lt);
 }
 
@@ -1912,7 +1960,17 @@ hipError_t prefill_one(const AttnArgs &a, hipStream_t s) {
 
 template <int D>
 hipError_t merge_one(const AttnArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(a.num_seqs * a.T * a.num_q_heads * (D / 64)), dim3(64), 0, s, a);
+  const dim3 grid(a.num_seqs * a.T * a.num_q_heads * (D / 64));
+  // more than 64 chunks per (sequence, KV head), as with one or two KV heads at long
+  // contexts: 2 or 4 waves per slice.  (Balanced calls rarely exceed 64; the one-wave
+  // kernel takes any count in batches.)
+  const int chunks = a.balanced ? 0 : a.n_splits;
+  if (chunks > 2 * 64)
+    hipLaunchKernelGGL((attn_merge_kernel<D, 4>), grid, dim3(256), 0, s, a);
+  else if (chunks > 64)
+    hipLaunchKernelGGL((attn_merge_kernel<D, 2>), grid, dim3(128), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<D, 1>), grid, dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -347,17 +347,27 @@ def test_many_sequences(K, name):
     _fused_check(K, w, rows=rows)
 
 
-@pytest.mark.parametrize("shp", [
-    S.tiny_shape(B=1, T=2, Hq=8, Hkv=1, D=128, lens=(20000,), src=S.SRC_F32, name="splits157_f32"),
-    S.tiny_shape(B=2, T=1, Hq=4, Hkv=1, D=128, lens=(40000, 9000), src=S.SRC_BF16, fmt=S.FMT_FP8_ROW,
-                 outliers=True, name="splits105_fp8"),
-], ids=lambda s: s.name)
-def test_merge_of_more_than_64_chunks(K, shp):
-    """One KV head and long contexts: more than 64 chunks per row, past the chunks the
-    merge holds in registers (its loop over the rest), with a short second sequence
-    whose rows stop early among them; both paths."""
+@pytest.mark.parametrize("shp,chunks", [
+    (S.tiny_shape(B=1, T=2, Hq=8, Hkv=1, D=128, lens=(20000,), src=S.SRC_F32, name="splits157_f32"), 157),
+    (S.tiny_shape(B=1, T=4, Hq=16, Hkv=2, D=256, lens=(12000,), src=S.SRC_BF16, outliers=True,
+                  name="splits94_kv2"), 94),
+    (S.tiny_shape(B=2, T=1, Hq=4, Hkv=1, D=128, lens=(40000, 9000), src=S.SRC_BF16, fmt=S.FMT_FP8_ROW,
+                  outliers=True, name="splits105_fp8"), 157),
+], ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_merge_of_more_than_64_chunks(K, shp, chunks):
+    """Few KV heads and long contexts: more than 64 chunks per (sequence, KV head).  157
+    chunks in one sequence take four merge waves per slice (the last one idle), 94 take
+    two; the balanced two-sequence call (157 chunks for its long sequence, chunk count set
+    on the device) takes the one-wave merge through three batches, and its short second
+    sequence's rows stop early among them.  Both the two-call path and the fused step."""
     n_splits, _ = K.num_splits(shp.B, shp.T, shp.Hq, shp.Hkv, shp.D, max(shp.lens))
-    assert n_splits > 64
+    if shp.B == 1:
+        assert n_splits == chunks
+    else:  # balanced: the long sequence's chunks, from the device-side rule (pages / even page count)
+        pages = [(L + 63) // 64 for L in shp.lens]
+        pp = max(2, -(-sum(pages) * shp.Hkv // 256))
+        pp += pp % 2
+        assert -(-pages[0] // pp) == chunks
     w = S.make(shp, seed=S.seed_of("tiny") + 800 + shp.B)
     check(K, w)
     _fused_check(K, w)

@@ -20,13 +20,16 @@ int check_cache(const kvq_cache_t *c) {
   return KVQ_OK;
 }
 
-// Chunking of the context: a pure function of the shape.  Pages per chunk are
-// chosen so that num_seqs * num_kv_heads * chunks is about one workgroup per
-// compute unit, rounded to whole rounds of the workgroup's teams.
+// Chunking of the context: a pure function of the shape.  Each (sequence, KV head) gets
+// as many chunks as keep all workgroups within one per compute unit (at least one), and
+// the pages are spread evenly over them, rounded to whole rounds of the workgroup's
+// teams.  Past one workgroup per compute unit a second chunk costs a second round and a
+// merge, and one chunk per (sequence, KV head) is faster even with compute units idle.
 int32_t chunk_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len) {
   const long pages = (static_cast<long>(max_seq_len) + kPage - 1) / kPage;
-  const long total = pages * num_seqs * num_kv_heads;
-  long pps = (total + kTargetWgs - 1) / kTargetWgs;
+  const long units = static_cast<long>(num_seqs) * num_kv_heads;
+  const long n = units >= kTargetWgs ? 1 : kTargetWgs / units;
+  long pps = (pages + n - 1) / n;
   pps = ((pps + kTeams - 1) / kTeams) * kTeams;
   if (pps < kTeams) pps = kTeams;
   if (pps > kMaxChunkPages) pps = kMaxChunkPages;

@@ -1,6 +1,8 @@
 // shape.cpp -- host-side shape logic (shape.h): descriptor checks, chunking, workspace sizes.
 #include "shape.h"
 
+#include <algorithm>
+
 namespace kvq {
 
 namespace {
@@ -62,10 +64,12 @@ int attn_shape(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_
   return KVQ_OK;
 }
 
-// Prefill: any number of query rows T*G per KV head, in blocks of kPrefillRows (16-row
-// tiles); the context of each (sequence, KV head, row block) is cut into as few chunks
-// as give about one workgroup per compute unit (at most kMaxPrefillChunkPages pages
-// each).  With one chunk the split kernel writes the rows itself (no merge, no partials).
+// Prefill: any number of query rows T*G per KV head, in blocks of block_rows; the
+// context of each (sequence, KV head, row block) is cut into n chunks of at most
+// kMaxPrefillChunkPages pages.  A prefill workgroup holds its compute unit alone, so the
+// workgroups run in rounds of kTargetWgs: n minimizes rounds x (pages per chunk +
+// kPrefillChunkCost), the smallest n within 1% of the best.  With one chunk the kernel
+// writes the rows itself (no merge, no partials).
 int prefill_shape(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                   int32_t max_seq_len, int block_rows, PrefillShape *s) {
   if (num_seqs < 1 || T < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_seq_len < 1) return KVQ_ERR_INVALID_ARG;
@@ -80,12 +84,20 @@ int prefill_shape(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_
   if (static_cast<long>(num_seqs) * T * num_q_heads * (head_dim / 64) > 0x7FFFFFFFL) return KVQ_ERR_UNSUPPORTED;
   const long pages = (static_cast<long>(max_seq_len) + kPage - 1) / kPage;
   const long units = static_cast<long>(num_seqs) * num_kv_heads * row_blocks;
-  long n = (kTargetWgs + units - 1) / units;
+  auto pages_per_chunk = [&](long n) {
+    const long p = ((pages + n - 1) / n + kPrefillTeams - 1) / kPrefillTeams * kPrefillTeams;
+    return p < kMaxPrefillChunkPages ? p : static_cast<long>(kMaxPrefillChunkPages);
+  };
+  auto cost = [&](long n) {
+    const long p = pages_per_chunk(n), wgs = (pages + p - 1) / p * units;
+    return (wgs + kTargetWgs - 1) / kTargetWgs * (p + kPrefillChunkCost);
+  };
   const long nmin = (pages + kMaxPrefillChunkPages - 1) / kMaxPrefillChunkPages;
-  if (n < nmin) n = nmin;
-  long pps = (pages + n - 1) / n;
-  pps = ((pps + kPrefillTeams - 1) / kPrefillTeams) * kPrefillTeams;
-  if (pps > kMaxPrefillChunkPages) pps = kMaxPrefillChunkPages;
+  long best = cost(nmin);
+  for (long n = nmin + 1; n <= pages && n <= nmin + kPrefillChunkSearch; ++n) best = std::min(best, cost(n));
+  long n = nmin;
+  while (cost(n) * 100 > best * 101) ++n;
+  const long pps = pages_per_chunk(n);
   s->group = group;
   s->rows = static_cast<int32_t>(rows);
   s->row_blocks = static_cast<int32_t>(row_blocks);

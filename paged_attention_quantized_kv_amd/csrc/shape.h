@@ -22,6 +22,10 @@ constexpr int kTeams = KVQ_TEAMS;           // 4-wave teams per attention workgr
 constexpr int kTargetWgs = 512 / KVQ_TEAMS; // 8 waves per compute unit of the 256-CU chip
 constexpr int kMaxChunkPages = 256;   // pages of one decode attention chunk (block ids staged in LDS)
 constexpr int kMaxPrefillChunkPages = 4096;  // the same for prefill (262,144 tokens per chunk)
+// Per-workgroup cost of a prefill chunk beyond its pages (queries in, partials out), in
+// pages: measured at 256K, 128 query rows, between 10 chunks (one round) and 32 (three).
+constexpr long kPrefillChunkCost = 16;
+constexpr long kPrefillChunkSearch = 1024;  // chunk counts tried above the fewest allowed
 #ifndef KVQ_PREFILL_NT
 #define KVQ_PREFILL_NT 4
 #endif

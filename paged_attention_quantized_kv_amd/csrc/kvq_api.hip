@@ -75,10 +75,14 @@ int attn_call(Phase phase, const kvq_cache_t *cache, const void *q, int32_t q_dt
   a.qk_scale_log2 = softmax_scale * 1.4426950408889634f;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // The step's rows are quantized inside the split launch, except for the rotated formats with
-  // more than 16 query rows per KV head, whose fused instance runs out of registers (the 4-bit
-  // row quantizer beside two row tiles) and is slower than the row kernel launched first.
-  if (k_new && (cache->format == KVQ_RK8V4 || cache->format == KVQ_RK4V4) && s.rows > 16) {
+  // The step's rows are quantized inside the split launch, except where the row kernel
+  // launched first is faster: the rotated formats with more than 16 query rows per KV head,
+  // whose fused instance runs out of registers (the 4-bit row quantizer beside two row
+  // tiles), and split grids of more than two rounds of workgroups, where every round waits
+  // on its workgroups' own row quantization before their pages.
+  const long split_wgs = s.balanced ? s.slots : static_cast<long>(num_seqs) * cache->num_kv_heads * s.n_splits;
+  const bool rotated_wide = (cache->format == KVQ_RK8V4 || cache->format == KVQ_RK4V4) && s.rows > 16;
+  if (k_new && (rotated_wide || split_wgs > 2 * kvq::kTargetWgs)) {
     kvq::AppendArgs ap;
     ap.k_new = k_new;
     ap.v_new = v_new;

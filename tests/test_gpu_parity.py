@@ -330,6 +330,8 @@ MANY = {
                                  outliers=True, name="b300_t1_int8"),
     "b1024_t2_fp8": S.tiny_shape(B=1024, T=2, Hq=8, Hkv=2, D=128, lens=_lens(72, 1024, 2, 150), src=S.SRC_F32,
                                  fmt=S.FMT_FP8_ROW, name="b1024_t2_fp8"),
+    "b600_t1_bf16": S.tiny_shape(B=600, T=1, Hq=8, Hkv=1, D=128, lens=_lens(74, 600, 1, 300), src=S.SRC_BF16,
+                                 fmt=S.FMT_BF16, name="b600_t1_bf16"),
 }
 
 
@@ -337,7 +339,8 @@ MANY = {
 def test_many_sequences(K, name):
     """Cohorts up to the 1024-sequence limit with ragged contexts (lengths down to T):
     B * Hkv reaches or passes the 256 workgroups a launch aims for, so each (sequence,
-    KV head) is one chunk; both the two-call path and the fused step."""
+    KV head) is one chunk; both the two-call path and paged_decode_step, which past 512
+    split workgroups (b300, b1024, b600) appends with the row kernel before the split."""
     shp = MANY[name]
     n_splits, _ = K.num_splits(shp.B, shp.T, shp.Hq, shp.Hkv, shp.D, max(shp.lens))
     assert n_splits == 1

@@ -513,7 +513,9 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   const int tid = threadIdx.x, lane = tid & 63, wave = (tid >> 6) & 3, team = tid >> 8;
   const int q4 = lane >> 4, c16 = lane & 15;
   int split = blockIdx.x, kvh = blockIdx.y % a.num_kv_heads, b = blockIdx.z;
-  const int row0 = (blockIdx.y / a.num_kv_heads) * ROWS;  // first query row (t*G + g) of this block
+  // first query row (t*G + g) of this block; prefill row blocks go out last first, since the
+  // later rows see the most keys (longest workgroups first keeps the last round short)
+  const int row0 = (a.row_blocks - 1 - static_cast<int>(blockIdx.y) / a.num_kv_heads) * ROWS;
   int tps = a.tokens_per_split;
   size_t part = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits + split;  // partial slot
   if constexpr (APP != 2) {
@@ -1485,7 +1487,8 @@ __global__ __launch_bounds__(64 * 8 / KVQ_PREFILL_NTW, 1) void prefill_kernel(At
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q4 = lane >> 4, c16 = lane & 15;
   const int split = blockIdx.x, kvh = blockIdx.y % a.num_kv_heads, b = blockIdx.z;
-  const int row0 = (blockIdx.y / a.num_kv_heads) * ROWS;
+  // row blocks last first: the later rows see the most keys (longest workgroups first)
+  const int row0 = (a.row_blocks - 1 - static_cast<int>(blockIdx.y) / a.num_kv_heads) * ROWS;
   const int L = a.seq_lens[b];
   const int R = a.rows;
   if (L < a.T || L > a.max_seq_len || L > static_cast<long>(a.max_blocks) * kPage) {  // the merge writes NaN rows

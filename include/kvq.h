@@ -189,13 +189,13 @@ size_t paged_decode_attn_workspace_bytes(int32_t num_seqs, int32_t T, int32_t nu
  *              initialization needed; calls that share a workspace must be
  *              ordered on one stream.
  * The context of each (sequence, KV head) is cut into chunks attended in
- * parallel and merged with log-sum-exp weights.  One sequence, or more than 32:
- * the chunks are those of paged_decode_attn_num_splits(), and when one chunk per
- * (sequence, KV head) already fills the chip (num_splits == 1) the chunks write
- * their normalized rows and no merge runs.  2..32 sequences: the chunk length is
- * set on the device from the actual lengths, the smallest even number of pages
- * for which all chunks fit one workgroup per compute unit, so short sequences
- * take few chunks and long ones many (num_splits is then only the host's bound).
+ * parallel and merged with log-sum-exp weights.  2..64 sequences with fewer than
+ * 256 (sequence, KV head) pairs: the chunk length is set on the device from the
+ * actual lengths, the smallest even number of pages for which all chunks fit one
+ * workgroup per compute unit, so short sequences take few chunks and long ones
+ * many (num_splits is then only the host's bound).  Otherwise the chunks are those
+ * of paged_decode_attn_num_splits(), and when that is one chunk per (sequence, KV
+ * head) the chunks write their normalized rows and no merge runs.
  * Accuracy: K/V codes enter the matrix cores exactly (converted to f16); each
  * query row enters scaled by a power of two that puts its largest element in
  * [2^14, 2^15) (its scores take the power of two back), so a bf16 row whose

@@ -30,7 +30,9 @@ int check_cache(const kvq_cache_t *c) {
 int32_t chunk_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len) {
   const long pages = (static_cast<long>(max_seq_len) + kPage - 1) / kPage;
   const long units = static_cast<long>(num_seqs) * num_kv_heads;
-  const long n = units >= kTargetWgs ? 1 : kTargetWgs / units;
+  long n = units >= kTargetWgs ? 1 : kTargetWgs / units;
+  // past kMaxChunkPages per chunk: the fewest chunks that fit, of even length
+  n = std::max(n, (pages + kMaxChunkPages - 1) / kMaxChunkPages);
   long pps = (pages + n - 1) / n;
   pps = ((pps + kTeams - 1) / kTeams) * kTeams;
   if (pps < kTeams) pps = kTeams;
@@ -53,7 +55,10 @@ int attn_shape(int32_t num_seqs, int32_t T, int32_t num_q_heads, int32_t num_kv_
   s->rows = T * group;
   s->tokens_per_split = chunk_tokens(num_seqs, num_kv_heads, max_seq_len);
   s->n_splits = static_cast<int32_t>((static_cast<long>(max_seq_len) + s->tokens_per_split - 1) / s->tokens_per_split);
-  s->balanced = num_seqs >= 2 && num_seqs <= kMaxBalancedSeqs;
+  // balanced chunking can only split something while the (sequence, KV head) pairs number
+  // fewer than the workgroup budget; from there on every pair is one chunk, written directly
+  s->balanced = num_seqs >= 2 && num_seqs <= kMaxBalancedSeqs &&
+                static_cast<long>(num_seqs) * num_kv_heads < kTargetWgs;
   const long slots = s->balanced ? balanced_slots(num_seqs, num_kv_heads, max_seq_len)
                                  : static_cast<long>(num_seqs) * num_kv_heads * s->n_splits;
   if (slots > 0x7FFFFFFFL) return KVQ_ERR_UNSUPPORTED;

@@ -38,7 +38,7 @@ constexpr int kPrefillRows = 16 * kPrefillNT;   // query rows (t*G + g) of a pre
 constexpr int kBulkAppendRows = 64;   // appends of at least this many rows per sequence go page by page
 
 constexpr int32_t kMaxSeqLen = 1 << 30;  // longest supported context (2^24 pages of 64 tokens)
-constexpr int kMaxBalancedSeqs = 32;
+constexpr int kMaxBalancedSeqs = 64;  // one sequence per lane of the planning wave
 // partial slots (and split workgroups) of a balanced call: one per chunk at most, where every
 // (sequence, KV head) may round up by one chunk and a chunk holds at most kMaxChunkPages pages
 inline long balanced_slots(long num_seqs, long num_kv_heads, long max_seq_len) {

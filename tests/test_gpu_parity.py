@@ -384,15 +384,19 @@ BALANCED = {
                            src=S.SRC_F32, fmt=S.FMT_FP8_ROW, name="b32_t4"),
     "b2_t4_rk8v4": S.tiny_shape(B=2, T=4, Hq=24, Hkv=4, D=256, lens=(30000, 29000), src=S.SRC_BF16,
                                 fmt=S.FMT_RK8V4, outliers=True, name="b2_t4_rk8v4"),
+    "b48_t2_kv2": S.tiny_shape(B=48, T=2, Hq=8, Hkv=2, D=128, lens=tuple(int(x) for x in
+                                                                      np.random.default_rng(10).integers(2, 12000, 48)),
+                               src=S.SRC_BF16, outliers=True, name="b48_t2_kv2"),
 }
 
 
 @pytest.mark.parametrize("name", list(BALANCED))
 def test_balanced_chunking(K, name):
-    """Cohorts of 2..32 sequences: chunks of one common length set on the device from the
-    actual lengths, so a sequence's chunk count follows its own length (a 131,072-token
-    sequence beside tiny ones takes nearly all the workgroups).  Parity with the oracle,
-    the two phases called apart equal to the one call bit for bit, and the fused step."""
+    """Cohorts of 2..64 sequences with fewer than 256 (sequence, KV head) pairs: chunks of
+    one common length set on the device from the actual lengths, so a sequence's chunk
+    count follows its own length (a 131,072-token sequence beside tiny ones takes nearly
+    all the workgroups).  Parity with the oracle, the two phases called apart equal to the
+    one call bit for bit, and the fused step."""
     shp = BALANCED[name]
     w = S.make(shp, seed=S.seed_of("tiny") + 900 + list(BALANCED).index(name))
     rows = _sample_rows(w, 2)

@@ -92,7 +92,8 @@ def test_sink_256k_t1_64_chunks(K, fmt):
 
 
 def balanced_chunk_tokens(lens, Hkv, W=256):
-    """Chunk length of a 2..32-sequence call: the smallest even page count (at most 256) for
+    """Chunk length of a balanced call (2..64 sequences, fewer than 256 (sequence, KV head)
+    pairs): the smallest even page count (at most 256) for
     which the call's chunks, sum of ceil(pages / length) over (sequence, KV head), fit in W."""
     pages = [(L + 63) // 64 for L in lens]
     count = lambda q: Hkv * sum(max(1, -(-p // q)) for p in pages)

@@ -518,6 +518,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
   const int row0 = (a.row_blocks - 1 - static_cast<int>(blockIdx.y) / a.num_kv_heads) * ROWS;
   int tps = a.tokens_per_split;
   size_t part = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.n_splits + split;  // partial slot
+  bool direct = a.direct_out != 0;  // normalized rows to out, no partials
   if constexpr (APP != 2) {
     if (a.balanced != 0) {  // this workgroup's (sequence, KV head, chunk) from the actual lengths
       const BalancedChunks c = balanced_chunks(a, lane);
@@ -530,6 +531,7 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
       split = (w - first) % nb;
       tps = c.tps;
       part = w;
+      direct = a.direct_single != 0 && nb == 1;  // a one-chunk sequence: the merge skips it
     }
   }
   const int L = a.seq_lens[b];
@@ -1305,8 +1307,8 @@ __global__ __launch_bounds__(256 * NTEAM, 1) void attn_split_kernel(AttnArgs a) 
     for (int nt = 0; nt < NT; ++nt) {
       const int rl = 16 * nt + c16, r = row0 + rl;
       if (r < R) {
-        // one chunk per row block: the normalized row goes to out[b][t][h] (t*G + g = r)
-        const bool direct = a.direct_out != 0;
+        // one chunk per row block (or a one-chunk sequence of a balanced call): the
+        // normalized row goes to out[b][t][h] (t*G + g = r)
         const size_t orow = ((static_cast<size_t>(b) * a.T + r / a.group) * a.num_q_heads + kvh * a.group +
                              r % a.group) * D;
 #pragma unroll
@@ -1360,6 +1362,11 @@ __global__ __launch_bounds__(64 * MW) void attn_merge_kernel(AttnArgs a) {
     nsl = __shfl(c.n, b);
     part0 = static_cast<size_t>(__shfl(c.first, b)) + static_cast<size_t>(kvh) * nsl;
     tps = c.tps;
+    if (a.direct_single != 0 && nsl == 1) {  // the split workgroup wrote these rows itself
+      const int L = a.seq_lens[b];
+      if (w == 0 && (L < a.T || L > a.max_seq_len || L > static_cast<long>(a.max_blocks) * kPage)) dst[lane] = NAN;
+      return;
+    }
   }
   const int c4 = lane & 15, sg = lane >> 4, col = qs * 16 + c4;
   const float2 *ml2 = reinterpret_cast<const float2 *>(a.ws_ml);

@@ -42,6 +42,9 @@ struct AttnArgs {
   // the device from the actual lengths (balanced_chunks); n_splits is then the number of
   // partial slots and split workgroups (grid x), not the chunks per (sequence, KV head)
   int32_t balanced;
+  // balanced, one call: a sequence of one chunk writes its normalized rows and the merge
+  // skips it
+  int32_t direct_single;
 };
 
 // Launch arguments of kvq_check_tables, validated on the host.

@@ -72,6 +72,7 @@ int attn_call(Phase phase, const kvq_cache_t *cache, const void *q, int32_t q_dt
   // one call with one chunk per (sequence, KV head): the split kernel writes the normalized
   // rows itself and no merge runs (the two phases called apart keep the partials)
   a.direct_out = (phase == Phase::kBoth && !s.balanced && s.n_splits == 1) ? 1 : 0;
+  a.direct_single = (phase == Phase::kBoth && s.balanced) ? 1 : 0;
   a.qk_scale_log2 = softmax_scale * 1.4426950408889634f;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -311,6 +312,7 @@ int paged_prefill_attn(const kvq_cache_t *cache, const void *q, int32_t q_dtype,
   a.n_splits = s.n_splits;
   a.row_blocks = s.row_blocks;
   a.balanced = 0;
+  a.direct_single = 0;
   a.direct_out = s.direct ? 1 : 0;
   a.qk_scale_log2 = softmax_scale * 1.4426950408889634f;
 

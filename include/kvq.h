@@ -243,10 +243,12 @@ int paged_decode_attn_merge(const kvq_cache_t *cache, const void *q, int32_t q_d
  * paged_decode_attn over the cache including them.  Same results as the two
  * calls in sequence; the rows are quantized inside the attention launch by the
  * workgroup whose context chunk holds them, which saves one launch per step.
- * (The rotated formats with more than 16 query rows per KV head append through a
- * separate launch first, on the same stream: their fused kernel runs out of
- * registers and is the slower of the two.)  A sequence whose length is outside
- * [T, max_seq_len] gets no new rows and NaN output rows.
+ * (Two cases append through a separate launch first, on the same stream, where
+ * that is the faster of the two: the rotated formats with more than 16 query rows
+ * per KV head, whose fused kernel runs out of registers, and calls of more than
+ * 512 attention workgroups, where every round of workgroups would wait on its own
+ * rows.)  A sequence whose length is outside [T, max_seq_len] gets no new rows and
+ * NaN output rows.
  *
  *   k_new, v_new  [num_seqs][T][num_kv_heads][head_dim], same dtype as q (dtype)
  *   other arguments as for paged_decode_attn (workspace size included).

@@ -86,6 +86,19 @@ def test_prefill_chunk_at_full_context_sampled(K, name):
     check(K, w, rows=_prefill_rows(w, (0, 1, 2047, 4094, 4095), 2), chunk=65536, prefill=True)
 
 
+@pytest.mark.parametrize("fmt", [S.FMT_INT8_G64, S.FMT_FP8_ROW])
+def test_prefill_chunk_in_rounds_sampled(K, fmt):
+    """A 512-row chunk ending a 65,536-token context: 24 row blocks of 128 rows x 4 KV
+    heads, so each row block's context is cut into 8 chunks (768 workgroups, three full
+    rounds) and merged, with the row blocks dispatched last rows first.  Sampled rows
+    over the whole chunk, the first and last rows of row blocks among them."""
+    shp = S.tiny_shape(B=1, T=512, Hq=24, Hkv=4, D=256, lens=(65536,), src=S.SRC_BF16, fmt=fmt, outliers=True,
+                       name="pf_rounds")
+    w = S.make(shp, seed=S.seed_of("tiny") + 700 + fmt)
+    assert not _direct(K, w.shape, w.max_seq_len)
+    check(K, w, rows=_prefill_rows(w, (0, 1, 21, 22, 255, 490, 511), 3), chunk=8192, prefill=True)
+
+
 def test_prefill_t_le_8_matches_decode(K):
     """For T <= 8 the prefill call computes what paged_decode_attn computes."""
     w = S.make(S.tiny_shape(B=2, T=4, Hq=24, Hkv=4, D=256, lens=(3000, 515), src=S.SRC_BF16, outliers=True),

@@ -111,6 +111,27 @@ def test_workspace_and_chunking_are_pure_functions_of_the_shape(K):
         assert n * 4 == 256
 
 
+def test_decode_chunk_rule(K):
+    # each (sequence, KV head) gets 256 / pairs chunks, at least one, its pages spread evenly
+    assert K.num_splits(1, 4, 24, 4, 256, 131072) == (64, 32 * 64)
+    assert K.num_splits(1, 1, 8, 1, 256, 262144) == (256, 16 * 64)
+    assert K.num_splits(64, 1, 16, 2, 128, 8192) == (2, 64 * 64)   # 128 pairs: 256 workgroups
+    assert K.num_splits(48, 1, 24, 4, 256, 4096) == (1, 64 * 64)   # 192 pairs: one chunk each
+    # past the 256-page chunk cap: 294 pages as 148 + 146, not 256 + 38
+    assert K.num_splits(64, 1, 32, 4, 128, 18768) == (2, 148 * 64)
+
+
+def test_prefill_chunks_fill_whole_rounds(K):
+    # 262,144 tokens, Hq=24 over Hkv=4, D=256: the 128-row prefill kernel's 24 * T / 512
+    # row blocks x 4 KV heads take the chunk counts whose workgroups fill whole rounds of
+    # 256 (512 rows: 96 units x 8 = 768), and the 4096-row chunk (768 units) one chunk
+    for T, chunks in ((512, 8), (1024, 4), (2048, 2)):
+        parts = 4 * chunks * T * 6
+        ml = (parts * 2 * 4 + 255) // 256 * 256
+        assert K.prefill_workspace_bytes(1, T, 24, 4, 256, 262144) == ml + parts * 256 * 4, T
+    assert K.prefill_workspace_bytes(1, 4096, 24, 4, 256, 262144) == 256
+
+
 def test_check_tables_validation(K):
     d = _desc(K)
 

@@ -376,6 +376,16 @@ def test_merge_of_more_than_64_chunks(K, shp, chunks):
     _fused_check(K, w)
 
 
+def test_merge_past_256_chunks_at_4m_tokens(K):
+    """One KV head at 4,210,688 tokens (65,792 pages): the chunk cap of 256 pages gives 257
+    chunks, so the four-wave merge takes chunk 256 in a second round of batches (wave 0,
+    slots 256..319).  Every output row against the oracle."""
+    L = 257 * 256 * 64
+    assert K.num_splits(1, 1, 4, 1, 128, L) == (257, 256 * 64)
+    w = S.make(S.tiny_shape(B=1, T=1, Hq=4, Hkv=1, D=128, lens=(L,), src=S.SRC_BF16, name="mqa_4m"), seed=41)
+    check(K, w, chunk=1 << 20)
+
+
 BALANCED = {
     "skew_b8": S.tiny_shape(B=8, T=1, Hq=24, Hkv=4, D=256, lens=(131072, 64, 65, 100, 200, 1, 2, 3000),
                             src=S.SRC_BF16, outliers=True, name="skew_b8"),
